@@ -1,0 +1,153 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE FFN layer forward pass.
+ *
+ * One call computes, for T tokens, the forward pass of one Mixture-of-Experts
+ * FFN layer with block-scaled low-precision expert weights:
+ *
+ *   1. router logits  l[t,e] = sum_i W_r[e,i] x[t,i] (+ bias[t,e]), in f32
+ *      (dragon.c page, "Precision": the router runs in f32);
+ *   2. softmax over all E experts and top-k; equal logits go to the lower
+ *      index; the k ids of a token are listed in ascending expert id;
+ *      weights w = p[ids], divided by their sum when renorm is set;
+ *   3. a counting-sort permute that groups the token-slots s = t*k + j by
+ *      expert, stable in s (Trochilus README, "Acknowledgements": (token,
+ *      expert) pairs sorted by a counting sort);
+ *   4. per slot, a SwiGLU expert: g = W_gate x, u = W_up x,
+ *      h = bf16(silu(g) * u), y = W_down h, with the weights decoded exactly
+ *      from e4m3 codes with 128x128 f32 block scales (dragon.c page,
+ *      "Precision" and section 8 Round 3) or from e2m1 codes with one UE8M0
+ *      power-of-two scale per 32 inputs (dev.to page, DeepSeek-V4.1-Flash
+ *      post, "Bytes per token decide everything");
+ *   5. out[t] = sum_j w[t,j] y[t*k+j], j ascending, in f32 (WARP BACKENDS.md,
+ *      "Coherent memory": one partial per selected expert, reduced in router
+ *      order, is what makes the result reproducible bit for bit).
+ *
+ * Memory: every pointer passed to moe_forward is HIP device memory owned by
+ * the caller.  The library allocates no device memory: all scratch lives in
+ * the caller's workspace.  A plan holds host metadata only and is immutable,
+ * so forwards on different streams with different workspaces may overlap.
+ *
+ * Errors: every check runs on the host before the first launch, so a call
+ * that returns an error has written nothing.  moe_forward is asynchronous on
+ * `stream` and never synchronises the host; a fault inside a kernel surfaces
+ * at the caller's next synchronisation.  No exception crosses this ABI and
+ * the library never aborts.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  MOE_ERR_BAD_SHAPE = 2,    /* a size is out of range (T < 0, T > max_tokens, k > E, ...) */
+  MOE_ERR_UNSUPPORTED = 3,  /* dims not divisible by the format's block, E or k too large */
+  MOE_ERR_ALIGNMENT = 4,    /* a pointer or stride breaks the alignment stated below */
+  MOE_ERR_WORKSPACE = 5,    /* workspace_bytes < moe_workspace_size(plan, T) */
+  MOE_ERR_HIP = 6,          /* a HIP call failed; moe_plan_info() names it */
+  MOE_ERR_DEVICE = 7        /* no HIP device, or the current device is not gfx950 */
+} moe_status;
+
+/* Expert weight formats. */
+typedef enum {
+  /* OCP E4M3FN codes (1 byte each), one f32 scale per 128x128 block.
+   * Requires d_model % 128 == 0 and d_ff % 128 == 0. */
+  MOE_W_E4M3_B128 = 0,
+  /* OCP E2M1 codes, two per byte, element 2i in the low nibble; one UE8M0
+   * byte (scale 2^(b-127)) per 32 contiguous inputs of a row.
+   * Requires d_model % 32 == 0 and d_ff % 32 == 0. */
+  MOE_W_E2M1_UE8M0_G32 = 1
+} moe_wfmt;
+
+/* Which variant of the one GPU path runs the expert stage. */
+typedef enum {
+  MOE_PATH_AUTO = 0,     /* decode below a per-plan token threshold, grouped above */
+  MOE_PATH_DECODE = 1,   /* HBM-streaming matvec per selected expert */
+  MOE_PATH_GROUPED = 2   /* grouped MFMA GEMM over expert tiles */
+} moe_path;
+
+typedef struct {
+  int32_t d_model;     /* hidden size d */
+  int32_t d_ff;        /* expert FFN width f */
+  int32_t n_experts;   /* E, 1..1024 */
+  int32_t top_k;       /* k, 1..min(E, 16) */
+  int32_t max_tokens;  /* largest T a forward may be called with, >= 1 */
+  int32_t wfmt;        /* moe_wfmt */
+  int32_t renorm;      /* 1: divide the k weights by their sum; 0: keep softmax probabilities */
+  int32_t path;        /* moe_path */
+} moe_desc;
+
+typedef struct moe_plan_s* moe_plan_t;
+
+/* One expert matrix family [E][N][K] (gate and up: N = d_ff, K = d_model;
+ * down: N = d_model, K = d_ff).  Rows are K-contiguous.
+ *   e4m3: q is uint8 [E][N][K]; scale is f32 [E][N/128][K/128].
+ *   e2m1: q is uint8 [E][N][K/2]; scale is uint8 [E][N][K/32].
+ * q_expert_stride / s_expert_stride: bytes from expert e to expert e+1, so
+ * both one buffer per matrix and one block per expert can be described.
+ * Alignment: q and q_expert_stride 16 bytes; e4m3 scale and s_expert_stride
+ * 4 bytes; e2m1 scales 1 byte. */
+typedef struct {
+  const void* q;
+  const void* scale;
+  int64_t q_expert_stride;
+  int64_t s_expert_stride;
+} moe_mat;
+
+/* Validate `desc`, check the current HIP device and choose kernel variants.
+ * On success *out holds a plan (host memory only).  Shape errors are
+ * reported before the device is queried. */
+moe_status moe_plan(const moe_desc* desc, moe_plan_t* out);
+
+/* Bytes of device workspace a forward over n_tokens tokens needs (0 if
+ * n_tokens <= 0 or the plan is NULL).  256-byte alignment is required. */
+size_t moe_workspace_size(moe_plan_t plan, int32_t n_tokens);
+
+/* The forward pass over T = n_tokens tokens, enqueued on `stream` (a
+ * hipStream_t; NULL means the default stream).
+ *   x          bf16 bits [T][d], 16-byte aligned
+ *   w_router   f32 [E][d], 16-byte aligned
+ *   logit_bias f32 [T][E] added to the router logits, or NULL
+ *   gate, up, down   expert matrices (see moe_mat)
+ *   out        f32 [T][d], 16-byte aligned
+ * Optional outputs (NULL: kept inside the workspace instead):
+ *   topk_ids int32 [T][k] (ascending per token), topk_w f32 [T][k],
+ *   counts int32 [E], offsets int32 [E+1] (exclusive scan of counts),
+ *   perm int32 [T*k] (sorted position -> slot t*k+j).
+ * T = 0 returns MOE_OK and launches nothing. */
+moe_status moe_forward(moe_plan_t plan, int32_t n_tokens, const uint16_t* x, const float* w_router,
+                       const float* logit_bias, const moe_mat* gate, const moe_mat* up,
+                       const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Byte offset, inside the workspace of a forward over n_tokens tokens, of
+ * the expert hidden activations h: bf16 bits [T*k][d_ff] in sorted-slot
+ * order (row p belongs to slot perm[p]).  -1 if the plan is NULL or
+ * n_tokens <= 0.  Valid after the forward has completed. */
+int64_t moe_workspace_h_offset(moe_plan_t plan, int32_t n_tokens);
+
+/* Which variant a forward over n_tokens tokens runs: MOE_PATH_DECODE or
+ * MOE_PATH_GROUPED (-1 for a NULL plan). */
+int32_t moe_plan_path(moe_plan_t plan, int32_t n_tokens);
+
+void moe_plan_free(moe_plan_t plan);
+
+/* Static string naming a status code. */
+const char* moe_status_str(moe_status status);
+
+/* Human-readable description of the plan: device, chosen variants, tiles,
+ * and the last HIP error seen by a call on this plan.  Owned by the plan. */
+const char* moe_plan_info(moe_plan_t plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,165 @@
+"""Python binding of libmoe.so, the gfx950 MoE FFN layer (see include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI.  torch supplies device memory and the stream; the functions
+below take torch tensors (or raw device addresses as ints) and pass their
+pointers through.  There is no fallback: if libmoe.so is missing or cannot be
+loaded, importing the binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_NULL_ARG, MOE_ERR_BAD_SHAPE, MOE_ERR_UNSUPPORTED = 0, 1, 2, 3
+MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
+MOE_W_E4M3_B128, MOE_W_E2M1_UE8M0_G32 = 0, 1
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
+WFMT = {"e4m3": MOE_W_E4M3_B128, "e2m1": MOE_W_E2M1_UE8M0_G32}
+
+
+class moe_desc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("wfmt", ctypes.c_int32),
+                ("renorm", ctypes.c_int32), ("path", ctypes.c_int32)]
+
+
+class moe_mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("q_expert_stride", ctypes.c_int64), ("s_expert_stride", ctypes.c_int64)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, info: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_str(status)}" + (f" ({info})" if info else ""))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python -m mixture_experts_layer_f32_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.moe_plan.argtypes = [ctypes.POINTER(moe_desc), ctypes.POINTER(vp)]
+    L.moe_plan.restype = ctypes.c_int
+    L.moe_workspace_size.argtypes = [vp, i32]
+    L.moe_workspace_size.restype = sz
+    L.moe_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(moe_mat),
+                              ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat), vp, vp, vp, vp,
+                              vp, vp, vp, sz, vp]
+    L.moe_forward.restype = ctypes.c_int
+    L.moe_workspace_h_offset.argtypes = [vp, i32]
+    L.moe_workspace_h_offset.restype = i64
+    L.moe_plan_path.argtypes = [vp, i32]
+    L.moe_plan_path.restype = i32
+    L.moe_plan_free.argtypes = [vp]
+    L.moe_plan_free.restype = None
+    L.moe_status_str.argtypes = [ctypes.c_int]
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_plan_info.argtypes = [vp]
+    L.moe_plan_info.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def moe_status_str(status: int) -> str:
+    return lib.moe_status_str(int(status)).decode()
+
+
+class Plan:
+    """Owns a moe_plan_t; freed with the object."""
+
+    def __init__(self, handle: int, desc: moe_desc):
+        self.handle = handle
+        self.desc = desc
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            lib.moe_plan_free(self.handle)
+            self.handle = None
+
+
+def moe_plan(d_model: int, d_ff: int, n_experts: int, top_k: int, max_tokens: int,
+             wfmt: int | str, renorm: bool, path: int = MOE_PATH_AUTO) -> Plan:
+    if isinstance(wfmt, str):
+        wfmt = WFMT[wfmt]
+    desc = moe_desc(d_model, d_ff, n_experts, top_k, max_tokens, int(wfmt), int(bool(renorm)),
+                    int(path))
+    h = ctypes.c_void_p()
+    st = lib.moe_plan(ctypes.byref(desc), ctypes.byref(h))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_plan")
+    return Plan(h.value, desc)
+
+
+def moe_plan_status(desc: moe_desc) -> int:
+    """Raw status of moe_plan for a descriptor (the plan, if any, is freed)."""
+    h = ctypes.c_void_p()
+    st = lib.moe_plan(ctypes.byref(desc), ctypes.byref(h))
+    if h.value:
+        lib.moe_plan_free(h.value)
+    return st
+
+
+def moe_workspace_size(plan: Plan, n_tokens: int) -> int:
+    return int(lib.moe_workspace_size(plan.handle, int(n_tokens)))
+
+
+def moe_workspace_h_offset(plan: Plan, n_tokens: int) -> int:
+    return int(lib.moe_workspace_h_offset(plan.handle, int(n_tokens)))
+
+
+def moe_plan_path(plan: Plan, n_tokens: int) -> int:
+    return int(lib.moe_plan_path(plan.handle, int(n_tokens)))
+
+
+def moe_plan_info(plan: Plan) -> str:
+    return lib.moe_plan_info(plan.handle).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def mat(q, scale, q_expert_stride: Optional[int] = None,
+        s_expert_stride: Optional[int] = None) -> moe_mat:
+    """moe_mat from device tensors with a leading expert axis (strides in bytes
+    default to one expert's contiguous size)."""
+    if q_expert_stride is None:
+        q_expert_stride = q.stride(0) * q.element_size()
+    if s_expert_stride is None:
+        s_expert_stride = scale.stride(0) * scale.element_size()
+    return moe_mat(_ptr(q), _ptr(scale), int(q_expert_stride), int(s_expert_stride))
+
+
+def moe_forward(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_mat, up: moe_mat,
+                down: moe_mat, out, topk_ids=None, topk_w=None, counts=None, offsets=None,
+                perm=None, workspace=None, workspace_bytes: Optional[int] = None,
+                stream=None) -> None:
+    """Enqueue the forward on `stream` (a torch stream, a raw hipStream_t int,
+    or None for torch's current stream).  Raises MoeError on a non-OK status."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.moe_forward(plan.handle, int(n_tokens), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                         ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), _ptr(out),
+                         _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm),
+                         _ptr(workspace), int(workspace_bytes), stream or None)
+    if st != MOE_OK:
+        raise MoeError(st, "moe_forward", moe_plan_info(plan))

@@ -1,0 +1,79 @@
+// Shared device helpers for the gfx950 MoE kernels: vector types, exact
+// format conversions, wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define WAVE 64
+
+namespace moe {
+
+// bf16 bits -> f32: the bf16 pattern is the top half of the f32 pattern
+// (dragon.c page, section 8 Round 3: bf16 -> f32 is a 16-bit left shift).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// UE8M0 byte -> the f32 power of two 2^(b-127) (b = 0 gives the subnormal
+// 2^-127; b = 255 is not produced by the format's encoder).
+__device__ __forceinline__ float ue8m0_to_f32(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// Two OCP e4m3 codes (bytes 0,1 of w, or 2,3 with HI) -> two exact f32.
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+// Same pairs -> bf16 (exact: every e4m3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_to_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+// Two e2m1 codes (byte `sel` of w: low nibble first) times a power-of-two
+// scale -> bf16x2 / f32x2, exact while the result stays a normal number.
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2_to_bf16(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace moe

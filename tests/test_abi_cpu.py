@@ -1,0 +1,65 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/moe.h declares, and rejects bad layer descriptors before touching a
+device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    import mixture_experts_layer_f32_amd as m
+    names = declared_functions()
+    assert {"moe_plan", "moe_forward", "moe_workspace_size", "moe_plan_free", "moe_status_str",
+            "moe_plan_info"} <= set(names)
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings():
+    import mixture_experts_layer_f32_amd as m
+    assert m.moe_status_str(0) == "MOE_OK"
+    assert m.moe_status_str(m.MOE_ERR_WORKSPACE) == "MOE_ERR_WORKSPACE"
+    assert m.moe_status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(d_model=0), 2), (dict(top_k=9), 2), (dict(max_tokens=0), 2), (dict(renorm=2), 2),
+    (dict(path=5), 2), (dict(n_experts=2048, top_k=2), 3), (dict(top_k=17, n_experts=64), 3),
+    (dict(d_model=200), 3), (dict(d_ff=96), 3), (dict(wfmt=7), 3),
+    (dict(wfmt=1, d_model=48), 3), (dict(wfmt=1, d_ff=80), 3),
+])
+def test_descriptor_validation_before_device(fields, status):
+    import mixture_experts_layer_f32_amd as m
+    base = dict(d_model=256, d_ff=256, n_experts=8, top_k=2, max_tokens=4, wfmt=0, renorm=1,
+                path=0)
+    base.update(fields)
+    assert m.moe_plan_status(m.moe_desc(**base)) == status
+
+
+def test_plan_needs_gfx950_device():
+    import torch
+    import mixture_experts_layer_f32_amd as m
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present; covered by the GPU tests")
+    d = m.moe_desc(256, 256, 8, 2, 4, 0, 1, 0)
+    assert m.moe_plan_status(d) == m.MOE_ERR_DEVICE
+
+
+def test_null_plan_queries():
+    import mixture_experts_layer_f32_amd as m
+    assert m.lib.moe_workspace_size(None, 4) == 0
+    assert m.lib.moe_workspace_h_offset(None, 4) == -1
+    assert m.lib.moe_plan_path(None, 4) == -1
+    assert m.lib.moe_plan_info(None) == b""
+    m.lib.moe_plan_free(None)
