@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+One step = one forward of the whole layer (router, top-k, permute, gate/up +
+SwiGLU, down, combine) over one batch of T synthetic tokens whose inputs are
+already resident in HBM.  Default workload: the OLMoE-1B-7B-shaped decode
+layer (d=2048, f=1024, 64 experts, top-8, e4m3 weights with 128x128 f32 block
+scales, no renormalisation) at T=8 tokens.
+
+Prints one JSON line with the throughput, the roofline of the dominant kernel
+(its duration measured with HIP events recorded on the launch stream by the
+library's own timing hooks) and the CPU oracle's throughput on a bounded
+sample of the same workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; achieved HBM GB/s (decode), MFMA TFLOPS (prefill)"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+KERNEL_SOURCES = ["moe_common.h", "moe_route.h", "moe_decode.h", "moe_gemm.h", "moe_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_f32_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def expert_stage_bytes(wl, U, T):
+    """Algorithmic bytes of the two expert kernels for one launch: every
+    selected expert's weights once (codes + scales), activations in, results out."""
+    d, f, k = wl.d, wl.f, wl.k
+    S = T * k
+    if wl.fmt == "e4m3":
+        gu = 2 * (f * d + 4 * (f // 128) * (d // 128))
+        dn = d * f + 4 * (d // 128) * (f // 128)
+    else:
+        gu = 2 * (f * d // 2 + f * d // 32)
+        dn = d * f // 2 + d * f // 32
+    gateup = U * gu + T * d * 2 + S * f * 2          # weights, x rows, h (bf16) out
+    down = U * dn + S * f * 2 + S * d * 4            # weights, h in, y (f32) out
+    return gateup, down
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="olmoe-decode")
+    ap.add_argument("--tokens", type=int, default=8)
+    ap.add_argument("--path", choices=["auto", "decode", "grouped"], default="auto")
+    ap.add_argument("--batches", type=int, default=16, help="distinct x batches rotated")
+    ap.add_argument("--copy-gib", type=float, default=1.0,
+                    help="rotate weight copies until this many GiB are cycled (defeats the 256 MB "
+                         "Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bounded CPU-oracle sample (0 disables)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured with rocprofv3 --pmc")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this layer "
+              "build runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import mixture_experts_layer_f32_amd as moe
+    from mixture_experts_layer_f32_amd.device import DeviceWeights, Runner, to_dev
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    T = args.tokens
+    t_gen = time.time()
+    layer = synth.make_layer(wl)
+    batches = [synth.make_batch(wl, layer, T, batch_index=i) for i in range(args.batches)]
+    print(f"# generated {wl.name} layer + {len(batches)} batches of T={T} in "
+          f"{time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    W0 = DeviceWeights.upload(layer.w_router, layer.gate.q, layer.gate.s, layer.up.q, layer.up.s,
+                              layer.down.q, layer.down.s)
+    layer_bytes = W0.nbytes()
+    free, _ = torch.cuda.mem_get_info()
+    copies = max(1, min(math.ceil(args.copy_gib * 2 ** 30 / layer_bytes),
+                        int(0.5 * free // layer_bytes) + 1, 16))
+    Ws = [W0] + [DeviceWeights(*(t.clone() for t in (W0.w_router, W0.gate_q, W0.gate_s, W0.up_q,
+                                                      W0.up_s, W0.down_q, W0.down_s)))
+                 for _ in range(copies - 1)]
+    xs = [to_dev(b.x) for b in batches]
+    biases = [to_dev(b.bias) if b.bias is not None else None for b in batches]
+    path = {"auto": moe.MOE_PATH_AUTO, "decode": moe.MOE_PATH_DECODE,
+            "grouped": moe.MOE_PATH_GROUPED}[args.path]
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path)
+    outs = run.outputs(T)
+    used_path = "decode" if moe.moe_plan_path(run.plan, T) == moe.MOE_PATH_DECODE else "grouped"
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        run.forward(Ws[i % copies], xs[i % len(xs)], biases[i % len(xs)], outs, stream)
+
+    # distinct experts per batch (U) from the GPU's own counts
+    Us = []
+    for i in range(len(xs)):
+        step(i)
+        torch.cuda.synchronize()
+        Us.append(int((outs["counts"] > 0).sum().item()))
+    U = float(np.mean(Us))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = T * args.steps / (t1 - t0)
+
+    # live per-stage durations: HIP events recorded by the library on `stream`
+    moe.moe_timing_enable(run.plan, moe.STAGES, max_forwards=args.steps)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    stage_ms, n_fw = moe.moe_timing_collect(run.plan)
+    t3 = time.perf_counter()
+    moe.moe_timing_disable(run.plan)
+    stage_avg_us = {k: 1e3 * v / n_fw for k, v in stage_ms.items()}
+    timed_ms_per_step = (t3 - t2) * 1e3 / args.steps
+
+    gu_bytes, dn_bytes = expert_stage_bytes(wl, U, T)
+    S = T * wl.k
+    flops = {"gateup": 4.0 * S * wl.d * wl.f, "down": 2.0 * S * wl.d * wl.f}
+    nbytes = {"gateup": gu_bytes, "down": dn_bytes}
+    dom = max(("gateup", "down"), key=lambda s: stage_avg_us[s])
+    dur_s = stage_avg_us[dom] * 1e-6
+    intensity = flops[dom] / nbytes[dom]
+    if intensity > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved, peak, unit, bound = flops[dom] / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = nbytes[dom] / dur_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+
+    traffic = None
+    ksrc = kernel_source_hash()
+    key = f"{wl.name}/T={T}/{used_path}/{dom}"
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        ent = tr.get("entries", {}).get(key)
+        if ent and ent.get("kernel_source") == ksrc:
+            traffic = ent["bytes_per_launch"]
+
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                "kernel_us": round(stage_avg_us[dom], 3),
+                "algorithmic_bytes": int(nbytes[dom]), "algorithmic_flops": int(flops[dom])}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()
+                         if p.get("user_api") == "blas"] or [1])
+        except Exception:  # noqa: BLE001
+            cores = 1
+        M = lambda m: oracle.Mat(m.q, m.s, m.K)  # noqa: E731
+        done, tok, tc0 = 0, 0, time.perf_counter()
+        while True:
+            b = batches[done % len(batches)]
+            oracle.moe_forward(b.x, layer.w_router, b.bias, M(layer.gate), M(layer.up),
+                               M(layer.down), wl.k, wl.renorm, wl.fmt)
+            done += 1
+            tok += T
+            if time.perf_counter() - tc0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - tc0
+        cpu = {"value": round(tok / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"{done} full forwards of T={T} tokens of the {wl.name} workload "
+                         f"({el:.1f} s, float64 numpy oracle)"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if used_path == "decode" else "bf16-mfma/f32-acc",
+        "data": "synthetic (seeded; random-init weights quantised to the workload's format)",
+        "config": {
+            "workload": f"{wl.name}: d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.fmt} "
+                        f"renorm={int(wl.renorm)}, T={T} tokens per step",
+            "tokens_per_step": T,
+            "path": used_path,
+            "weights": "e4m3 + f32 128x128 block scales" if wl.fmt == "e4m3"
+                       else "e2m1 + ue8m0 per 32",
+            "activations": "bf16",
+            "distinct_experts_per_step": U,
+            "weight_copies_rotated": copies,
+            "x_batches_rotated": len(xs),
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_us": {k: round(v, 3) for k, v in stage_avg_us.items()},
+        "ms_per_step_with_stage_events": round(timed_ms_per_step, 5),
+        "kernel_source": ksrc,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,6 +137,32 @@ int64_t moe_workspace_h_offset(moe_plan_t plan, int32_t n_tokens);
  * MOE_PATH_GROUPED (-1 for a NULL plan). */
 int32_t moe_plan_path(moe_plan_t plan, int32_t n_tokens);
 
+/* Stages of a forward, in launch order (bit i of a timing mask = stage i). */
+typedef enum {
+  MOE_STAGE_ROUTER = 0,   /* router logits */
+  MOE_STAGE_TOPK = 1,     /* softmax + top-k */
+  MOE_STAGE_PERMUTE = 2,  /* counting-sort permute */
+  MOE_STAGE_GATEUP = 3,   /* gate/up projections + SwiGLU -> h */
+  MOE_STAGE_DOWN = 4,     /* down projection -> y */
+  MOE_STAGE_COMBINE = 5,  /* fixed-order weighted combine -> out */
+  MOE_N_STAGES = 6
+} moe_stage;
+
+/* Instrumentation: while enabled, each moe_forward (up to max_forwards of
+ * them) records a HIP event before and after every stage whose bit is set in
+ * stage_mask, on the forward's stream.  The events are created here (no
+ * device memory is allocated).  Timing makes the plan stateful: use it from
+ * one host thread and one stream at a time. */
+moe_status moe_timing_enable(moe_plan_t plan, uint32_t stage_mask, int32_t max_forwards);
+
+/* Waits for the last recorded event, then writes for each stage the summed
+ * GPU time in milliseconds over the recorded forwards (stage_ms[MOE_N_STAGES];
+ * 0 for stages not in the mask) and their number, and starts a new count. */
+moe_status moe_timing_collect(moe_plan_t plan, float* stage_ms, int32_t* n_forwards);
+
+/* Stops recording and destroys the events. */
+moe_status moe_timing_disable(moe_plan_t plan);
+
 void moe_plan_free(moe_plan_t plan);
 
 /* Static string naming a status code. */

@@ -19,6 +19,7 @@ MOE_OK, MOE_ERR_NULL_ARG, MOE_ERR_BAD_SHAPE, MOE_ERR_UNSUPPORTED = 0, 1, 2, 3
 MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
 MOE_W_E4M3_B128, MOE_W_E2M1_UE8M0_G32 = 0, 1
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
+STAGES = ("router", "topk", "permute", "gateup", "down", "combine")
 WFMT = {"e4m3": MOE_W_E4M3_B128, "e2m1": MOE_W_E2M1_UE8M0_G32}
 
 
@@ -58,6 +59,12 @@ def _load():
     L.moe_workspace_h_offset.restype = i64
     L.moe_plan_path.argtypes = [vp, i32]
     L.moe_plan_path.restype = i32
+    L.moe_timing_enable.argtypes = [vp, ctypes.c_uint32, i32]
+    L.moe_timing_enable.restype = ctypes.c_int
+    L.moe_timing_collect.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
+    L.moe_timing_collect.restype = ctypes.c_int
+    L.moe_timing_disable.argtypes = [vp]
+    L.moe_timing_disable.restype = ctypes.c_int
     L.moe_plan_free.argtypes = [vp]
     L.moe_plan_free.restype = None
     L.moe_status_str.argtypes = [ctypes.c_int]
@@ -156,10 +163,34 @@ def moe_forward(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_ma
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
     if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if hasattr(workspace, "numel") else 0)
     st = lib.moe_forward(plan.handle, int(n_tokens), _ptr(x), _ptr(w_router), _ptr(logit_bias),
                          ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), _ptr(out),
                          _ptr(topk_ids), _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm),
                          _ptr(workspace), int(workspace_bytes), stream or None)
     if st != MOE_OK:
         raise MoeError(st, "moe_forward", moe_plan_info(plan))
+
+
+def moe_timing_enable(plan: Plan, stages=STAGES, max_forwards: int = 1024) -> None:
+    mask = 0
+    for st in stages:
+        mask |= 1 << (STAGES.index(st) if isinstance(st, str) else int(st))
+    st = lib.moe_timing_enable(plan.handle, mask, int(max_forwards))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_timing_enable", moe_plan_info(plan))
+
+
+def moe_timing_collect(plan: Plan):
+    """-> (dict stage -> summed ms, number of recorded forwards)."""
+    ms = (ctypes.c_float * len(STAGES))()
+    n = ctypes.c_int32()
+    st = lib.moe_timing_collect(plan.handle, ms, ctypes.byref(n))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_timing_collect", moe_plan_info(plan))
+    return {name: float(ms[i]) for i, name in enumerate(STAGES)}, int(n.value)
+
+
+def moe_timing_disable(plan: Plan) -> None:
+    lib.moe_timing_disable(plan.handle)

@@ -1,4 +1,7 @@
-"""Compile libmoe.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc."""
+"""Compile libmoe.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc.
+
+Run as a script (python mixture_experts_layer_f32_amd/build.py) or through
+__graft_entry__.build(); importing the package itself requires the library."""
 import os
 import subprocess
 import sys

@@ -5,9 +5,11 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "moe.h"
 #include "moe_common.h"
@@ -25,13 +27,12 @@ inline size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 // Tile sizes of the grouped GEMMs and the decode matvecs.
 constexpr int GEMM_BM = 64;
 constexpr int GEMM_BN = 64;
-constexpr int DEC_RPW = 2;       // rows per wavefront in the decode matvecs
-constexpr int GEMV_MAX_T = 16;   // router: one wave per expert up to this many tokens
+constexpr int GEMV_MAX_T = 256;  // router: one wave per expert up to this many tokens
 
 struct Layout {
-  size_t logits, ids, w, counts, offsets, perm, inv_perm, rank, hist, base, active, n_active,
+  size_t logits, ids, w, counts, offsets, perm, inv_perm, tok_of, rank, hist, base, slot_info, n_active,
       tiles, n_tiles, h, y, total;
-  int nchunk, max_tiles;
+  int nchunk, max_tiles, n_slots;
 };
 
 }  // namespace
@@ -42,8 +43,16 @@ struct moe_plan_s {
   int cus = 0;
   std::string arch;
   int t_decode = 0;  // AUTO: decode variant for T <= t_decode
+  int dec_nrg = 0;     // decode row groups per wavefront (0: chosen from the shape)
+  int dec_stream = 0;  // 1: register-resident activations + row-group prefetch variant
+  int dec_persist = 0; // >0: persistent decode grid of CUs * dec_persist blocks
   std::string info;
   std::string last_error;
+  // instrumentation (moe_timing_*)
+  uint32_t timing_mask = 0;
+  int timing_max = 0;
+  int timing_n = 0;
+  std::vector<hipEvent_t> timing_ev;  // [forward][stage][begin, end]
 };
 
 namespace {
@@ -60,6 +69,7 @@ Layout layout(const moe_plan_s* p, int T) {
   Layout L;
   L.nchunk = (T + WAVE - 1) / WAVE;
   L.max_tiles = (int)((S + GEMM_BM - 1) / GEMM_BM + std::min<size_t>(E, S));
+  L.n_slots = (int)std::min<size_t>(E, S);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -73,10 +83,11 @@ Layout layout(const moe_plan_s* p, int T) {
   L.offsets = take((E + 1) * 4);
   L.perm = take(S * 4);
   L.inv_perm = take(S * 4);
+  L.tok_of = take(S * 4);
   L.rank = take(S * 4);
   L.hist = take((size_t)L.nchunk * E * 4);
   L.base = take((size_t)L.nchunk * E * 4);
-  L.active = take(E * 4);
+  L.slot_info = take((size_t)L.n_slots * 16);
   L.n_active = take(4);
   L.tiles = take((size_t)L.max_tiles * 16);
   L.n_tiles = take(4);
@@ -86,6 +97,13 @@ Layout layout(const moe_plan_s* p, int T) {
   return L;
 }
 
+// Records the begin (end = false) or end event of `stage` for the current
+// forward when timing is on for that stage.
+void mark(moe_plan_s* p, int stage, bool end, hipStream_t s) {
+  if (!(p->timing_mask >> stage & 1u) || p->timing_n >= p->timing_max) return;
+  (void)hipEventRecord(p->timing_ev[((size_t)p->timing_n * MOE_N_STAGES + stage) * 2 + end], s);
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status hip_fail(moe_plan_s* p, hipError_t err, const char* what) {
@@ -93,42 +111,120 @@ moe_status hip_fail(moe_plan_s* p, hipError_t err, const char* what) {
   return MOE_ERR_HIP;
 }
 
+// Decode matvec configuration for rows of K inputs: CPL chunks of 16 inputs
+// per lane (0: rows longer than 8 passes take the looping kernel), slots per
+// pass TG (activations of TG slots x CPL chunks stay in registers), rows per
+// load group RPW.
+constexpr int dec_rpw(int cpl) { return (cpl == 0 || cpl <= 4) ? 2 : 1; }
+constexpr int dec_tgmax(int cpl) { return cpl == 0 ? 4 : (cpl == 1 ? 8 : (cpl == 2 ? 4 : (cpl <= 4 ? 2 : 1))); }
+inline int dec_cpl(int K) {
+  const int c = (K / 16 + WAVE - 1) / WAVE;
+  return c <= 8 ? c : 0;
+}
+
+template <int FMT, bool GATEUP, int TG, int CPL>
+void launch_dec_cfg(int grid_x, int N, int K, int rpw_total, int T, const uint16_t* x,
+                    const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
+                    uint16_t* hout, float* y, hipStream_t st) {
+  const dim3 g(grid_x, (N + 4 * rpw_total - 1) / (4 * rpw_total));
+  if (GATEUP)
+    dec_gateup<FMT, TG, CPL, dec_rpw(CPL)><<<g, 256, 0, st>>>(x, A, B, info, tok_of, hout, K, N, T,
+                                                             rpw_total);
+  else
+    dec_down<FMT, TG, CPL, dec_rpw(CPL)><<<g, 256, 0, st>>>(hin, A, info, y, N, K, rpw_total);
+}
+
+template <int FMT, bool GATEUP, int CPL>
+void launch_dec_cpl(int T, int grid_x, int N, int K, int rpw_total, const uint16_t* x,
+                    const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
+                    uint16_t* hout, float* y, hipStream_t st) {
+  if (T == 1)
+    launch_dec_cfg<FMT, GATEUP, 1, CPL>(grid_x, N, K, rpw_total, T, x, hin, A, B, info, tok_of,
+                                        hout, y, st);
+  else
+    launch_dec_cfg<FMT, GATEUP, dec_tgmax(CPL), CPL>(grid_x, N, K, rpw_total, T, x, hin, A, B,
+                                                     info, tok_of, hout, y, st);
+}
+
+// Gate/up (N = f rows of K = d inputs) or down (N = d rows of K = f inputs).
+template <int FMT, bool GATEUP>
+void launch_dec(moe_plan_s* p, int T, int n_slots, int N, int K, const uint16_t* x,
+                const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
+                uint16_t* hout, float* y, hipStream_t st) {
+  const int cpl = p->dec_stream ? dec_cpl(K) : 0;
+  const int rpw = dec_rpw(cpl);
+  // rows per wavefront: enough blocks to cover the chip a few times over
+  int nrg = p->dec_nrg;
+  if (nrg <= 0 && cpl == 0) nrg = 1;
+  if (nrg <= 0) {
+    const long long rows = (long long)n_slots * N;
+    nrg = (int)std::max(1LL, std::min(8LL, rows / (4LL * rpw * 4 * p->cus)));
+  }
+  const int rpw_total = rpw * nrg;
+#define MOE_DEC_CASE(C)                                                                        \
+  case C:                                                                                      \
+    launch_dec_cpl<FMT, GATEUP, C>(T, n_slots, N, K, rpw_total, x, hin, A, B, info, tok_of, \
+                                   hout, y, st);                                               \
+    break;
+  switch (cpl) {
+    MOE_DEC_CASE(0)
+    MOE_DEC_CASE(1)
+    MOE_DEC_CASE(2)
+    MOE_DEC_CASE(3)
+    MOE_DEC_CASE(4)
+    MOE_DEC_CASE(5)
+    MOE_DEC_CASE(6)
+    MOE_DEC_CASE(7)
+    MOE_DEC_CASE(8)
+  }
+#undef MOE_DEC_CASE
+}
+
 template <int FMT>
 moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, DMat U, DMat D,
-                               const Layout& L, char* ws, int32_t* counts, int32_t* offsets,
-                               int32_t* perm, hipStream_t st) {
-  const int d = p->d.d_model, f = p->d.d_ff, E = p->d.n_experts, k = p->d.top_k;
-  const int S = T * k;
-  const int32_t* active = reinterpret_cast<const int32_t*>(ws + L.active);
-  const int32_t* n_active = reinterpret_cast<const int32_t*>(ws + L.n_active);
+                               const Layout& L, char* ws, hipStream_t st) {
+  const int d = p->d.d_model, f = p->d.d_ff;
+  const int4* info = reinterpret_cast<const int4*>(ws + L.slot_info);
+  const int32_t* tok_of = reinterpret_cast<const int32_t*>(ws + L.tok_of);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* y = reinterpret_cast<float*>(ws + L.y);
-  if (path_for(p, T) == MOE_PATH_DECODE) {
-    const int slots = std::min(S, E);
-    const dim3 g1(slots, (f / DEC_RPW + 3) / 4), g2(slots, (d / DEC_RPW + 3) / 4);
-    if (T == 1) {
-      dec_gateup<FMT, 1, DEC_RPW><<<g1, 256, 0, st>>>(x, G, U, active, n_active, counts, offsets,
-                                                      perm, h, d, f, k, T);
-      dec_down<FMT, 1, DEC_RPW><<<g2, 256, 0, st>>>(h, D, active, n_active, counts, offsets, y, d,
-                                                    f);
-    } else if (T <= 2) {
-      dec_gateup<FMT, 2, DEC_RPW><<<g1, 256, 0, st>>>(x, G, U, active, n_active, counts, offsets,
-                                                      perm, h, d, f, k, T);
-      dec_down<FMT, 2, DEC_RPW><<<g2, 256, 0, st>>>(h, D, active, n_active, counts, offsets, y, d,
-                                                    f);
-    } else {
-      dec_gateup<FMT, 4, DEC_RPW><<<g1, 256, 0, st>>>(x, G, U, active, n_active, counts, offsets,
-                                                      perm, h, d, f, k, T);
-      dec_down<FMT, 4, DEC_RPW><<<g2, 256, 0, st>>>(h, D, active, n_active, counts, offsets, y, d,
-                                                    f);
-    }
+  if (path_for(p, T) == MOE_PATH_DECODE && p->dec_persist > 0) {
+    const int32_t* n_act = reinterpret_cast<const int32_t*>(ws + L.n_active);
+    const int blocks = p->cus * p->dec_persist;
+    mark(p, MOE_STAGE_GATEUP, false, st);
+    if (T == 1)
+      dec_gateup_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
+    else if (T <= 2)
+      dec_gateup_persist<FMT, 2, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
+    else
+      dec_gateup_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
+    mark(p, MOE_STAGE_GATEUP, true, st);
+    mark(p, MOE_STAGE_DOWN, false, st);
+    if (T == 1)
+      dec_down_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(h, D, info, n_act, y, d, f);
+    else if (T <= 2)
+      dec_down_persist<FMT, 2, 2><<<blocks, 256, 0, st>>>(h, D, info, n_act, y, d, f);
+    else
+      dec_down_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(h, D, info, n_act, y, d, f);
+    mark(p, MOE_STAGE_DOWN, true, st);
+  } else if (path_for(p, T) == MOE_PATH_DECODE) {
+    mark(p, MOE_STAGE_GATEUP, false, st);
+    launch_dec<FMT, true>(p, T, L.n_slots, f, d, x, nullptr, G, U, info, tok_of, h, nullptr, st);
+    mark(p, MOE_STAGE_GATEUP, true, st);
+    mark(p, MOE_STAGE_DOWN, false, st);
+    launch_dec<FMT, false>(p, T, L.n_slots, d, f, nullptr, h, D, D, info, tok_of, nullptr, y, st);
+    mark(p, MOE_STAGE_DOWN, true, st);
   } else {
     const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
     const dim3 g1(L.max_tiles, (f + GEMM_BN - 1) / GEMM_BN), g2(L.max_tiles, (d + GEMM_BN - 1) / GEMM_BN);
-    gemm_gateup<FMT, GEMM_BM, GEMM_BN><<<g1, 256, 0, st>>>(x, G, U, tiles, n_tiles, perm, h, d, f,
-                                                          k, T);
+    mark(p, MOE_STAGE_GATEUP, false, st);
+    gemm_gateup<FMT, GEMM_BM, GEMM_BN><<<g1, 256, 0, st>>>(x, G, U, tiles, n_tiles, tok_of, h, d, f,
+                                                          T);
+    mark(p, MOE_STAGE_GATEUP, true, st);
+    mark(p, MOE_STAGE_DOWN, false, st);
     gemm_down<FMT, GEMM_BM, GEMM_BN><<<g2, 256, 0, st>>>(h, D, tiles, n_tiles, y, d, f);
+    mark(p, MOE_STAGE_DOWN, true, st);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return hip_fail(p, err, "expert stage launch");
@@ -200,21 +296,84 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   p->arch = prop.gcnArchName;
   // Decode while the slots per expert stay small: T*k <= 4*E.
   p->t_decode = std::max(1, 4 * d.n_experts / d.top_k);
+  // tuning knobs of the decode matvec
+  if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
+  if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
+  if (const char* v = std::getenv("MOE_DEC_PERSIST")) p->dec_persist = std::atoi(v);
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "
                 "(decode for T<=%d); router gemv<=%d tokens else 64x64 f32 tiles; "
-                "decode matvec rows/wave=%d; grouped MFMA 32x32x16 bf16 tiles BMxBN=%dx%d",
+                "decode streaming matvec (row groups per wave %d, 0=auto); grouped MFMA 32x32x16 "
+                "bf16 tiles BMxBN=%dx%d",
                 dev, p->arch.c_str(), p->cus, d.d_model, d.d_ff, d.n_experts, d.top_k,
                 d.wfmt == MOE_W_E4M3_B128 ? "e4m3/128x128" : "e2m1/ue8m0x32", d.renorm,
                 d.path == MOE_PATH_AUTO ? "auto" : (d.path == MOE_PATH_DECODE ? "decode" : "grouped"),
-                p->t_decode, GEMV_MAX_T, DEC_RPW, GEMM_BM, GEMM_BN);
+                p->t_decode, GEMV_MAX_T, p->dec_nrg, GEMM_BM, GEMM_BN);
   p->info = buf;
   *out = p;
   return MOE_OK;
 }
 
-void moe_plan_free(moe_plan_t p) { delete p; }
+moe_status moe_timing_disable(moe_plan_t p) {
+  if (p == nullptr) return MOE_ERR_NULL_ARG;
+  for (hipEvent_t e : p->timing_ev) (void)hipEventDestroy(e);
+  p->timing_ev.clear();
+  p->timing_mask = 0;
+  p->timing_max = p->timing_n = 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_enable(moe_plan_t p, uint32_t stage_mask, int32_t max_forwards) {
+  if (p == nullptr) return MOE_ERR_NULL_ARG;
+  if (max_forwards <= 0 || max_forwards > (1 << 16) || stage_mask >> MOE_N_STAGES)
+    return MOE_ERR_BAD_SHAPE;
+  moe_timing_disable(p);
+  p->timing_ev.assign((size_t)max_forwards * MOE_N_STAGES * 2, nullptr);
+  for (int f = 0; f < max_forwards; ++f)
+    for (int st = 0; st < MOE_N_STAGES; ++st)
+      if (stage_mask >> st & 1u)
+        for (int b = 0; b < 2; ++b) {
+          hipError_t err = hipEventCreate(&p->timing_ev[((size_t)f * MOE_N_STAGES + st) * 2 + b]);
+          if (err != hipSuccess) {
+            moe_timing_disable(p);
+            return hip_fail(p, err, "hipEventCreate");
+          }
+        }
+  p->timing_mask = stage_mask;
+  p->timing_max = max_forwards;
+  p->timing_n = 0;
+  return MOE_OK;
+}
+
+moe_status moe_timing_collect(moe_plan_t p, float* stage_ms, int32_t* n_forwards) {
+  if (p == nullptr || stage_ms == nullptr) return MOE_ERR_NULL_ARG;
+  for (int st = 0; st < MOE_N_STAGES; ++st) stage_ms[st] = 0.0f;
+  const int n = p->timing_n;
+  if (n_forwards) *n_forwards = n;
+  if (n == 0 || p->timing_mask == 0) return MOE_OK;
+  int last = MOE_N_STAGES - 1;
+  while (!(p->timing_mask >> last & 1u)) --last;
+  hipError_t err = hipEventSynchronize(p->timing_ev[((size_t)(n - 1) * MOE_N_STAGES + last) * 2 + 1]);
+  if (err != hipSuccess) return hip_fail(p, err, "hipEventSynchronize");
+  for (int f = 0; f < n; ++f)
+    for (int st = 0; st < MOE_N_STAGES; ++st) {
+      if (!(p->timing_mask >> st & 1u)) continue;
+      float ms = 0.0f;
+      const size_t i = ((size_t)f * MOE_N_STAGES + st) * 2;
+      err = hipEventElapsedTime(&ms, p->timing_ev[i], p->timing_ev[i + 1]);
+      if (err != hipSuccess) return hip_fail(p, err, "hipEventElapsedTime");
+      stage_ms[st] += ms;
+    }
+  p->timing_n = 0;
+  return MOE_OK;
+}
+
+void moe_plan_free(moe_plan_t p) {
+  if (p == nullptr) return;
+  moe_timing_disable(p);
+  delete p;
+}
 
 const char* moe_plan_info(moe_plan_t p) {
   if (p == nullptr) return "";
@@ -282,6 +441,7 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   int32_t* base = reinterpret_cast<int32_t*>(ws + L.base);
 
   // a1: router logits
+  mark(p, MOE_STAGE_ROUTER, false, s);
   if (T <= GEMV_MAX_T) {
     const dim3 g((E + 3) / 4);
     if (T == 1)
@@ -294,16 +454,22 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
     const dim3 g((T + 63) / 64, (E + 63) / 64);
     router_gemm<<<g, 256, 0, s>>>(x, w_router, logit_bias, logits, T, d, E);
   }
+  mark(p, MOE_STAGE_ROUTER, true, s);
   // a2: softmax + top-k
+  mark(p, MOE_STAGE_TOPK, false, s);
   route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, T, E, k, p->d.renorm);
+  mark(p, MOE_STAGE_TOPK, true, s);
   // a3: counting-sort permute
+  mark(p, MOE_STAGE_PERMUTE, false, s);
   permute_count<<<L.nchunk, WAVE, 0, s>>>(ids, rank, hist, T, E, k);
-  permute_scan<<<1, 1024, 0, s>>>(hist, base, cnt, off, reinterpret_cast<int32_t*>(ws + L.active),
-                                  reinterpret_cast<int32_t*>(ws + L.n_active),
-                                  reinterpret_cast<int4*>(ws + L.tiles),
+  permute_scan<<<1, 1024, 0, s>>>(hist, base, cnt, off, reinterpret_cast<int4*>(ws + L.slot_info),
+                                  reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots, reinterpret_cast<int4*>(ws + L.tiles),
                                   reinterpret_cast<int32_t*>(ws + L.n_tiles), L.nchunk, E, S,
                                   GEMM_BM);
-  permute_scatter<<<(S + 255) / 256, 256, 0, s>>>(ids, rank, base, off, prm, inv, S, E, k);
+  permute_scatter<<<(S + 255) / 256, 256, 0, s>>>(ids, rank, base, off, prm, inv,
+                                                  reinterpret_cast<int32_t*>(ws + L.tok_of), S, E,
+                                                  k);
+  mark(p, MOE_STAGE_PERMUTE, true, s);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return hip_fail(p, err, "routing launch");
 
@@ -315,13 +481,16 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   const DMat D{static_cast<const uint8_t*>(down->q), static_cast<const uint8_t*>(down->scale),
                down->q_expert_stride, down->s_expert_stride};
   st = p->d.wfmt == MOE_W_E4M3_B128
-           ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, cnt, off, prm, s)
-           : launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, cnt, off, prm, s);
+           ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, s)
+           : launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, s);
   if (st != MOE_OK) return st;
 
   // a6: fixed-order combine
+  mark(p, MOE_STAGE_COMBINE, false, s);
   combine_fixed_order<<<dim3(T, (d / 4 + 255) / 256), 256, 0, s>>>(
       reinterpret_cast<const float*>(ws + L.y), w, inv, out, d, k);
+  mark(p, MOE_STAGE_COMBINE, true, s);
+  if (p->timing_mask && p->timing_n < p->timing_max) ++p->timing_n;
   err = hipGetLastError();
   if (err != hipSuccess) return hip_fail(p, err, "combine launch");
   return MOE_OK;

@@ -22,14 +22,17 @@ struct DMat {
 };
 
 // A "chunk" is 16 consecutive inputs of one weight row: 16 bytes of e4m3
-// codes or 8 bytes of e2m1 codes.  These helpers return the dot product of
-// one chunk with 16 activations (already f32), including the scale.
+// codes or 8 bytes of e2m1 codes.  A chunk is decoded once into 8 exact bf16
+// pairs (e4m3 values are bf16 values; an e2m1 value times its power-of-two
+// scale is a bf16 value) and dotted with each token's 16 bf16 activations by
+// v_dot2_f32_bf16, whose products are exact in f32.
 template <int FMT>
 struct Chunk;
 
 template <>
 struct Chunk<FMT_E4M3> {
   typedef u32x4 raw;
+  static constexpr bool kPostScale = true;  // scale applied to the chunk's partial sum
   static __device__ __forceinline__ raw load(const uint8_t* row, int c) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + c);
   }
@@ -37,22 +40,20 @@ struct Chunk<FMT_E4M3> {
   static __device__ __forceinline__ float scale(const uint8_t* s, int n, int c, int K) {
     return reinterpret_cast<const float*>(s)[(n >> 7) * (K >> 7) + (c >> 3)];
   }
-  static __device__ __forceinline__ float dot(raw w, float sc, const float* xv) {
-    float p = 0.0f;
+  static __device__ __forceinline__ void decode(raw w, float, bf16x2 (&o)[8]) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x2 a = e4m3x2_to_f32<false>(ws[i]);
-      const f32x2 b = e4m3x2_to_f32<true>(ws[i]);
-      p += a.x * xv[4 * i] + a.y * xv[4 * i + 1] + b.x * xv[4 * i + 2] + b.y * xv[4 * i + 3];
+      o[2 * i] = e4m3x2_to_bf16<false>(ws[i]);
+      o[2 * i + 1] = e4m3x2_to_bf16<true>(ws[i]);
     }
-    return p * sc;
   }
 };
 
 template <>
 struct Chunk<FMT_E2M1> {
   typedef u32x2 raw;
+  static constexpr bool kPostScale = false;  // scale applied exactly inside the conversion
   static __device__ __forceinline__ raw load(const uint8_t* row, int c) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row) + c);
   }
@@ -60,20 +61,15 @@ struct Chunk<FMT_E2M1> {
   static __device__ __forceinline__ float scale(const uint8_t* s, int n, int c, int K) {
     return ue8m0_to_f32(s[(size_t)n * (K >> 5) + (c >> 1)]);
   }
-  static __device__ __forceinline__ float dot(raw w, float sc, const float* xv) {
-    float p = 0.0f;
-    const uint32_t ws[2] = {w.x, w.y};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const f32x2 a = e2m1x2_to_f32<0>(ws[i], sc);
-      const f32x2 b = e2m1x2_to_f32<1>(ws[i], sc);
-      const f32x2 c2 = e2m1x2_to_f32<2>(ws[i], sc);
-      const f32x2 d2 = e2m1x2_to_f32<3>(ws[i], sc);
-      p += a.x * xv[8 * i] + a.y * xv[8 * i + 1] + b.x * xv[8 * i + 2] + b.y * xv[8 * i + 3] +
-           c2.x * xv[8 * i + 4] + c2.y * xv[8 * i + 5] + d2.x * xv[8 * i + 6] +
-           d2.y * xv[8 * i + 7];
-    }
-    return p;  // the scale is applied exactly inside the conversion
+  static __device__ __forceinline__ void decode(raw w, float sc, bf16x2 (&o)[8]) {
+    o[0] = e2m1x2_to_bf16<0>(w.x, sc);
+    o[1] = e2m1x2_to_bf16<1>(w.x, sc);
+    o[2] = e2m1x2_to_bf16<2>(w.x, sc);
+    o[3] = e2m1x2_to_bf16<3>(w.x, sc);
+    o[4] = e2m1x2_to_bf16<0>(w.y, sc);
+    o[5] = e2m1x2_to_bf16<1>(w.y, sc);
+    o[6] = e2m1x2_to_bf16<2>(w.y, sc);
+    o[7] = e2m1x2_to_bf16<3>(w.y, sc);
   }
 };
 
@@ -82,132 +78,304 @@ __device__ __forceinline__ int64_t row_bytes(int K) {
   return FMT == FMT_E4M3 ? (int64_t)K : (int64_t)K / 2;
 }
 
-// 16 bf16 activations starting at input 16c of a row -> f32.
-__device__ __forceinline__ void load_act16(const uint16_t* row, int c, float* xv) {
+// 16 bf16 activations (inputs 16c .. 16c+15 of a row) as 8 packed pairs.
+__device__ __forceinline__ void load_act16(const uint16_t* row, int c, uint32_t (&v)[8]) {
   const u32x4* p = reinterpret_cast<const u32x4*>(row + 16 * c);
   const u32x4 a = p[0], b = p[1];
-  const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    xv[2 * i] = bf16_lo(v[i]);
-    xv[2 * i + 1] = bf16_hi(v[i]);
-  }
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// Gate/up + SwiGLU.  grid.x: index into the list of experts that received at
-// least one slot (blocks past its length exit); grid.y: groups of 4*RPW rows
-// of f.  For every slot of the expert, in sorted order, writes
-// h[p][n] = bf16(silu(g[n]) * u[n]) at sorted position p.
-template <int FMT, int TG, int RPW>
-__global__ __launch_bounds__(256) void dec_gateup(
-    const uint16_t* __restrict__ x, DMat gate, DMat up, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-    uint16_t* __restrict__ h, int d, int f, int k, int T) {
-  if ((int)blockIdx.x >= *n_active) return;
-  const int e = active[blockIdx.x];
-  const int p0 = offsets[e], cnt = counts[e];
-  const int n0 = (blockIdx.y * 4 + wave_id()) * RPW;
-  if (n0 >= f) return;
+// sum over 16 inputs of w * x, f32 (exact products, v_dot2_f32_bf16 chain)
+__device__ __forceinline__ float dot16(const bf16x2 (&w)[8], const uint32_t (&x)[8]) {
+  float p = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    p = __builtin_amdgcn_fdot2_f32_bf16(w[q], __builtin_bit_cast(bf16x2, x[q]), p, false);
+  return p;
+}
+
+// Decode matvec over the experts that received at least one slot.
+// grid.x: index into that list (entries past its length hold expert -1 and
+// their blocks exit at once);
+// grid.y: groups of 4*RPW weight rows (one wavefront per RPW rows).
+// NM weight matrices share the rows (2: gate and up, 1: down).  Each lane
+// takes chunks c = lane, lane+64, ... of every row; all of a pass's chunks
+// are loaded before any is used.  Token slots are handled TG at a time;
+// empty slots of the last group are skipped with a wave-uniform branch.
+// The per-(row, slot) sums are reduced across the wavefront at the end.
+template <int FMT, int NM, int TG, int RPW, int U, typename ActRow, typename Store>
+__device__ __forceinline__ void dec_matvec(const uint8_t* const (&q)[NM],
+                                           const uint8_t* const (&s)[NM], int n0, int K, int cnt,
+                                           ActRow act_row, Store store) {
   const int lane = lane_id();
-  const int nch = d / 16;
-  const int64_t rb = row_bytes<FMT>(d);
-  const uint8_t* gq = gate.q + e * gate.qs + n0 * rb;
-  const uint8_t* uq = up.q + e * up.qs + n0 * rb;
-  const uint8_t* gs = gate.s + e * gate.ss;
-  const uint8_t* us = up.s + e * up.ss;
+  const int nch = K / 16;
+  const int64_t rb = row_bytes<FMT>(K);
   for (int t0 = 0; t0 < cnt; t0 += TG) {
-    const uint16_t* xr[TG];
+    const int ntok = min(TG, cnt - t0);
+    const uint16_t* ar[TG];
 #pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      const int r = min(t0 + t, cnt - 1);
-      xr[t] = x + (size_t)min((uint32_t)perm[p0 + r] / (uint32_t)k, (uint32_t)(T - 1)) * d;
-    }
-    float ag[RPW][TG], au[RPW][TG];
+    for (int t = 0; t < TG; ++t) ar[t] = act_row(t0 + min(t, ntok - 1));
+    float acc[NM][RPW][TG];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int t = 0; t < TG; ++t) ag[r][t] = au[r][t] = 0.0f;
-    for (int c = lane; c < nch; c += WAVE) {
-      typename Chunk<FMT>::raw wg[RPW], wu[RPW];
+      for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        wg[r] = Chunk<FMT>::load(gq + r * rb, c);
-        wu[r] = Chunk<FMT>::load(uq + r * rb, c);
+        for (int t = 0; t < TG; ++t) acc[m][r][t] = 0.0f;
+    for (int c0 = lane; c0 < nch; c0 += WAVE * U) {
+      typename Chunk<FMT>::raw w[U][NM][RPW];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + WAVE * u;
+        if (c < nch) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) w[u][m][r] = Chunk<FMT>::load(q[m] + r * rb, c);
+        }
       }
-      float xv[TG][16];
 #pragma unroll
-      for (int t = 0; t < TG; ++t) load_act16(xr[t], c, xv[t]);
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + WAVE * u;
+        if (c < nch) {
+          uint32_t xv[TG][8];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float sg = Chunk<FMT>::scale(gs, n0 + r, c, d);
-        const float su = Chunk<FMT>::scale(us, n0 + r, c, d);
+          for (int t = 0; t < TG; ++t)
+            if (t < ntok) load_act16(ar[t], c, xv[t]);
 #pragma unroll
-        for (int t = 0; t < TG; ++t) {
-          ag[r][t] += Chunk<FMT>::dot(wg[r], sg, xv[t]);
-          au[r][t] += Chunk<FMT>::dot(wu[r], su, xv[t]);
+          for (int m = 0; m < NM; ++m) {
+            // e4m3: the RPW rows (RPW divides 128, n0 a multiple of RPW) share one 128-row block
+            const float sc0 = Chunk<FMT>::scale(s[m], n0, c, K);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+              const float sc = Chunk<FMT>::kPostScale ? sc0 : Chunk<FMT>::scale(s[m], n0 + r, c, K);
+              bf16x2 wb[8];
+              Chunk<FMT>::decode(w[u][m][r], sc, wb);
+#pragma unroll
+              for (int t = 0; t < TG; ++t)
+                if (t < ntok) {
+                  const float p = dot16(wb, xv[t]);
+                  acc[m][r][t] = Chunk<FMT>::kPostScale ? fmaf(p, sc, acc[m][r][t])
+                                                        : acc[m][r][t] + p;
+                }
+            }
+          }
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int t = 0; t < TG; ++t) {
-        const float g = wave_sum(ag[r][t]);
-        const float u = wave_sum(au[r][t]);
-        if (lane == r * TG + t && t0 + t < cnt)
-          h[(size_t)(p0 + t0 + t) * f + n0 + r] = (uint16_t)f32_to_bf16_rne(silu(g) * u);
+      for (int t = 0; t < TG; ++t)
+        if (t < ntok) {
+          float v[NM];
+#pragma unroll
+          for (int m = 0; m < NM; ++m) v[m] = wave_sum(acc[m][r][t]);
+          if (lane == r * TG + t) store(t0 + t, r, v);
+        }
+  }
+}
+
+// Streaming variant for rows that fit one pass (K <= 16 * 64 * CPL): every
+// lane owns chunks lane, lane+64, ..., lane+64*(CPL-1) of every row.  A
+// wavefront walks NRG groups of RPW consecutive rows of one expert: the
+// slots' activation chunks are loaded into registers once, and the next
+// row group's weights are loaded before the current group is decoded,
+// multiplied and reduced, so the weight stream does not stall on the
+// reductions.
+template <int FMT, int NM, int TG, int CPL, int RPW, typename ActRow, typename Store>
+__device__ __forceinline__ void dec_stream(const uint8_t* const (&q)[NM],
+                                           const uint8_t* const (&s)[NM], int n0, int nrows,
+                                           int K, int cnt, ActRow act_row, Store store) {
+  const int lane = lane_id();
+  const int nch = K / 16;
+  const int64_t rb = row_bytes<FMT>(K);
+  typedef typename Chunk<FMT>::raw raw;
+  for (int t0 = 0; t0 < cnt; t0 += TG) {
+    const int ntok = min(TG, cnt - t0);
+    uint32_t xv[TG][CPL][8];
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+      if (t < ntok) {
+        const uint16_t* a = act_row(t0 + t);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = lane + WAVE * j;
+          if (c < nch) load_act16(a, c, xv[t][j]);
+        }
       }
+    raw wc[NM][RPW][CPL], wn[NM][RPW][CPL];
+    auto load_group = [&](raw (&w)[NM][RPW][CPL], int r0) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            const int c = lane + WAVE * j;
+            if (c < nch && r0 + r < nrows) w[m][r][j] = Chunk<FMT>::load(q[m] + (r0 + r) * rb, c);
+          }
+    };
+    load_group(wc, 0);
+    for (int r0 = 0; r0 < nrows; r0 += RPW) {
+      if (r0 + RPW < nrows) load_group(wn, r0 + RPW);
+      float acc[NM][RPW][TG];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int t = 0; t < TG; ++t) acc[m][r][t] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            const int c = lane + WAVE * j;
+            if (c < nch) {
+              const float sc = Chunk<FMT>::scale(s[m], n0 + r0 + r, c, K);
+              bf16x2 wb[8];
+              Chunk<FMT>::decode(wc[m][r][j], sc, wb);
+#pragma unroll
+              for (int t = 0; t < TG; ++t)
+                if (t < ntok) {
+                  const float p = dot16(wb, xv[t][j]);
+                  acc[m][r][t] = Chunk<FMT>::kPostScale ? fmaf(p, sc, acc[m][r][t])
+                                                        : acc[m][r][t] + p;
+                }
+            }
+          }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int t = 0; t < TG; ++t)
+          if (t < ntok && r0 + r < nrows) {
+            float v[NM];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) v[m] = wave_sum(acc[m][r][t]);
+            if (lane == r * TG + t) store(t0 + t, r0 + r, v);
+          }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) wc[m][r][j] = wn[m][r][j];
+    }
+  }
+}
+
+// Gate/up + SwiGLU: for every slot of the expert (sorted position p),
+// h[p][n] = bf16(silu(g[n]) * u[n]).  grid.x: slot_info entry; grid.y:
+// blocks of 4 wavefronts x `rpw_total` rows.  CPL = 0 selects the looping
+// matvec (rows longer than one pass).
+template <int FMT, int TG, int CPL, int RPW>
+__global__ __launch_bounds__(256) void dec_gateup(
+    const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ slot_info,
+    const int32_t* __restrict__ tok_of, uint16_t* __restrict__ h, int d, int f, int T,
+    int rpw_total) {
+  const int4 info = slot_info[blockIdx.x];
+  if (info.x < 0) return;
+  const int e = info.x, p0 = info.y, cnt = info.z;
+  const int n0 = (blockIdx.y * 4 + wave_id()) * rpw_total;
+  if (n0 >= f) return;
+  const int nrows = min(rpw_total, f - n0);
+  const int64_t rb = row_bytes<FMT>(d);
+  const uint8_t* const q[2] = {gate.q + e * gate.qs + n0 * rb, up.q + e * up.qs + n0 * rb};
+  const uint8_t* const s[2] = {gate.s + e * gate.ss, up.s + e * up.ss};
+  auto act_row = [&](int i) -> const uint16_t* {
+    return x + (size_t)min((uint32_t)tok_of[p0 + i], (uint32_t)(T - 1)) * d;
+  };
+  auto store = [&](int i, int r, const float (&v)[2]) {
+    h[(size_t)(p0 + i) * f + n0 + r] = (uint16_t)f32_to_bf16_rne(silu(v[0]) * v[1]);
+  };
+  if (CPL == 0) {
+    for (int r0 = 0; r0 < nrows; r0 += RPW) {
+      const uint8_t* const qq[2] = {q[0] + r0 * rb, q[1] + r0 * rb};
+      auto st2 = [&](int i, int r, const float (&v)[2]) { store(i, r0 + r, v); };
+      dec_matvec<FMT, 2, TG, RPW, 2>(qq, s, n0 + r0, d, cnt, act_row, st2);
+    }
+  } else {
+    dec_stream<FMT, 2, TG, (CPL > 0 ? CPL : 1), RPW>(q, s, n0, nrows, d, cnt, act_row, store);
   }
 }
 
 // Down projection: y[p][m] = sum_n h[p][n] Wd[m][n] (f32) for every sorted
-// position p of the expert; grid as dec_gateup with rows m of d.
-template <int FMT, int TG, int RPW>
+// position p of the expert.
+template <int FMT, int TG, int CPL, int RPW>
 __global__ __launch_bounds__(256) void dec_down(
-    const uint16_t* __restrict__ h, DMat down, const int32_t* __restrict__ active,
-    const int32_t* __restrict__ n_active, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, float* __restrict__ y, int d, int f) {
-  if ((int)blockIdx.x >= *n_active) return;
-  const int e = active[blockIdx.x];
-  const int p0 = offsets[e], cnt = counts[e];
-  const int m0 = (blockIdx.y * 4 + wave_id()) * RPW;
+    const uint16_t* __restrict__ h, DMat down, const int4* __restrict__ slot_info,
+    float* __restrict__ y, int d, int f, int rpw_total) {
+  const int4 info = slot_info[blockIdx.x];
+  if (info.x < 0) return;
+  const int e = info.x, p0 = info.y, cnt = info.z;
+  const int m0 = (blockIdx.y * 4 + wave_id()) * rpw_total;
   if (m0 >= d) return;
-  const int lane = lane_id();
-  const int nch = f / 16;
+  const int nrows = min(rpw_total, d - m0);
   const int64_t rb = row_bytes<FMT>(f);
-  const uint8_t* dq = down.q + e * down.qs + m0 * rb;
-  const uint8_t* ds = down.s + e * down.ss;
-  for (int t0 = 0; t0 < cnt; t0 += TG) {
-    const uint16_t* hr[TG];
-#pragma unroll
-    for (int t = 0; t < TG; ++t) hr[t] = h + (size_t)(p0 + min(t0 + t, cnt - 1)) * f;
-    float acc[RPW][TG];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int t = 0; t < TG; ++t) acc[r][t] = 0.0f;
-    for (int c = lane; c < nch; c += WAVE) {
-      typename Chunk<FMT>::raw wd[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) wd[r] = Chunk<FMT>::load(dq + r * rb, c);
-      float hv[TG][16];
-#pragma unroll
-      for (int t = 0; t < TG; ++t) load_act16(hr[t], c, hv[t]);
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const float sd = Chunk<FMT>::scale(ds, m0 + r, c, f);
-#pragma unroll
-        for (int t = 0; t < TG; ++t) acc[r][t] += Chunk<FMT>::dot(wd[r], sd, hv[t]);
-      }
+  const uint8_t* const q[1] = {down.q + e * down.qs + m0 * rb};
+  const uint8_t* const s[1] = {down.s + e * down.ss};
+  auto act_row = [&](int i) -> const uint16_t* { return h + (size_t)(p0 + i) * f; };
+  auto store = [&](int i, int r, const float (&v)[1]) { y[(size_t)(p0 + i) * d + m0 + r] = v[0]; };
+  if (CPL == 0) {
+    for (int r0 = 0; r0 < nrows; r0 += RPW) {
+      const uint8_t* const qq[1] = {q[0] + r0 * rb};
+      auto st1 = [&](int i, int r, const float (&v)[1]) { store(i, r0 + r, v); };
+      dec_matvec<FMT, 1, TG, RPW, 2>(qq, s, m0 + r0, f, cnt, act_row, st1);
     }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int t = 0; t < TG; ++t) {
-        const float v = wave_sum(acc[r][t]);
-        if (lane == r * TG + t && t0 + t < cnt) y[(size_t)(p0 + t0 + t) * d + m0 + r] = v;
-      }
+  } else {
+    dec_stream<FMT, 1, TG, (CPL > 0 ? CPL : 1), RPW>(q, s, m0, nrows, f, cnt, act_row, store);
+  }
+}
+
+// Persistent variant: a fixed grid of wavefronts walks the work items
+// (expert slot i, group of RPW rows) in a grid-stride loop, item = i * G + g
+// with G = ceil(N / RPW), so neighbouring wavefronts read neighbouring rows
+// of the same expert and no workgroup is launched per item.
+template <int FMT, int TG, int RPW>
+__global__ __launch_bounds__(256) void dec_gateup_persist(
+    const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ slot_info,
+    const int32_t* __restrict__ n_active, const int32_t* __restrict__ tok_of,
+    uint16_t* __restrict__ h, int d, int f, int T) {
+  const int G = (f + RPW - 1) / RPW;
+  const int items = *n_active * G;
+  const int W = gridDim.x * 4;
+  const int64_t rb = row_bytes<FMT>(d);
+  for (int item = blockIdx.x * 4 + wave_id(); item < items; item += W) {
+    const int i = item / G, n0 = (item - i * G) * RPW;
+    const int4 info = slot_info[i];
+    const int e = info.x, p0 = info.y, cnt = info.z;
+    const uint8_t* const q[2] = {gate.q + e * gate.qs + n0 * rb, up.q + e * up.qs + n0 * rb};
+    const uint8_t* const s[2] = {gate.s + e * gate.ss, up.s + e * up.ss};
+    auto act_row = [&](int j) -> const uint16_t* {
+      return x + (size_t)min((uint32_t)tok_of[p0 + j], (uint32_t)(T - 1)) * d;
+    };
+    auto store = [&](int j, int r, const float (&v)[2]) {
+      h[(size_t)(p0 + j) * f + n0 + r] = (uint16_t)f32_to_bf16_rne(silu(v[0]) * v[1]);
+    };
+    dec_matvec<FMT, 2, TG, RPW, 2>(q, s, n0, d, cnt, act_row, store);
+  }
+}
+
+template <int FMT, int TG, int RPW>
+__global__ __launch_bounds__(256) void dec_down_persist(
+    const uint16_t* __restrict__ h, DMat down, const int4* __restrict__ slot_info,
+    const int32_t* __restrict__ n_active, float* __restrict__ y, int d, int f) {
+  const int G = (d + RPW - 1) / RPW;
+  const int items = *n_active * G;
+  const int W = gridDim.x * 4;
+  const int64_t rb = row_bytes<FMT>(f);
+  for (int item = blockIdx.x * 4 + wave_id(); item < items; item += W) {
+    const int i = item / G, m0 = (item - i * G) * RPW;
+    const int4 info = slot_info[i];
+    const int e = info.x, p0 = info.y, cnt = info.z;
+    const uint8_t* const q[1] = {down.q + e * down.qs + m0 * rb};
+    const uint8_t* const s[1] = {down.s + e * down.ss};
+    auto act_row = [&](int j) -> const uint16_t* { return h + (size_t)(p0 + j) * f; };
+    auto store = [&](int j, int r, const float (&v)[1]) { y[(size_t)(p0 + j) * d + m0 + r] = v[0]; };
+    dec_matvec<FMT, 1, TG, RPW, 2>(q, s, m0, f, cnt, act_row, store);
   }
 }
 

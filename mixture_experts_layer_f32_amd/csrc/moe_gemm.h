@@ -144,8 +144,8 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
 template <int FMT, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_gateup(
     const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ tiles,
-    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ perm,
-    uint16_t* __restrict__ h, int d, int f, int k, int T) {
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
+    uint16_t* __restrict__ h, int d, int f, int T) {
   constexpr int BK = GemmCfg<FMT>::BK, LDK = GemmCfg<FMT>::LDK;
   constexpr int TM = BM / 64, TN = BN / 64;
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void gemm_gateup(
   const int lane = lane_id(), wv = wave_id();
   const int wm0 = (wv >> 1) * (BM / 2), wn0 = (wv & 1) * (BN / 2);
   for (int r = threadIdx.x; r < BM; r += 256)
-    tok[r] = r < rows ? (int)min((uint32_t)perm[p_start + r] / (uint32_t)k, (uint32_t)(T - 1)) : -1;
+    tok[r] = r < rows ? (int)min((uint32_t)tok_of[p_start + r], (uint32_t)(T - 1)) : -1;
   __syncthreads();
   const uint8_t* gq = gate.q + e * gate.qs;
   const uint8_t* uq = up.q + e * up.qs;

@@ -108,11 +108,22 @@ __global__ __launch_bounds__(256) void router_gemm(const uint16_t* __restrict__ 
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 16;
 
+// Order-preserving map of f32 to uint32: a > b  <=>  key(a) > key(b).
+// NaN (outside the contract) maps to 0, below every other value.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if (v != v) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-// Selection takes k rounds of a wave-wide arg-max under the order
-// (logit descending, index ascending), so equal logits go to the lower index.
-// The k winners are then listed in ascending expert id with their softmax
-// probabilities (renormalised over the k when `renorm`).
+// Selection is a radix select on the order keys: 32 rounds of wave ballots
+// build the k-th largest key K bit by bit (the largest value with at least k
+// keys >= it).  Every expert above K is selected, and of those equal to K the
+// lowest indices fill the remaining places, so equal logits go to the lower
+// index.  Each selected expert's place in ascending id order comes from the
+// ballot masks; its weight is its softmax probability over all E experts
+// (max-subtracted), divided by the sum over the k when `renorm`.
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
                                                   int32_t* __restrict__ ids,
                                                   float* __restrict__ w, int T, int E, int k,
@@ -120,69 +131,73 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
   const int t = blockIdx.x * 4 + wave_id();
   if (t >= T) return;
   const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;
   constexpr int NPL = MAX_E / WAVE;
+  const int groups = (E + WAVE - 1) / WAVE;
   float l[NPL];
+  uint32_t key[NPL];
   const float* row = logits + (size_t)t * E;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + WAVE * i;
-    const float v = e < E ? row[e] : -INFINITY;
-    l[i] = (v == v) ? v : -INFINITY;  // NaN (outside the contract) ranks lowest, keeping the order total
+    const float v = (i < groups && e < E) ? row[e] : -INFINITY;
+    l[i] = (v == v) ? v : -INFINITY;
+    key[i] = order_key(v);
+  }
+  auto valid = [&](int i) { return lane + WAVE * i < E; };
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (i < groups) n += __popcll(__ballot(valid(i) && key[i] >= cand));
+    if (n >= k) thr = cand;
+  }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i)
+    if (i < groups) above += __popcll(__ballot(valid(i) && key[i] > thr));
+  const int need = k - above;  // places left for keys equal to the threshold
+  uint32_t sel = 0;            // bit i: expert lane + 64 i is selected
+  int ties_before = 0, sel_before = 0, pos[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    pos[i] = 0;
+    if (i < groups) {
+      const uint64_t tie = __ballot(valid(i) && key[i] == thr);
+      const bool take = valid(i) && (key[i] > thr ||
+                                     (key[i] == thr && ties_before + __popcll(tie & below) < need));
+      const uint64_t sm = __ballot(take);
+      if (take) {
+        sel |= 1u << i;
+        pos[i] = sel_before + __popcll(sm & below);
+      }
+      ties_before += __popcll(tie);
+      sel_before += __popcll(sm);
+    }
   }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) m = fmaxf(m, l[i]);
   m = wave_max(m);
-  float z = 0.0f;
+  float z = 0.0f, ps = 0.0f;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + WAVE * i;
-    if (e < E) z += __expf(l[i] - m);
-  }
+  for (int i = 0; i < NPL; ++i)
+    if (i < groups && valid(i)) {
+      const float ex = __expf(l[i] - m);
+      z += ex;
+      if (sel >> i & 1u) ps += ex;
+    }
   z = wave_sum(z);
-
-  // Round r's winner is kept by lane r.
-  int my_id = 0;
-  float my_l = -INFINITY;
-  uint32_t taken = 0;  // bit i: l[i] already selected
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
+  ps = wave_sum(ps) / z;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + WAVE * i;
-      if (e < E && !(taken >> i & 1u) && (l[i] > bv || be == 0x7FFFFFFF)) {
-        bv = l[i];
-        be = e;
-      }
+  for (int i = 0; i < NPL; ++i)
+    if (sel >> i & 1u) {
+      const float p = __expf(l[i] - m) / z;
+      ids[(size_t)t * k + pos[i]] = lane + WAVE * i;
+      w[(size_t)t * k + pos[i]] = renorm ? p / ps : p;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, WAVE);
-      const int oe = __shfl_xor(be, o, WAVE);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (lane == r) {
-      my_id = be;
-      my_l = bv;
-    }
-    if ((be & (WAVE - 1)) == lane) taken |= 1u << (be / WAVE);
-  }
-  // position of this lane's id in ascending order among the k winners
-  int pos = 0;
-  for (int j = 0; j < k; ++j) {
-    const int oid = __shfl(my_id, j, WAVE);
-    pos += (oid < my_id) ? 1 : 0;
-  }
-  const float p = lane < k ? __expf(my_l - m) / z : 0.0f;
-  const float psum = wave_sum(p);
-  if (lane < k) {
-    ids[(size_t)t * k + pos] = min(max(my_id, 0), E - 1);
-    w[(size_t)t * k + pos] = renorm ? p / psum : p;
-  }
 }
 
 // ---------------------------------------------------------------- permute
@@ -247,16 +262,17 @@ __device__ inline int block_exclusive_scan(int v, int* total) {
 }
 
 // One block of 1024 threads, thread e per expert: base[c][e] = slots of
-// expert e in chunks before c; counts, offsets (exclusive scan over e), the
-// ascending list of experts with at least one slot, and the grouped-GEMM
-// tile list: for every expert, ceil(count/BM) tiles of (expert, first sorted
-// position, rows).
+// expert e in chunks before c; counts, offsets (exclusive scan over e);
+// slot_info[i] = (expert, first sorted position, count) for the i-th expert,
+// in ascending order, that received at least one slot, and (-1, 0, 0) for
+// the remaining entries up to n_slots; and the grouped-GEMM tile list: for
+// every expert, ceil(count/BM) tiles of (expert, first sorted position, rows).
 __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__ hist,
                                                      int32_t* __restrict__ base,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ active,
-                                                     int32_t* __restrict__ n_active,
+                                                     int4* __restrict__ slot_info,
+                                                     int32_t* __restrict__ n_active, int n_slots,
                                                      int4* __restrict__ tiles,
                                                      int32_t* __restrict__ n_tiles, int nchunk,
                                                      int E, int S, int BM) {
@@ -274,8 +290,9 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   if (e < E) offsets[e] = off;
   if (e == 0) offsets[E] = S;
   const int act = block_exclusive_scan((e < E && c_e > 0) ? 1 : 0, &tot);
-  if (e < E && c_e > 0) active[act] = e;
+  if (e < E && c_e > 0) slot_info[act] = make_int4(e, off, c_e, 0);
   if (e == 0) *n_active = tot;
+  for (int i = tot + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
   const int mt = (e < E) ? (c_e + BM - 1) / BM : 0;
   const int tb = block_exclusive_scan(mt, &tot);
   for (int i = 0; i < mt; ++i) {
@@ -285,20 +302,25 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   if (e == 0) *n_tiles = tot;
 }
 
-// perm[offsets[e] + base[chunk][e] + rank[s]] = s; inv_perm[s] = that position.
+// perm[offsets[e] + base[chunk][e] + rank[s]] = s; inv_perm[s] = that
+// position; tok_of[that position] = s / k, the slot's token.
 __global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict__ ids,
                                                        const int32_t* __restrict__ rank,
                                                        const int32_t* __restrict__ base,
                                                        const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm,
-                                                       int32_t* __restrict__ inv_perm, int S,
+                                                       int32_t* __restrict__ inv_perm,
+                                                       int32_t* __restrict__ tok_of, int S,
                                                        int E, int k) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= S) return;
   const int e = min(max(ids[s], 0), E - 1);
   const int chunk = (s / k) / WAVE;
   const int p = offsets[e] + base[(size_t)chunk * E + e] + rank[s];
-  if (p >= 0 && p < S) perm[p] = s;
+  if (p >= 0 && p < S) {
+    perm[p] = s;
+    tok_of[p] = s / k;
+  }
   inv_perm[s] = min(max(p, 0), S - 1);
 }
 

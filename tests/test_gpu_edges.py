@@ -1,0 +1,170 @@
+"""GPU edge cases: argument errors (checked on the host before any launch),
+empty and maximal batches, routing extremes forced through the logit bias
+(every token on one expert, exact ties), zero input, the one-block-per-
+expert weight layout described by strides, and non-finite input rows."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import check_h, check_out, check_routing, device_weights, gpu_run, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.Workload("edge-e4m3", 256, 384, 6, 2, "e4m3", True, (9,), False, 4001)
+WL4 = synth.Workload("edge-e2m1", 128, 96, 8, 3, "e2m1", False, (9,), False, 4002)
+_cache = {}
+
+
+def get(wl):
+    if wl.name not in _cache:
+        L = synth.make_layer(wl)
+        _cache[wl.name] = (L, device_weights(L))
+    return _cache[wl.name]
+
+
+def runner(wl, max_tokens, path=0):
+    from mixture_experts_layer_f32_amd.device import Runner
+    return Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, max_tokens, path)
+
+
+def test_argument_errors_launch_nothing():
+    import torch
+    import mixture_experts_layer_f32_amd as m
+    from mixture_experts_layer_f32_amd.device import to_dev
+    L, W = get(WL)
+    run = runner(WL, 4)
+    batch = synth.make_batch(WL, L, 4)
+    x = to_dev(batch.x)
+    outs = run.outputs(4)
+    outs["out"].fill_(7.0)
+    g, u, d = W.mats()
+
+    def call(**kw):
+        args = dict(plan=run.plan, n_tokens=4, x=x, w_router=W.w_router, logit_bias=None, gate=g,
+                    up=u, down=d, out=outs["out"], workspace=run.workspace)
+        args.update(kw)
+        with pytest.raises(m.MoeError) as e:
+            m.moe_forward(**args)
+        return e.value.status
+
+    assert call(n_tokens=5) == m.MOE_ERR_BAD_SHAPE
+    assert call(n_tokens=-1) == m.MOE_ERR_BAD_SHAPE
+    assert call(x=0) == m.MOE_ERR_NULL_ARG
+    assert call(out=0) == m.MOE_ERR_NULL_ARG
+    assert call(workspace=0) == m.MOE_ERR_NULL_ARG
+    assert call(workspace_bytes=m.moe_workspace_size(run.plan, 4) - 1) == m.MOE_ERR_WORKSPACE
+    assert call(x=x.data_ptr() + 2) == m.MOE_ERR_ALIGNMENT
+    assert call(out=outs["out"].data_ptr() + 4) == m.MOE_ERR_ALIGNMENT
+    bad = m.moe_mat(g.q + 8, g.scale, g.q_expert_stride, g.s_expert_stride)
+    assert call(gate=bad) == m.MOE_ERR_ALIGNMENT
+    bad = m.moe_mat(g.q, None, g.q_expert_stride, g.s_expert_stride)
+    assert call(up=bad) == m.MOE_ERR_NULL_ARG
+    torch.cuda.synchronize()
+    assert torch.all(outs["out"] == 7.0)          # nothing was written
+    # T = 0 is a no-op
+    m.moe_forward(run.plan, 0, x, W.w_router, None, g, u, d, outs["out"], workspace=run.workspace)
+    torch.cuda.synchronize()
+    assert torch.all(outs["out"] == 7.0)
+    assert m.moe_workspace_size(run.plan, 0) == 0
+
+
+@pytest.mark.parametrize("wl", [WL, WL4], ids=lambda w: w.name)
+@pytest.mark.parametrize("path", [1, 2])
+def test_all_tokens_on_one_expert(wl, path):
+    """A large bias on expert 3 sends every token there: one expert gets all T
+    slots (several M tiles in the grouped path), the others share the rest."""
+    L, W = get(wl)
+    T = 150
+    batch = synth.make_batch(wl, L, T)
+    bias = np.zeros((T, wl.E), np.float32)
+    bias[:, 3] = 100.0
+    batch = synth.Batch(batch.x, bias)
+    ref = oracle_run(wl, L, batch)
+    assert ref.counts[3] == T
+    g, _ = gpu_run(wl, W, batch, path)
+    check_routing(g, ref)
+    check_h(g["h"], ref.h)
+    check_out(g["out"], ref.out)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_exact_ties_go_to_lower_index(path):
+    """Zero router weights and a bias with three equal maxima: the top-2 are
+    the two lowest of the three."""
+    L, W = get(WL)
+    import torch
+    T = 5
+    batch = synth.make_batch(WL, L, T)
+    bias = np.zeros((T, WL.E), np.float32)
+    bias[:, [1, 2, 4]] = 1.0
+    wr = np.zeros_like(L.w_router)
+    Lz = synth.Layer(WL, wr, L.gate, L.up, L.down)
+    Wz = device_weights(Lz)
+    batch = synth.Batch(batch.x, bias)
+    ref = oracle_run(WL, Lz, batch)
+    assert ref.ids.tolist() == [[1, 2]] * T
+    g, _ = gpu_run(WL, Wz, batch, path)
+    check_routing(g, ref)
+    check_out(g["out"], ref.out)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_zero_input(path):
+    L, W = get(WL)
+    x = np.zeros((3, WL.d), np.uint16)
+    g, _ = gpu_run(WL, W, synth.Batch(x, None), path)
+    assert np.all(g["out"] == 0)
+    assert g["topk_ids"].tolist() == [[0, 1]] * 3
+
+
+def test_max_tokens_boundary():
+    L, W = get(WL)
+    batch = synth.make_batch(WL, L, 40)
+    ref = oracle_run(WL, L, batch)
+    g, run = gpu_run(WL, W, batch, 0, max_tokens=40)
+    check_routing(g, ref)
+    check_out(g["out"], ref.out)
+
+
+@pytest.mark.parametrize("wl", [WL, WL4], ids=lambda w: w.name)
+def test_one_block_per_expert_layout(wl):
+    """Each expert's gate | up | down codes and scales packed in one block,
+    described by expert strides: same bits as the one-buffer-per-matrix layout."""
+    import torch
+    import mixture_experts_layer_f32_amd as m
+    from mixture_experts_layer_f32_amd.device import to_dev
+    L, W = get(wl)
+    T = 7
+    batch = synth.make_batch(wl, L, T)
+    a, _ = gpu_run(wl, W, batch, 0)
+    parts = [L.gate.q, L.up.q, L.down.q, L.gate.s, L.up.s, L.down.s]
+    sizes = [p[0].nbytes for p in parts]
+    offs = np.concatenate([[0], np.cumsum([(s + 255) // 256 * 256 for s in sizes])])
+    blk = int(offs[-1])
+    buf = np.zeros((wl.E, blk), np.uint8)
+    for i, p in enumerate(parts):
+        buf[:, offs[i]:offs[i] + sizes[i]] = p.reshape(wl.E, -1).view(np.uint8)
+    dbuf = to_dev(buf)
+    base = dbuf.data_ptr()
+    mk = lambda qi, si: m.moe_mat(base + int(offs[qi]), base + int(offs[si]), blk, blk)  # noqa
+    run = runner(wl, T)
+    outs = run.outputs(T)
+    m.moe_forward(run.plan, T, to_dev(batch.x), W.w_router, None, mk(0, 3), mk(1, 4), mk(2, 5),
+                  outs["out"], workspace=run.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(outs["out"].cpu().numpy().view(np.uint32), a["out"].view(np.uint32))
+
+
+def test_nonfinite_input_row_does_not_fault():
+    """A NaN activation row is outside the contract: the call must still
+    complete, and the other tokens' outputs are unaffected."""
+    L, W = get(WL)
+    T = 6
+    batch = synth.make_batch(WL, L, T)
+    ref = oracle_run(WL, L, batch)
+    x = batch.x.copy()
+    x[2, :] = 0x7FC0  # bf16 quiet NaN
+    g, _ = gpu_run(WL, W, synth.Batch(x, None), 0)
+    ok = [t for t in range(T) if t != 2]
+    check_out(g["out"][ok], ref.out[ok])
