@@ -24,10 +24,7 @@ namespace {
 constexpr size_t ALIGN = 256;
 inline size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
-// Tile sizes of the grouped GEMMs and the decode matvecs.
-constexpr int GEMM_BM = 64;
-constexpr int GEMM_BN = 64;
-constexpr int GEMV_MAX_T = 256;  // router: one wave per expert up to this many tokens
+constexpr int GEMV_MAX_T = 16;   // router: wavefront GEMV up to this many tokens, MFMA above
 
 struct Layout {
   size_t logits, ids, w, counts, offsets, perm, inv_perm, tok_of, rank, hist, base, slot_info, n_active,
@@ -63,12 +60,34 @@ int path_for(const moe_plan_s* p, int T) {
   return T <= p->t_decode ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
 }
 
+// Router K-split: enough blocks to cover the chip, slices of >= 256 inputs
+// (multiples of 32).  Returns the number of slices; *slice gets their width.
+int router_split(const moe_plan_s* p, int T, int* slice) {
+  const int d = p->d.d_model, E = p->d.n_experts;
+  const int blocks = T <= GEMV_MAX_T ? (E + 3) / 4 : ((T + 63) / 64) * ((E + 63) / 64);
+  const int target = T <= GEMV_MAX_T ? 2 * p->cus : 4 * p->cus;
+  int n = std::max(1, std::min(std::min(d / 256, MAX_SPLIT), (target + blocks - 1) / blocks));
+  int w = (d + n - 1) / n;
+  w = (w + 31) / 32 * 32;
+  n = (d + w - 1) / w;
+  if (slice) *slice = w;
+  return n;
+}
+
+// Rows per grouped-GEMM tile from the mean slots per expert.
+int gemm_bm(const moe_plan_s* p, int T) {
+  const long long S = (long long)T * p->d.top_k;
+  const long long per = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
+  return per >= 96 ? 128 : (per >= 40 ? 64 : 32);
+}
+
 Layout layout(const moe_plan_s* p, int T) {
   const size_t E = p->d.n_experts, k = p->d.top_k, d = p->d.d_model, f = p->d.d_ff;
   const size_t S = (size_t)T * k;
+  const size_t BM = gemm_bm(p, T);
   Layout L;
   L.nchunk = (T + WAVE - 1) / WAVE;
-  L.max_tiles = (int)((S + GEMM_BM - 1) / GEMM_BM + std::min<size_t>(E, S));
+  L.max_tiles = (int)((S + BM - 1) / BM + std::min<size_t>(E, S));
   L.n_slots = (int)std::min<size_t>(E, S);
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -76,7 +95,7 @@ Layout layout(const moe_plan_s* p, int T) {
     o = align_up(o + bytes);
     return at;
   };
-  L.logits = take((size_t)T * E * 4);
+  L.logits = take((size_t)router_split(p, T, nullptr) * T * E * 4);
   L.ids = take(S * 4);
   L.w = take(S * 4);
   L.counts = take(E * 4);
@@ -180,6 +199,24 @@ void launch_dec(moe_plan_s* p, int T, int n_slots, int N, int K, const uint16_t*
 #undef MOE_DEC_CASE
 }
 
+// Grouped GEMM launch: grid (column blocks of N, tile-list entries), LDS
+// sized per configuration (above the 64 KB static limit, set once).
+template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK, int PF>
+void launch_gemm(int max_tiles, int N, int K, int T, const uint16_t* act, DMat W0, DMat W1,
+                 const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of, void* out,
+                 hipStream_t st) {
+  using C = G2<FMT, GATEUP ? 2 : 1, BM, WM, TN, BK>;
+  auto kern = &gemm_expert<FMT, GATEUP, BM, WM, TN, BK, PF>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
+    attr_set = true;
+  }
+  const dim3 g((N + C::BNM - 1) / C::BNM, max_tiles);
+  kern<<<g, 256, C::SMEM, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T);
+}
+
 template <int FMT>
 moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, DMat U, DMat D,
                                const Layout& L, char* ws, hipStream_t st) {
@@ -217,13 +254,28 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
   } else {
     const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
-    const dim3 g1(L.max_tiles, (f + GEMM_BN - 1) / GEMM_BN), g2(L.max_tiles, (d + GEMM_BN - 1) / GEMM_BN);
+    const int bm = gemm_bm(p, T);
     mark(p, MOE_STAGE_GATEUP, false, st);
-    gemm_gateup<FMT, GEMM_BM, GEMM_BN><<<g1, 256, 0, st>>>(x, G, U, tiles, n_tiles, tok_of, h, d, f,
-                                                          T);
+    if (bm == 128)
+      launch_gemm<FMT, true, 128, 2, 1, 64, 1>(L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
+                                               tok_of, h, st);
+    else if (bm == 64)
+      launch_gemm<FMT, true, 64, 2, 1, 64, 1>(L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
+                                              tok_of, h, st);
+    else
+      launch_gemm<FMT, true, 32, 1, 1, 64, 1>(L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
+                                              tok_of, h, st);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
-    gemm_down<FMT, GEMM_BM, GEMM_BN><<<g2, 256, 0, st>>>(h, D, tiles, n_tiles, y, d, f);
+    if (bm == 128)
+      launch_gemm<FMT, false, 128, 2, 2, 64, 1>(L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
+                                                tok_of, y, st);
+    else if (bm == 64)
+      launch_gemm<FMT, false, 64, 2, 2, 64, 1>(L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
+                                               tok_of, y, st);
+    else
+      launch_gemm<FMT, false, 32, 1, 1, 64, 1>(L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
+                                               tok_of, y, st);
     mark(p, MOE_STAGE_DOWN, true, st);
   }
   hipError_t err = hipGetLastError();
@@ -270,6 +322,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (d.n_experts > MAX_E || d.top_k > MAX_K) return MOE_ERR_UNSUPPORTED;
   if (d.wfmt == MOE_W_E4M3_B128) {
     if (d.d_model % 128 || d.d_ff % 128) return MOE_ERR_UNSUPPORTED;
+    if (d.d_model > 128 * MAX_KBLK || d.d_ff > 128 * MAX_KBLK) return MOE_ERR_UNSUPPORTED;
   } else if (d.wfmt == MOE_W_E2M1_UE8M0_G32) {
     if (d.d_model % 32 || d.d_ff % 32) return MOE_ERR_UNSUPPORTED;
   } else {
@@ -303,13 +356,13 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "
-                "(decode for T<=%d); router gemv<=%d tokens else 64x64 f32 tiles; "
-                "decode streaming matvec (row groups per wave %d, 0=auto); grouped MFMA 32x32x16 "
-                "bf16 tiles BMxBN=%dx%d",
+                "(decode for T<=%d); router: wavefront gemv up to %d tokens, else 64x64 bf16x3 MFMA tiles, split-K; "
+                "decode matvec (row groups per wave %d, 0=auto); grouped MFMA 32x32x16 bf16, "
+                "BM 32/64/128 by slots per expert, BK 64 double-buffered",
                 dev, p->arch.c_str(), p->cus, d.d_model, d.d_ff, d.n_experts, d.top_k,
                 d.wfmt == MOE_W_E4M3_B128 ? "e4m3/128x128" : "e2m1/ue8m0x32", d.renorm,
                 d.path == MOE_PATH_AUTO ? "auto" : (d.path == MOE_PATH_DECODE ? "decode" : "grouped"),
-                p->t_decode, GEMV_MAX_T, p->dec_nrg, GEMM_BM, GEMM_BN);
+                p->t_decode, GEMV_MAX_T, p->dec_nrg);
   p->info = buf;
   *out = p;
   return MOE_OK;
@@ -440,24 +493,27 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
   int32_t* base = reinterpret_cast<int32_t*>(ws + L.base);
 
-  // a1: router logits
+  // a1: router logits (K-slice partials)
+  int slice = 0;
+  const int nsplit = router_split(p, T, &slice);
   mark(p, MOE_STAGE_ROUTER, false, s);
   if (T <= GEMV_MAX_T) {
-    const dim3 g((E + 3) / 4);
+    const dim3 g((E + 3) / 4, nsplit);
     if (T == 1)
-      router_gemv<1><<<g, 256, 0, s>>>(x, w_router, logit_bias, logits, T, d, E);
+      router_gemv<1><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
     else if (T <= 4)
-      router_gemv<4><<<g, 256, 0, s>>>(x, w_router, logit_bias, logits, T, d, E);
+      router_gemv<4><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
     else
-      router_gemv<8><<<g, 256, 0, s>>>(x, w_router, logit_bias, logits, T, d, E);
+      router_gemv<8><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
   } else {
-    const dim3 g((T + 63) / 64, (E + 63) / 64);
-    router_gemm<<<g, 256, 0, s>>>(x, w_router, logit_bias, logits, T, d, E);
+    const dim3 g((T + 63) / 64, (E + 63) / 64, nsplit);
+    router_mfma<<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
   }
   mark(p, MOE_STAGE_ROUTER, true, s);
   // a2: softmax + top-k
   mark(p, MOE_STAGE_TOPK, false, s);
-  route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, ids, w, T, E, k, p->d.renorm);
+  route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, logit_bias, ids, w, T, E, k,
+                                         p->d.renorm);
   mark(p, MOE_STAGE_TOPK, true, s);
   // a3: counting-sort permute
   mark(p, MOE_STAGE_PERMUTE, false, s);
@@ -465,7 +521,7 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   permute_scan<<<1, 1024, 0, s>>>(hist, base, cnt, off, reinterpret_cast<int4*>(ws + L.slot_info),
                                   reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots, reinterpret_cast<int4*>(ws + L.tiles),
                                   reinterpret_cast<int32_t*>(ws + L.n_tiles), L.nchunk, E, S,
-                                  GEMM_BM);
+                                  gemm_bm(p, T));
   permute_scatter<<<(S + 255) / 256, 256, 0, s>>>(ids, rank, base, off, prm, inv,
                                                   reinterpret_cast<int32_t*>(ws + L.tok_of), S, E,
                                                   k);

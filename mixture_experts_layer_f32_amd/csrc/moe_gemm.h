@@ -1,17 +1,24 @@
 // Grouped variant of the expert stage: for many tokens per expert, each
-// expert's rows (in sorted-slot order) form the M dimension of a GEMM tile.
+// expert's rows (in sorted-slot order) form the M dimension of GEMM tiles.
 // Weight tiles are read from HBM once per M-tile, decoded exactly to bf16 in
 // LDS, and multiplied with bf16 MFMA (v_mfma_f32_32x32x16_bf16) into f32.
-//   e4m3: one f32 scale per 128x128 block; every 128-deep K step is summed
-//         into a fresh f32 partial, then added to the running sum times the
-//         block's scale (dragon.c page, section 8 Round 3: the 128-column
-//         block structure folds the scale multiply out of the inner loop).
+//   e4m3: one f32 scale per 128x128 block; the MFMA sums of each 128-deep K
+//         block go to a fresh f32 partial that is then added to the running
+//         sum times the block's scale (dragon.c page, section 8 Round 3: the
+//         128-column block structure folds the scale multiply out of the
+//         inner loop).
 //   e2m1: the power-of-two scale is applied exactly inside the fp4 -> bf16
 //         conversion, so MFMA accumulates straight into the running sum.
-// The A rows of the gate/up GEMM are gathered through the permutation (the
-// token's own activation row), never copied (Trochilus README, "How it keeps
+// The A rows of the gate/up GEMM are the tokens' own activation rows, read
+// through the permutation and never copied (Trochilus README, "How it keeps
 // up": gate and up read a token's row through a map instead of gathered
-// copies).  SwiGLU and the bf16 rounding of h are fused into the epilogue.
+// copies).  Gate and up rows of the same output column sit in the same lane
+// and register, so SwiGLU and the bf16 rounding of h happen in registers.
+//
+// Pipeline: 64-deep K stages, double-buffered in LDS; while the MFMAs of
+// stage k run, each thread's global loads for stage k+1 are in flight in
+// registers; they are decoded and written to the other LDS buffer after the
+// MFMAs, and one barrier per stage orders the buffers.
 #pragma once
 
 #include "moe_common.h"
@@ -19,118 +26,36 @@
 
 namespace moe {
 
-// Tile geometry: 4 wavefronts in a 2 x 2 grid, each owning a
-// (BM/2) x (BN/2) patch of 32x32 MFMA tiles.
-template <int FMT>
-struct GemmCfg {
-  static constexpr int BK = FMT == FMT_E4M3 ? 128 : 64;  // K depth per LDS stage
-  static constexpr int LDK = BK + 8;                      // padded LDS row (bf16)
+// BM rows per tile; WM wavefronts along M and 4/WM along N; each wavefront
+// owns TM x TN 32x32 tiles per weight matrix; NMAT matrices (2: gate and up
+// sharing A, 1: down).
+template <int FMT, int NMAT, int BM, int WM, int TN, int BK_ = 64>
+struct G2 {
+  static constexpr int BK = BK_, LDK = BK + 8;        // stage depth, padded LDS row (bf16)
+  static constexpr int WN = 4 / WM;
+  static constexpr int TM = BM / WM / 32;
+  static constexpr int BNM = WN * 32 * TN;            // weight rows per matrix per block
+  static constexpr int A_ELEMS = BM * LDK;
+  static constexpr int STAGE = A_ELEMS + NMAT * BNM * LDK;
+  static constexpr int SMEM = 2 * STAGE * 2;          // bytes, two stages
+  static constexpr int A_CPR = BK / 8;                                   // 16-B chunks (8 bf16) per row
+  static constexpr int A_TOTAL = BM * A_CPR;
+  static constexpr int A_CHUNKS = (A_TOTAL + 255) / 256;                 // per thread (last may idle)
+  static constexpr int B_CPR = FMT == FMT_E4M3 ? BK / 16 : BK / 32;     // 16-B code chunks per row
+  static constexpr int B_EPC = FMT == FMT_E4M3 ? 16 : 32;               // codes per chunk
+  static constexpr int B_TOTAL = NMAT * BNM * B_CPR;
+  static constexpr int B_CHUNKS = (B_TOTAL + 255) / 256;
+  static_assert(256 % A_CPR == 0 && (A_TOTAL % 256 == 0 || A_TOTAL < 256), "A tile / threads");
+  static_assert(B_TOTAL % 256 == 0 || B_TOTAL < 256, "B tile / threads");
+  static_assert(TM >= 1, "tile rows");
+  static_assert(FMT != FMT_E4M3 || 128 % BK == 0, "e4m3 stages divide a scale block");
 };
 
-// A tile: BM rows x BK bf16 from `row_ptr(r)` (nullptr -> zero row), columns
-// [k0, k0+BK) clipped to K.  16-byte loads, 256 threads.
-template <int BM, int BK, int LDK, typename RowPtr>
-__device__ __forceinline__ void load_a_tile(uint16_t* As, RowPtr row_ptr, int k0, int K) {
-  constexpr int CPR = BK / 8;  // 16-byte chunks per row
-  constexpr int TOTAL = BM * CPR;
-#pragma unroll
-  for (int i = 0; i < (TOTAL + 255) / 256; ++i) {
-    const int q = threadIdx.x + 256 * i;
-    if (q < TOTAL) {
-      const int r = q / CPR, c = q % CPR;
-      const uint16_t* src = row_ptr(r);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (src != nullptr && k0 + c * 8 < K) v = *reinterpret_cast<const u32x4*>(src + k0 + c * 8);
-      *reinterpret_cast<u32x4*>(As + r * LDK + c * 8) = v;
-    }
-  }
-}
+constexpr int MAX_KBLK = 128;  // e4m3 grouped GEMM: K <= 128 * 128 (scales held in 2 VGPRs)
 
-// B tile: BN weight rows [n0, n0+BN) x inputs [k0, k0+BK) of one expert,
-// decoded to bf16 into Bs[n][k].  Rows past N and inputs past K are zero.
-template <int FMT, int BN, int BK, int LDK>
-__device__ __forceinline__ void load_b_tile(uint16_t* Bs, const uint8_t* q, const uint8_t* s,
-                                            int n0, int N, int k0, int K) {
-  if (FMT == FMT_E4M3) {
-    constexpr int CPR = BK / 16;  // 16 codes per chunk
-    constexpr int TOTAL = BN * CPR;
-#pragma unroll
-    for (int i = 0; i < (TOTAL + 255) / 256; ++i) {
-      const int qi = threadIdx.x + 256 * i;
-      if (qi < TOTAL) {
-        const int r = qi / CPR, c = qi % CPR;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (n0 + r < N)
-          w = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(q + (size_t)(n0 + r) * K + k0 + c * 16));
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        bf16x2 o[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[2 * j] = e4m3x2_to_bf16<false>(ws[j]);
-          o[2 * j + 1] = e4m3x2_to_bf16<true>(ws[j]);
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(Bs + r * LDK + c * 16);
-        dst[0] = *reinterpret_cast<const u32x4*>(&o[0]);
-        dst[1] = *reinterpret_cast<const u32x4*>(&o[4]);
-      }
-    }
-  } else {
-    constexpr int CPR = BK / 16;  // 16 codes (8 bytes) per chunk
-    constexpr int TOTAL = BN * CPR;
-#pragma unroll
-    for (int i = 0; i < (TOTAL + 255) / 256; ++i) {
-      const int qi = threadIdx.x + 256 * i;
-      if (qi < TOTAL) {
-        const int r = qi / CPR, c = qi % CPR;
-        const int kk = k0 + c * 16;
-        u32x2 w = {0u, 0u};
-        float sc = 1.0f;
-        if (n0 + r < N && kk < K) {
-          w = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x2*>(q + (size_t)(n0 + r) * (K / 2) + kk / 2));
-          sc = ue8m0_to_f32(s[(size_t)(n0 + r) * (K / 32) + kk / 32]);
-        }
-        bf16x2 o[8];
-        o[0] = e2m1x2_to_bf16<0>(w.x, sc);
-        o[1] = e2m1x2_to_bf16<1>(w.x, sc);
-        o[2] = e2m1x2_to_bf16<2>(w.x, sc);
-        o[3] = e2m1x2_to_bf16<3>(w.x, sc);
-        o[4] = e2m1x2_to_bf16<0>(w.y, sc);
-        o[5] = e2m1x2_to_bf16<1>(w.y, sc);
-        o[6] = e2m1x2_to_bf16<2>(w.y, sc);
-        o[7] = e2m1x2_to_bf16<3>(w.y, sc);
-        u32x4* dst = reinterpret_cast<u32x4*>(Bs + r * LDK + c * 16);
-        dst[0] = *reinterpret_cast<const u32x4*>(&o[0]);
-        dst[1] = *reinterpret_cast<const u32x4*>(&o[4]);
-      }
-    }
-  }
-}
-
-// acc[tm][tn] += A[wave rows] * B[wave cols]^T over one BK-deep stage.
-// Operand layout of v_mfma_f32_32x32x16_bf16: lane l supplies row l%32 and
-// inputs 8*(l/32) .. 8*(l/32)+7 of the 16-deep slice, for A and for B.
-template <int TM, int TN, int BK, int LDK>
-__device__ __forceinline__ void mfma_stage(f32x16 (&acc)[TM][TN], const uint16_t* As,
-                                           const uint16_t* Bs, int wm0, int wn0) {
-  const int lane = lane_id();
-  const int r = lane & 31, kh = (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < BK; kk += 16) {
-    bf16x8 a[TM], b[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(As + (wm0 + 32 * i + r) * LDK + kk + kh);
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn0 + 32 * j + r) * LDK + kk + kh);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+__device__ __forceinline__ u32x4 pack4(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
 }
 
 // Row index (within the 32x32 tile) of accumulator register v for this lane;
@@ -139,143 +64,194 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
   return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// Gate/up + SwiGLU over the tile list.  grid.x: tile index (blocks past
-// *n_tiles exit); grid.y: BN-wide column block of f.
-template <int FMT, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_gateup(
-    const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ tiles,
+// grid.x: BNM-wide column block of N; grid.y: tile index (blocks past
+// *n_tiles exit).  GATEUP: act = x [T][K], out = h bf16 [S][N] (N = f,
+// K = d); otherwise act = h [S][K], out = y f32 [S][N] (N = d, K = f).
+template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK_, int PF>
+__global__ __launch_bounds__(256, 2) void gemm_expert(
+    const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
-    uint16_t* __restrict__ h, int d, int f, int T) {
-  constexpr int BK = GemmCfg<FMT>::BK, LDK = GemmCfg<FMT>::LDK;
-  constexpr int TM = BM / 64, TN = BN / 64;
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bg[BN * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bu[BN * LDK];
-  __shared__ int tok[BM];
-  if ((int)blockIdx.x >= *n_tiles) return;
-  const int4 tile = tiles[blockIdx.x];
+    void* __restrict__ out, int N, int K, int T) {
+  constexpr int NMAT = GATEUP ? 2 : 1;
+  using C = G2<FMT, NMAT, BM, WM, TN, BK_>;
+  constexpr int BK = C::BK, LDK = C::LDK, TM = C::TM, BNM = C::BNM;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  if ((int)blockIdx.y >= *n_tiles) return;
+  const int4 tile = tiles[blockIdx.y];
   const int e = tile.x, p_start = tile.y, rows = tile.z;
-  const int n0 = blockIdx.y * BN;
-  const int lane = lane_id(), wv = wave_id();
-  const int wm0 = (wv >> 1) * (BM / 2), wn0 = (wv & 1) * (BN / 2);
-  for (int r = threadIdx.x; r < BM; r += 256)
-    tok[r] = r < rows ? (int)min((uint32_t)tok_of[p_start + r], (uint32_t)(T - 1)) : -1;
-  __syncthreads();
-  const uint8_t* gq = gate.q + e * gate.qs;
-  const uint8_t* uq = up.q + e * up.qs;
-  const uint8_t* gs = gate.s + e * gate.ss;
-  const uint8_t* us = up.s + e * up.ss;
-  auto xrow = [&](int r) -> const uint16_t* {
-    return tok[r] >= 0 ? x + (size_t)tok[r] * d : nullptr;
-  };
-  f32x16 accg[TM][TN], accu[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) accg[i][j][v] = accu[i][j][v] = 0.0f;
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    load_a_tile<BM, BK, LDK>(As, xrow, k0, d);
-    load_b_tile<FMT, BN, BK, LDK>(Bg, gq, gs, n0, f, k0, d);
-    load_b_tile<FMT, BN, BK, LDK>(Bu, uq, us, n0, f, k0, d);
-    __syncthreads();
-    if (FMT == FMT_E4M3) {
-      f32x16 pg[TM][TN], pu[TM][TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) pg[i][j][v] = pu[i][j][v] = 0.0f;
-      mfma_stage<TM, TN, BK, LDK>(pg, As, Bg, wm0, wn0);
-      mfma_stage<TM, TN, BK, LDK>(pu, As, Bu, wm0, wn0);
-      const float* gsf = reinterpret_cast<const float*>(gs);
-      const float* usf = reinterpret_cast<const float*>(us);
-      const float sg = gsf[(n0 >> 7) * (d >> 7) + (k0 >> 7)];
-      const float su = usf[(n0 >> 7) * (d >> 7) + (k0 >> 7)];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            accg[i][j][v] += sg * pg[i][j][v];
-            accu[i][j][v] += su * pu[i][j][v];
-          }
-    } else {
-      mfma_stage<TM, TN, BK, LDK>(accg, As, Bg, wm0, wn0);
-      mfma_stage<TM, TN, BK, LDK>(accu, As, Bu, wm0, wn0);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = wm0 + 32 * i + acc_row(v, lane);
-        const int n = n0 + wn0 + 32 * j + (lane & 31);
-        if (m < rows && n < f)
-          h[(size_t)(p_start + m) * f + n] =
-              (uint16_t)f32_to_bf16_rne(silu(accg[i][j][v]) * accu[i][j][v]);
-      }
-}
+  const int n0 = blockIdx.x * BNM;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int wm0 = (wv / C::WN) * (BM / WM), wn0 = (wv % C::WN) * 32 * TN;
 
-// Down projection over the tile list: y[p][m] = sum_n h[p][n] Wd[m][n], f32.
-template <int FMT, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_down(const uint16_t* __restrict__ h, DMat down,
-                                                 const int4* __restrict__ tiles,
-                                                 const int32_t* __restrict__ n_tiles,
-                                                 float* __restrict__ y, int d, int f) {
-  constexpr int BK = GemmCfg<FMT>::BK, LDK = GemmCfg<FMT>::LDK;
-  constexpr int TM = BM / 64, TN = BN / 64;
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
-  if ((int)blockIdx.x >= *n_tiles) return;
-  const int4 tile = tiles[blockIdx.x];
-  const int e = tile.x, p_start = tile.y, rows = tile.z;
-  const int n0 = blockIdx.y * BN;
-  const int lane = lane_id(), wv = wave_id();
-  const int wm0 = (wv >> 1) * (BM / 2), wn0 = (wv & 1) * (BN / 2);
-  const uint8_t* dq = down.q + e * down.qs;
-  const uint8_t* ds = down.s + e * down.ss;
-  auto hrow = [&](int r) -> const uint16_t* {
-    return r < rows ? h + (size_t)(p_start + r) * f : nullptr;
+  // this thread's A rows (fixed over K) and column
+  const uint16_t* arow[C::A_CHUNKS];
+  const int acol = (tid % C::A_CPR) * 8;
+#pragma unroll
+  for (int i = 0; i < C::A_CHUNKS; ++i) {
+    const int q = tid + 256 * i;
+    const int r = q / C::A_CPR;
+    arow[i] = nullptr;
+    if (q < C::A_TOTAL && r < rows) {
+      const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + r], (uint32_t)(T - 1))
+                                : (size_t)(p_start + r);
+      arow[i] = act + src * K;
+    }
+  }
+  // this thread's B chunks: matrix, row, chunk column
+  const uint8_t* bq[C::B_CHUNKS];
+  const uint8_t* bsr[C::B_CHUNKS];
+  int bdst[C::B_CHUNKS];
+  const int64_t rbytes = FMT == FMT_E4M3 ? (int64_t)K : (int64_t)K / 2;
+#pragma unroll
+  for (int i = 0; i < C::B_CHUNKS; ++i) {
+    const int q = tid + 256 * i;
+    const int m = q / (BNM * C::B_CPR);
+    const int rem = q % (BNM * C::B_CPR);
+    const int r = rem / C::B_CPR, c = rem % C::B_CPR;
+    const DMat& W = (m == 0) ? W0 : W1;
+    const int n = n0 + r;
+    const bool ok = q < C::B_TOTAL && n < N;
+    bq[i] = ok ? W.q + e * W.qs + n * rbytes + c * 16 : nullptr;
+    bsr[i] = ok ? W.s + e * W.ss + (size_t)n * (K / 32) + c : nullptr;  // e2m1 group of the chunk
+    bdst[i] = q < C::B_TOTAL ? C::A_ELEMS + (m * BNM + r) * LDK + c * C::B_EPC : -1;
+  }
+
+  // e4m3: this block's scale row (one 128-row block of N) for each matrix,
+  // k-block kb held by lane kb % 64 of register kb / 64, read with v_readlane
+  float scv[NMAT][2];
+  if (FMT == FMT_E4M3) {
+    const int nb = min(n0, N - 1) >> 7, kbs = K >> 7;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const DMat& W = (m == 0) ? W0 : W1;
+      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)nb * kbs;
+      scv[m][0] = lane < kbs ? sf[lane] : 0.0f;
+      scv[m][1] = lane + 64 < kbs ? sf[lane + 64] : 0.0f;
+    }
+  }
+
+  // PF register sets of global loads in flight
+  u32x4 ra[PF][C::A_CHUNKS], rb[PF][C::B_CHUNKS];
+  float rsc[PF][C::B_CHUNKS];
+  auto gload = [&](int set, int k0) {
+#pragma unroll
+    for (int i = 0; i < C::A_CHUNKS; ++i) {
+      ra[set][i] = u32x4{0u, 0u, 0u, 0u};
+      if (arow[i] != nullptr && k0 + acol < K)
+        ra[set][i] = *reinterpret_cast<const u32x4*>(arow[i] + k0 + acol);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_CHUNKS; ++i) {
+      rb[set][i] = u32x4{0u, 0u, 0u, 0u};
+      rsc[set][i] = 1.0f;
+      const int c = (tid + 256 * i) % C::B_CPR;
+      if (bq[i] != nullptr && k0 + c * C::B_EPC < K) {
+        const int64_t off = FMT == FMT_E4M3 ? k0 : k0 / 2;
+        rb[set][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bq[i] + off));
+        if (FMT == FMT_E2M1) rsc[set][i] = ue8m0_to_f32(bsr[i][k0 / 32]);
+      }
+    }
   };
-  f32x16 acc[TM][TN];
+  auto lstore = [&](int set, uint16_t* st) {
+#pragma unroll
+    for (int i = 0; i < C::A_CHUNKS; ++i) {
+      const int q = tid + 256 * i;
+      if (q < C::A_TOTAL)
+        *reinterpret_cast<u32x4*>(st + (q / C::A_CPR) * LDK + acol) = ra[set][i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_CHUNKS; ++i) {
+      if (bdst[i] < 0) continue;
+      const uint32_t w[4] = {rb[set][i].x, rb[set][i].y, rb[set][i].z, rb[set][i].w};
+      u32x4* dst = reinterpret_cast<u32x4*>(st + bdst[i]);
+      if (FMT == FMT_E4M3) {
+        bf16x2 o[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[2 * j] = e4m3x2_to_bf16<false>(w[j]);
+          o[2 * j + 1] = e4m3x2_to_bf16<true>(w[j]);
+        }
+        dst[0] = pack4(o[0], o[1], o[2], o[3]);
+        dst[1] = pack4(o[4], o[5], o[6], o[7]);
+      } else {
+        const float sc = rsc[set][i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x2 o[4];
+          o[0] = e2m1x2_to_bf16<0>(w[j], sc);
+          o[1] = e2m1x2_to_bf16<1>(w[j], sc);
+          o[2] = e2m1x2_to_bf16<2>(w[j], sc);
+          o[3] = e2m1x2_to_bf16<3>(w[j], sc);
+          dst[j] = pack4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    }
+  };
+
+  f32x16 acc[TM][NMAT * TN], part[TM][NMAT * TN];
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < NMAT * TN; ++j) acc[i][j] = part[i][j] = zero;
+
+  // Stage ks lives in LDS buffer ks & 1; its global loads went to register
+  // set ks % PF, issued PF stages earlier.
+  constexpr int SPB = 128 / BK;  // e4m3: stages per scale block
+  const int nk = (K + BK - 1) / BK;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-  for (int k0 = 0; k0 < f; k0 += BK) {
-    load_a_tile<BM, BK, LDK>(As, hrow, k0, f);
-    load_b_tile<FMT, BN, BK, LDK>(Bs, dq, ds, n0, d, k0, f);
-    __syncthreads();
-    if (FMT == FMT_E4M3) {
-      f32x16 p[TM][TN];
+  for (int p = 0; p < PF; ++p)
+    if (p < nk) gload(p, p * BK);
+  lstore(0, smem);
+  __syncthreads();
+  const int r32 = lane & 31, kh = (lane >> 5) * 8;
+  for (int ks = 0; ks < nk; ++ks) {
+    const uint16_t* cur = smem + (ks & 1) * C::STAGE;
+    // the register set of stage ks was stored to LDS; refill it with stage ks + PF
+    if (ks + PF < nk) gload(ks % PF, (ks + PF) * BK);
+    const bool first = (FMT == FMT_E4M3) && (ks % SPB == 0);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 a[TM], b[NMAT * TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(cur + (wm0 + 32 * i + r32) * LDK + kk + kh);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          b[m * TN + j] = *reinterpret_cast<const bf16x8*>(
+              cur + C::A_ELEMS + (m * BNM + wn0 + 32 * j + r32) * LDK + kk + kh);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) p[i][j][v] = 0.0f;
-      mfma_stage<TM, TN, BK, LDK>(p, As, Bs, wm0, wn0);
-      const float sd = reinterpret_cast<const float*>(ds)[(n0 >> 7) * (f >> 7) + (k0 >> 7)];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[i][j][v] += sd * p[i][j][v];
-    } else {
-      mfma_stage<TM, TN, BK, LDK>(acc, As, Bs, wm0, wn0);
+        for (int j = 0; j < NMAT * TN; ++j) {
+          if (FMT == FMT_E4M3)  // a scale block's first product starts from zero
+            part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                a[i], b[j], (first && kk == 0) ? zero : part[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
     }
+    if (FMT == FMT_E4M3 && ((ks % SPB) == SPB - 1 || ks == nk - 1)) {
+      // end of a 128-deep scale block: acc += scale * partial
+      const int kb = (ks * BK) >> 7;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const float sc = __int_as_float(__builtin_amdgcn_readlane(
+            __float_as_int(kb < 64 ? scv[m][0] : scv[m][1]), kb & 63));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][m * TN + j][v] += sc * part[i][m * TN + j][v];
+      }
+    }
+    if (ks + 1 < nk) lstore((ks + 1) % PF, smem + ((ks + 1) & 1) * C::STAGE);
     __syncthreads();
   }
+
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -283,8 +259,14 @@ __global__ __launch_bounds__(256) void gemm_down(const uint16_t* __restrict__ h,
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wm0 + 32 * i + acc_row(v, lane);
-        const int n = n0 + wn0 + 32 * j + (lane & 31);
-        if (m < rows && n < d) y[(size_t)(p_start + m) * d + n] = acc[i][j][v];
+        const int n = n0 + wn0 + 32 * j + r32;
+        if (m < rows && n < N) {
+          if (GATEUP)
+            reinterpret_cast<uint16_t*>(out)[(size_t)(p_start + m) * N + n] =
+                (uint16_t)f32_to_bf16_rne(silu(acc[i][j][v]) * acc[i][TN + j][v]);
+          else
+            reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = acc[i][j][v];
+        }
       }
 }
 

@@ -8,24 +8,29 @@ namespace moe {
 
 // ---------------------------------------------------------------- router logits
 
-// Few tokens: one wavefront per expert streams its f32 router row with
-// 16-byte loads and dots it with up to TG tokens at a time; a wave-wide tree
-// sum finishes each logit.  logits[t][e] = sum_i W_r[e][i] x[t][i] + bias[t][e].
+// The router output of K-slice `split` goes to part[split][t][e]; the top-k
+// kernel adds the slices in order 0, 1, ... and then the bias, so every logit
+// has one fixed summation order.
+
+// Few tokens: one wavefront per (expert, K-slice) streams its slice of the f32
+// router row with 16-byte loads and dots it with up to TG tokens at a time; a
+// wave-wide sum finishes each partial logit.
 template <int TG>
 __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ wr,
-                                                   const float* __restrict__ bias,
-                                                   float* __restrict__ logits, int T, int d,
-                                                   int E) {
+                                                   float* __restrict__ part, int T, int d, int E,
+                                                   int slice) {
   const int e = blockIdx.x * 4 + wave_id();
   if (e >= E) return;
   const int lane = lane_id();
+  const int k0 = blockIdx.y * slice, k1 = min(d, k0 + slice);
   const float* wrow = wr + (size_t)e * d;
+  float* out = part + (size_t)blockIdx.y * T * E;
   for (int t0 = 0; t0 < T; t0 += TG) {
     float acc[TG];
 #pragma unroll
     for (int i = 0; i < TG; ++i) acc[i] = 0.0f;
-    for (int c = lane * 4; c < d; c += WAVE * 4) {
+    for (int c = k0 + lane * 4; c < k1; c += WAVE * 4) {
       const f32x4 w = *reinterpret_cast<const f32x4*>(wrow + c);
 #pragma unroll
       for (int i = 0; i < TG; ++i) {
@@ -38,68 +43,91 @@ __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
-      const float s = wave_sum(acc[i]);
-      const int t = t0 + i;
-      if (lane == 0 && t < T) logits[(size_t)t * E + e] = s + (bias ? bias[(size_t)t * E + e] : 0.0f);
+      if (t0 + i < T) {
+        const float sum = wave_sum(acc[i]);
+        if (lane == 0) out[(size_t)(t0 + i) * E + e] = sum;
+      }
     }
   }
 }
 
-// Many tokens: a 64-token x 64-expert tile per 256-thread block, f32 FMAs
-// from LDS, K in chunks of 32; each thread owns a 4x4 patch.
-__global__ __launch_bounds__(256) void router_gemm(const uint16_t* __restrict__ x,
+// Many tokens: 64-token x 64-expert tiles on MFMA.  An f32 router weight w is
+// the exact sum of three bf16 values hi + mid + lo (hi keeps the top 8 of its
+// 24 significand bits, mid the next 8, lo the last 8; each remainder is exact
+// in f32).  A bf16 activation times a bf16 value is exact in f32, so three
+// v_mfma_f32_32x32x16_bf16 per 16-deep slice give x.w with only the f32
+// accumulation rounding of an f32 dot product.  4 wavefronts in a 2x2 grid
+// own 32x32 patches; K advances 32 per LDS stage within this block's slice.
+__device__ __forceinline__ void split3_bf16(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  const uint32_t u = __float_as_uint(w);
+  const float fh = __uint_as_float(u & 0xFFFF0000u);
+  const float r1 = w - fh;
+  const uint32_t ur = __float_as_uint(r1);
+  const float fm = __uint_as_float(ur & 0xFFFF0000u);
+  const float r2 = r1 - fm;
+  hi = (uint16_t)(u >> 16);
+  mid = (uint16_t)(ur >> 16);
+  lo = (uint16_t)(__float_as_uint(r2) >> 16);
+}
+
+__global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ wr,
-                                                   const float* __restrict__ bias,
-                                                   float* __restrict__ logits, int T, int d,
-                                                   int E) {
-  __shared__ float xs[32][64 + 4];
-  __shared__ float ws[32][64 + 4];
-  const int tid = threadIdx.x;
+                                                   float* __restrict__ part, int T, int d, int E,
+                                                   int slice) {
+  constexpr int BK = 32, LDK = BK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[3][64 * LDK];
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int ty = tid / 16, tx = tid % 16;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    {  // x tile: 64 tokens x 32 k, one 16-byte load (8 bf16) per thread
-      const int r = tid / 4, c8 = (tid % 4) * 8;
+  const int k0 = blockIdx.z * slice, k1 = min(d, k0 + slice);
+  const int wm0 = (wv >> 1) * 32, wn0 = (wv & 1) * 32;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int k = k0; k < k1; k += BK) {
+    {  // activations: 64 rows x 32 bf16, one 16-byte chunk per thread
+      const int r = tid >> 2, c = (tid & 3) * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (t0 + r < T) v = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * d + k0 + c8);
-      xs[c8 + 0][r] = bf16_lo(v.x); xs[c8 + 1][r] = bf16_hi(v.x);
-      xs[c8 + 2][r] = bf16_lo(v.y); xs[c8 + 3][r] = bf16_hi(v.y);
-      xs[c8 + 4][r] = bf16_lo(v.z); xs[c8 + 5][r] = bf16_hi(v.z);
-      xs[c8 + 6][r] = bf16_lo(v.w); xs[c8 + 7][r] = bf16_hi(v.w);
+      if (t0 + r < T) v = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * d + k + c);
+      *reinterpret_cast<u32x4*>(xs + r * LDK + c) = v;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // router tile: 64 experts x 32 k
+    for (int i = 0; i < 2; ++i) {  // router rows: 64 x 32 f32, split into hi / mid / lo
       const int q = tid + 256 * i;
-      const int r = q / 8, c4 = (q % 8) * 4;
+      const int r = q >> 3, c = (q & 7) * 4;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (e0 + r < E) v = *reinterpret_cast<const f32x4*>(wr + (size_t)(e0 + r) * d + k0 + c4);
-      ws[c4 + 0][r] = v.x; ws[c4 + 1][r] = v.y; ws[c4 + 2][r] = v.z; ws[c4 + 3][r] = v.w;
+      if (e0 + r < E) v = *reinterpret_cast<const f32x4*>(wr + (size_t)(e0 + r) * d + k + c);
+      uint16_t h[4], m[4], l[4];
+      split3_bf16(v.x, h[0], m[0], l[0]);
+      split3_bf16(v.y, h[1], m[1], l[1]);
+      split3_bf16(v.z, h[2], m[2], l[2]);
+      split3_bf16(v.w, h[3], m[3], l[3]);
+      *reinterpret_cast<u32x2*>(ws[0] + r * LDK + c) =
+          u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+      *reinterpret_cast<u32x2*>(ws[1] + r * LDK + c) =
+          u32x2{(uint32_t)m[0] | ((uint32_t)m[1] << 16), (uint32_t)m[2] | ((uint32_t)m[3] << 16)};
+      *reinterpret_cast<u32x2*>(ws[2] + r * LDK + c) =
+          u32x2{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float a[4], b[4];
+    const int r = lane & 31, kh = (lane >> 5) * 8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
+    for (int kk = 0; kk < BK; kk += 16) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(xs + (wm0 + r) * LDK + kk + kh);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(ws[p] + (wn0 + r) * LDK + kk + kh);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
     }
     __syncthreads();
   }
+  float* out = part + (size_t)blockIdx.z * T * E;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[(size_t)t * E + e] : 0.0f);
-    }
+  for (int v = 0; v < 16; ++v) {
+    const int t = t0 + wm0 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const int e = e0 + wn0 + (lane & 31);
+    if (t < T && e < E) out[(size_t)t * E + e] = acc[v];
   }
 }
 
@@ -107,6 +135,7 @@ __global__ __launch_bounds__(256) void router_gemm(const uint16_t* __restrict__ 
 
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 16;
+constexpr int MAX_SPLIT = 8;  // router K-slices summed by route_topk
 
 // Order-preserving map of f32 to uint32: a > b  <=>  key(a) > key(b).
 // NaN (outside the contract) maps to 0, below every other value.
@@ -117,6 +146,7 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 }
 
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
+// (the K-slice partials summed in slice order, then the bias added).
 // Selection is a radix select on the order keys: 32 rounds of wave ballots
 // build the k-th largest key K bit by bit (the largest value with at least k
 // keys >= it).  Every expert above K is selected, and of those equal to K the
@@ -124,7 +154,8 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // index.  Each selected expert's place in ascending id order comes from the
 // ballot masks; its weight is its softmax probability over all E experts
 // (max-subtracted), divided by the sum over the k when `renorm`.
-__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int nsplit,
+                                                  const float* __restrict__ bias,
                                                   int32_t* __restrict__ ids,
                                                   float* __restrict__ w, int T, int E, int k,
                                                   int renorm) {
@@ -136,11 +167,21 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
   const int groups = (E + WAVE - 1) / WAVE;
   float l[NPL];
   uint32_t key[NPL];
-  const float* row = logits + (size_t)t * E;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + WAVE * i;
-    const float v = (i < groups && e < E) ? row[e] : -INFINITY;
+    float v = -INFINITY;
+    if (i < groups && e < E) {
+      float ps[MAX_SPLIT];  // all slices loaded before the in-order sum
+#pragma unroll
+      for (int sp = 0; sp < MAX_SPLIT; ++sp)
+        ps[sp] = sp < nsplit ? part[((size_t)sp * T + t) * E + e] : 0.0f;
+      v = ps[0];
+#pragma unroll
+      for (int sp = 1; sp < MAX_SPLIT; ++sp)
+        if (sp < nsplit) v += ps[sp];
+      if (bias) v += bias[(size_t)t * E + e];
+    }
     l[i] = (v == v) ? v : -INFINITY;
     key[i] = order_key(v);
   }
