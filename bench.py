@@ -53,6 +53,67 @@ def expert_stage_bytes(wl, U, T):
     return gateup, down
 
 
+COPY_BYTES = 512 * 2 ** 20
+
+
+def copy_probe():
+    """A plain device-to-device copy of COPY_BYTES, 20 times: the reference for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 20}))
+
+
+def _pmc_means(path, counter):
+    """Mean counter value per dispatch, by kernel name, from a rocprofv3 CSV."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(args):
+    """profiles/traffic.json from four rocprofv3 --pmc CSVs (FETCH_SIZE and
+    WRITE_SIZE of the benchmark, then of --copy-probe).  Each counter is scaled
+    by the ratio of the copy's known bytes to what the counter read for it."""
+    fetch, write, cfetch, cwrite = args.write_traffic
+    def copy_kib(path, counter):
+        m = _pmc_means(path, counter)
+        k = [v for n, v in m.items() if "copyBuffer" in n or "copy" in n.lower()]
+        return max(k)
+    f_fetch = COPY_BYTES / (copy_kib(cfetch, "FETCH_SIZE") * 1024.0)
+    f_write = COPY_BYTES / (copy_kib(cwrite, "WRITE_SIZE") * 1024.0)
+    mf, mw = _pmc_means(fetch, "FETCH_SIZE"), _pmc_means(write, "WRITE_SIZE")
+    key = args.traffic_key
+    kern = args.traffic_kernel
+    names = [n for n in mf if kern in n]
+    assert names, f"no kernel matching {kern}"
+    name = names[0]
+    fb = mf[name] * 1024.0 * f_fetch
+    wb = mw.get(name, 0.0) * 1024.0 * f_write
+    out = {}
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            out = json.load(f)
+    out.setdefault("entries", {})[key] = {
+        "kernel": name, "kernel_source": kernel_source_hash(),
+        "fetch_kib_per_launch": round(mf[name], 1), "write_kib_per_launch": round(mw.get(name, 0.0), 1),
+        "copy_scale_fetch": round(f_fetch, 4), "copy_scale_write": round(f_write, 4),
+        "bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb), "write_bytes": int(wb)}
+    with open(args.traffic, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out["entries"][key]))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,8 +130,21 @@ def main():
                     help="bounded CPU-oracle sample (0 disables)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 --pmc")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a known-size copy (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="write --traffic from rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--traffic-key", default="olmoe-decode/T=8/decode/gateup")
+    ap.add_argument("--traffic-kernel", default="dec_gateup")
     args = ap.parse_args()
 
+    if args.write_traffic:
+        write_traffic(args)
+        return
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this layer "
               "build runs on a single MI355X).", file=sys.stderr)

@@ -42,7 +42,8 @@ struct moe_plan_s {
   int t_decode = 0;  // AUTO: decode variant for T <= t_decode
   int dec_nrg = 0;     // decode row groups per wavefront (0: chosen from the shape)
   int dec_stream = 0;  // 1: register-resident activations + row-group prefetch variant
-  int dec_persist = 0; // >0: persistent decode grid of CUs * dec_persist blocks
+  int dec_persist = -1; // >0: persistent decode grid of CUs * dec_persist blocks; <0: by shape
+  int dec_wpb = 4;     // wavefronts per decode workgroup
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -142,26 +143,28 @@ inline int dec_cpl(int K) {
 }
 
 template <int FMT, bool GATEUP, int TG, int CPL>
-void launch_dec_cfg(int grid_x, int N, int K, int rpw_total, int T, const uint16_t* x,
+void launch_dec_cfg(int grid_x, int N, int K, int rpw_total, int wpb, int T, const uint16_t* x,
                     const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
                     uint16_t* hout, float* y, hipStream_t st) {
-  const dim3 g(grid_x, (N + 4 * rpw_total - 1) / (4 * rpw_total));
+  const int rows_per_block = wpb * rpw_total;
+  const dim3 g(grid_x, (N + rows_per_block - 1) / rows_per_block);
   if (GATEUP)
-    dec_gateup<FMT, TG, CPL, dec_rpw(CPL)><<<g, 256, 0, st>>>(x, A, B, info, tok_of, hout, K, N, T,
-                                                             rpw_total);
+    dec_gateup<FMT, TG, CPL, dec_rpw(CPL)><<<g, WAVE * wpb, 0, st>>>(x, A, B, info, tok_of, hout, K,
+                                                                    N, T, rpw_total);
   else
-    dec_down<FMT, TG, CPL, dec_rpw(CPL)><<<g, 256, 0, st>>>(hin, A, info, y, N, K, rpw_total);
+    dec_down<FMT, TG, CPL, dec_rpw(CPL)><<<g, WAVE * wpb, 0, st>>>(hin, A, info, y, N, K,
+                                                                  rpw_total);
 }
 
 template <int FMT, bool GATEUP, int CPL>
-void launch_dec_cpl(int T, int grid_x, int N, int K, int rpw_total, const uint16_t* x,
+void launch_dec_cpl(int T, int grid_x, int N, int K, int rpw_total, int wpb, const uint16_t* x,
                     const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
                     uint16_t* hout, float* y, hipStream_t st) {
   if (T == 1)
-    launch_dec_cfg<FMT, GATEUP, 1, CPL>(grid_x, N, K, rpw_total, T, x, hin, A, B, info, tok_of,
-                                        hout, y, st);
+    launch_dec_cfg<FMT, GATEUP, 1, CPL>(grid_x, N, K, rpw_total, wpb, T, x, hin, A, B, info,
+                                        tok_of, hout, y, st);
   else
-    launch_dec_cfg<FMT, GATEUP, dec_tgmax(CPL), CPL>(grid_x, N, K, rpw_total, T, x, hin, A, B,
+    launch_dec_cfg<FMT, GATEUP, dec_tgmax(CPL), CPL>(grid_x, N, K, rpw_total, wpb, T, x, hin, A, B,
                                                      info, tok_of, hout, y, st);
 }
 
@@ -182,8 +185,8 @@ void launch_dec(moe_plan_s* p, int T, int n_slots, int N, int K, const uint16_t*
   const int rpw_total = rpw * nrg;
 #define MOE_DEC_CASE(C)                                                                        \
   case C:                                                                                      \
-    launch_dec_cpl<FMT, GATEUP, C>(T, n_slots, N, K, rpw_total, x, hin, A, B, info, tok_of, \
-                                   hout, y, st);                                               \
+    launch_dec_cpl<FMT, GATEUP, C>(T, n_slots, N, K, rpw_total, p->dec_wpb, x, hin, A, B, info, \
+                                   tok_of, hout, y, st);                                       \
     break;
   switch (cpl) {
     MOE_DEC_CASE(0)
@@ -225,9 +228,18 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
   const int32_t* tok_of = reinterpret_cast<const int32_t*>(ws + L.tok_of);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* y = reinterpret_cast<float*>(ws + L.y);
-  if (path_for(p, T) == MOE_PATH_DECODE && p->dec_persist > 0) {
+  // Persistent decode grid (CUs x persist workgroups walking (expert, row pair)
+  // items) when each wavefront gets a few items: measured faster there, and
+  // slower with one item or with tens of items per wavefront.
+  int persist = p->dec_persist;
+  if (persist < 0) {
+    const long long items = (long long)std::min(T * p->d.top_k, p->d.n_experts) * (f / 2);
+    const long long per_wave = items / (6LL * 4 * p->cus);
+    persist = (per_wave >= 2 && per_wave <= 8) ? 6 : 0;
+  }
+  if (path_for(p, T) == MOE_PATH_DECODE && persist > 0) {
     const int32_t* n_act = reinterpret_cast<const int32_t*>(ws + L.n_active);
-    const int blocks = p->cus * p->dec_persist;
+    const int blocks = p->cus * persist;
     mark(p, MOE_STAGE_GATEUP, false, st);
     if (T == 1)
       dec_gateup_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
@@ -353,6 +365,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_PERSIST")) p->dec_persist = std::atoi(v);
+  if (const char* v = std::getenv("MOE_DEC_WPB")) p->dec_wpb = std::max(1, std::min(16, std::atoi(v)));
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "

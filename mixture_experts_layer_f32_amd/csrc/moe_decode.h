@@ -269,17 +269,17 @@ __device__ __forceinline__ void dec_stream(const uint8_t* const (&q)[NM],
 
 // Gate/up + SwiGLU: for every slot of the expert (sorted position p),
 // h[p][n] = bf16(silu(g[n]) * u[n]).  grid.x: slot_info entry; grid.y:
-// blocks of 4 wavefronts x `rpw_total` rows.  CPL = 0 selects the looping
+// blocks of (blockDim / 64) wavefronts x `rpw_total` rows.  CPL = 0 selects the looping
 // matvec (rows longer than one pass).
 template <int FMT, int TG, int CPL, int RPW>
-__global__ __launch_bounds__(256) void dec_gateup(
+__global__ __launch_bounds__(1024) void dec_gateup(
     const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ slot_info,
     const int32_t* __restrict__ tok_of, uint16_t* __restrict__ h, int d, int f, int T,
     int rpw_total) {
   const int4 info = slot_info[blockIdx.x];
   if (info.x < 0) return;
   const int e = info.x, p0 = info.y, cnt = info.z;
-  const int n0 = (blockIdx.y * 4 + wave_id()) * rpw_total;
+  const int n0 = (blockIdx.y * (blockDim.x / WAVE) + wave_id()) * rpw_total;
   if (n0 >= f) return;
   const int nrows = min(rpw_total, f - n0);
   const int64_t rb = row_bytes<FMT>(d);
@@ -305,13 +305,13 @@ __global__ __launch_bounds__(256) void dec_gateup(
 // Down projection: y[p][m] = sum_n h[p][n] Wd[m][n] (f32) for every sorted
 // position p of the expert.
 template <int FMT, int TG, int CPL, int RPW>
-__global__ __launch_bounds__(256) void dec_down(
+__global__ __launch_bounds__(1024) void dec_down(
     const uint16_t* __restrict__ h, DMat down, const int4* __restrict__ slot_info,
     float* __restrict__ y, int d, int f, int rpw_total) {
   const int4 info = slot_info[blockIdx.x];
   if (info.x < 0) return;
   const int e = info.x, p0 = info.y, cnt = info.z;
-  const int m0 = (blockIdx.y * 4 + wave_id()) * rpw_total;
+  const int m0 = (blockIdx.y * (blockDim.x / WAVE) + wave_id()) * rpw_total;
   if (m0 >= d) return;
   const int nrows = min(rpw_total, d - m0);
   const int64_t rb = row_bytes<FMT>(f);
