@@ -51,6 +51,7 @@ struct moe_plan_s {
   int timing_max = 0;
   int timing_n = 0;
   std::vector<hipEvent_t> timing_ev;  // [forward][stage][begin, end]
+  std::vector<uint32_t> timing_done;  // [forward]: bit s = stage s recorded
 };
 
 namespace {
@@ -122,6 +123,7 @@ Layout layout(const moe_plan_s* p, int T) {
 void mark(moe_plan_s* p, int stage, bool end, hipStream_t s) {
   if (!(p->timing_mask >> stage & 1u) || p->timing_n >= p->timing_max) return;
   (void)hipEventRecord(p->timing_ev[((size_t)p->timing_n * MOE_N_STAGES + stage) * 2 + end], s);
+  if (end) p->timing_done[p->timing_n] |= 1u << stage;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -385,6 +387,7 @@ moe_status moe_timing_disable(moe_plan_t p) {
   if (p == nullptr) return MOE_ERR_NULL_ARG;
   for (hipEvent_t e : p->timing_ev) (void)hipEventDestroy(e);
   p->timing_ev.clear();
+  p->timing_done.clear();
   p->timing_mask = 0;
   p->timing_max = p->timing_n = 0;
   return MOE_OK;
@@ -396,6 +399,7 @@ moe_status moe_timing_enable(moe_plan_t p, uint32_t stage_mask, int32_t max_forw
     return MOE_ERR_BAD_SHAPE;
   moe_timing_disable(p);
   p->timing_ev.assign((size_t)max_forwards * MOE_N_STAGES * 2, nullptr);
+  p->timing_done.assign((size_t)max_forwards, 0u);
   for (int f = 0; f < max_forwards; ++f)
     for (int st = 0; st < MOE_N_STAGES; ++st)
       if (stage_mask >> st & 1u)
@@ -418,13 +422,15 @@ moe_status moe_timing_collect(moe_plan_t p, float* stage_ms, int32_t* n_forwards
   const int n = p->timing_n;
   if (n_forwards) *n_forwards = n;
   if (n == 0 || p->timing_mask == 0) return MOE_OK;
+  const uint32_t last_done = p->timing_done[n - 1];
+  if (last_done == 0u) return MOE_OK;
   int last = MOE_N_STAGES - 1;
-  while (!(p->timing_mask >> last & 1u)) --last;
+  while (!(last_done >> last & 1u)) --last;
   hipError_t err = hipEventSynchronize(p->timing_ev[((size_t)(n - 1) * MOE_N_STAGES + last) * 2 + 1]);
   if (err != hipSuccess) return hip_fail(p, err, "hipEventSynchronize");
   for (int f = 0; f < n; ++f)
     for (int st = 0; st < MOE_N_STAGES; ++st) {
-      if (!(p->timing_mask >> st & 1u)) continue;
+      if (!(p->timing_done[f] >> st & 1u)) continue;
       float ms = 0.0f;
       const size_t i = ((size_t)f * MOE_N_STAGES + st) * 2;
       err = hipEventElapsedTime(&ms, p->timing_ev[i], p->timing_ev[i + 1]);
@@ -432,6 +438,7 @@ moe_status moe_timing_collect(moe_plan_t p, float* stage_ms, int32_t* n_forwards
       stage_ms[st] += ms;
     }
   p->timing_n = 0;
+  std::fill(p->timing_done.begin(), p->timing_done.end(), 0u);
   return MOE_OK;
 }
 
@@ -523,10 +530,42 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
     router_mfma<<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
   }
   mark(p, MOE_STAGE_ROUTER, true, s);
+  const int ng = (E + WAVE - 1) / WAVE;
+  const int ngp = ng <= 1 ? 1 : ng <= 2 ? 2 : ng <= 4 ? 4 : ng <= 8 ? 8 : 16;
+  if (T <= 16) {
+    // a2 + a3 in one workgroup
+    mark(p, MOE_STAGE_TOPK, false, s);
+#define MOE_SMALL(NG)                                                                            \
+  route_small<NG><<<1, 1024, 0, s>>>(logits, nsplit, logit_bias, ids, w, cnt, off, prm, inv,     \
+                                     reinterpret_cast<int32_t*>(ws + L.tok_of),                  \
+                                     reinterpret_cast<int4*>(ws + L.slot_info),                  \
+                                     reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots,     \
+                                     reinterpret_cast<int4*>(ws + L.tiles),                      \
+                                     reinterpret_cast<int32_t*>(ws + L.n_tiles), T, E, k,        \
+                                     p->d.renorm, gemm_bm(p, T))
+    switch (ngp) {
+      case 1: MOE_SMALL(1); break;
+      case 2: MOE_SMALL(2); break;
+      case 4: MOE_SMALL(4); break;
+      case 8: MOE_SMALL(8); break;
+      default: MOE_SMALL(16); break;
+    }
+#undef MOE_SMALL
+    mark(p, MOE_STAGE_TOPK, true, s);
+  } else {
   // a2: softmax + top-k
   mark(p, MOE_STAGE_TOPK, false, s);
-  route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, logit_bias, ids, w, T, E, k,
-                                         p->d.renorm);
+#define MOE_TOPK(NG)                                                                          \
+  route_topk<NG><<<(T + 3) / 4, 256, 0, s>>>(logits, nsplit, logit_bias, ids, w, T, E, k, \
+                                             p->d.renorm)
+  switch (ngp) {
+    case 1: MOE_TOPK(1); break;
+    case 2: MOE_TOPK(2); break;
+    case 4: MOE_TOPK(4); break;
+    case 8: MOE_TOPK(8); break;
+    default: MOE_TOPK(16); break;
+  }
+#undef MOE_TOPK
   mark(p, MOE_STAGE_TOPK, true, s);
   // a3: counting-sort permute
   mark(p, MOE_STAGE_PERMUTE, false, s);
@@ -539,6 +578,7 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                                                   reinterpret_cast<int32_t*>(ws + L.tok_of), S, E,
                                                   k);
   mark(p, MOE_STAGE_PERMUTE, true, s);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return hip_fail(p, err, "routing launch");
 

@@ -154,6 +154,80 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // index.  Each selected expert's place in ascending id order comes from the
 // ballot masks; its weight is its softmax probability over all E experts
 // (max-subtracted), divided by the sum over the k when `renorm`.
+template <int NG>
+__device__ __forceinline__ void topk_token(int t, const float* __restrict__ part, int nsplit,
+                                           const float* __restrict__ bias,
+                                           int32_t* __restrict__ ids, float* __restrict__ w,
+                                           int T, int E, int k, int renorm) {
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;
+  float l[NG];
+  uint32_t key[NG];
+  bool valid[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int e = lane + WAVE * i;
+    valid[i] = e < E;
+    const size_t col = (size_t)t * E + min(e, E - 1);
+    float ps[MAX_SPLIT];  // every slice loaded (clamped index) before the in-order sum
+#pragma unroll
+    for (int sp = 0; sp < MAX_SPLIT; ++sp) ps[sp] = part[(size_t)min(sp, nsplit - 1) * T * E + col];
+    float v = ps[0];
+#pragma unroll
+    for (int sp = 1; sp < MAX_SPLIT; ++sp) v += sp < nsplit ? ps[sp] : 0.0f;
+    if (bias) v += bias[col];
+    v = v == 0.0f ? 0.0f : v;  // one key for both signed zeros
+    l[i] = valid[i] && v == v ? v : -INFINITY;
+    key[i] = valid[i] ? order_key(v) : 0u;
+  }
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) n += __popcll(__ballot(valid[i] && key[i] >= cand));
+    if (n >= k) thr = cand;
+  }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) above += __popcll(__ballot(valid[i] && key[i] > thr));
+  const int need = k - above;  // places left for keys equal to the threshold
+  int ties_before = 0, sel_before = 0;
+  bool take[NG];
+  int pos[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const uint64_t tie = __ballot(valid[i] && key[i] == thr);
+    take[i] = valid[i] && (key[i] > thr ||
+                           (key[i] == thr && ties_before + __popcll(tie & below) < need));
+    const uint64_t sm = __ballot(take[i]);
+    pos[i] = sel_before + __popcll(sm & below);
+    ties_before += __popcll(tie);
+    sel_before += __popcll(sm);
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) m = fmaxf(m, l[i]);
+  m = wave_max(m);
+  float z = 0.0f, ps = 0.0f, ex[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    ex[i] = valid[i] ? __expf(l[i] - m) : 0.0f;
+    z += ex[i];
+    ps += take[i] ? ex[i] : 0.0f;
+  }
+  z = wave_sum(z);
+  ps = wave_sum(ps) / z;
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+    if (take[i]) {
+      const float p = ex[i] / z;
+      ids[(size_t)t * k + pos[i]] = lane + WAVE * i;
+      w[(size_t)t * k + pos[i]] = renorm ? p / ps : p;
+    }
+}
+
+template <int NG>
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int nsplit,
                                                   const float* __restrict__ bias,
                                                   int32_t* __restrict__ ids,
@@ -161,84 +235,7 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
                                                   int renorm) {
   const int t = blockIdx.x * 4 + wave_id();
   if (t >= T) return;
-  const int lane = lane_id();
-  const uint64_t below = (1ull << lane) - 1ull;
-  constexpr int NPL = MAX_E / WAVE;
-  const int groups = (E + WAVE - 1) / WAVE;
-  float l[NPL];
-  uint32_t key[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + WAVE * i;
-    float v = -INFINITY;
-    if (i < groups && e < E) {
-      float ps[MAX_SPLIT];  // all slices loaded before the in-order sum
-#pragma unroll
-      for (int sp = 0; sp < MAX_SPLIT; ++sp)
-        ps[sp] = sp < nsplit ? part[((size_t)sp * T + t) * E + e] : 0.0f;
-      v = ps[0];
-#pragma unroll
-      for (int sp = 1; sp < MAX_SPLIT; ++sp)
-        if (sp < nsplit) v += ps[sp];
-      if (bias) v += bias[(size_t)t * E + e];
-    }
-    l[i] = (v == v) ? v : -INFINITY;
-    key[i] = order_key(v);
-  }
-  auto valid = [&](int i) { return lane + WAVE * i < E; };
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (i < groups) n += __popcll(__ballot(valid(i) && key[i] >= cand));
-    if (n >= k) thr = cand;
-  }
-  int above = 0;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i)
-    if (i < groups) above += __popcll(__ballot(valid(i) && key[i] > thr));
-  const int need = k - above;  // places left for keys equal to the threshold
-  uint32_t sel = 0;            // bit i: expert lane + 64 i is selected
-  int ties_before = 0, sel_before = 0, pos[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    pos[i] = 0;
-    if (i < groups) {
-      const uint64_t tie = __ballot(valid(i) && key[i] == thr);
-      const bool take = valid(i) && (key[i] > thr ||
-                                     (key[i] == thr && ties_before + __popcll(tie & below) < need));
-      const uint64_t sm = __ballot(take);
-      if (take) {
-        sel |= 1u << i;
-        pos[i] = sel_before + __popcll(sm & below);
-      }
-      ties_before += __popcll(tie);
-      sel_before += __popcll(sm);
-    }
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) m = fmaxf(m, l[i]);
-  m = wave_max(m);
-  float z = 0.0f, ps = 0.0f;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i)
-    if (i < groups && valid(i)) {
-      const float ex = __expf(l[i] - m);
-      z += ex;
-      if (sel >> i & 1u) ps += ex;
-    }
-  z = wave_sum(z);
-  ps = wave_sum(ps) / z;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i)
-    if (sel >> i & 1u) {
-      const float p = __expf(l[i] - m) / z;
-      ids[(size_t)t * k + pos[i]] = lane + WAVE * i;
-      w[(size_t)t * k + pos[i]] = renorm ? p / ps : p;
-    }
+  topk_token<NG>(t, part, nsplit, bias, ids, w, T, E, k, renorm);
 }
 
 // ---------------------------------------------------------------- permute
@@ -363,6 +360,60 @@ __global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict
     tok_of[p] = s / k;
   }
   inv_perm[s] = min(max(p, 0), S - 1);
+}
+
+// Few tokens (T <= 16, one per wavefront): top-k and the whole counting-sort permute in one 1024-thread
+// workgroup (the same arithmetic as route_topk + permute_count/scan/scatter
+// with a single 64-token chunk): 16 wavefronts take the tokens' top-k, then
+// LDS lane masks give the stable ranks, one scan gives counts, offsets, the
+// per-expert records and the tile list, and the scatter writes perm,
+// inv_perm and the token of each sorted position.
+template <int NG>
+__global__ __launch_bounds__(1024) void route_small(
+    const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ tok_of, int4* __restrict__ slot_info, int32_t* __restrict__ n_active,
+    int n_slots, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles, int T, int E, int k,
+    int renorm, int BM) {
+  __shared__ unsigned long long mask[MAX_E];
+  __shared__ int off_s[MAX_E];
+  const int tid = threadIdx.x;
+  for (int t = wave_id(); t < T; t += 16) topk_token<NG>(t, part, nsplit, bias, ids, w, T, E, k, renorm);
+  for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
+  __syncthreads();  // ids written by this workgroup are visible to it after the barrier
+  if (tid < T)
+    for (int j = 0; j < k; ++j) atomicOr(&mask[min(max(ids[tid * k + j], 0), E - 1)], 1ull << tid);
+  __syncthreads();
+  const int e = tid;
+  const int c_e = e < E ? __popcll(mask[e]) : 0;
+  if (e < E) counts[e] = c_e;
+  int tot;
+  const int off = block_exclusive_scan(e < E ? c_e : 0, &tot);
+  if (e < E) {
+    offsets[e] = off;
+    off_s[e] = off;
+  }
+  const int S = T * k;
+  if (e == 0) offsets[E] = S;
+  const int act = block_exclusive_scan((e < E && c_e > 0) ? 1 : 0, &tot);
+  if (e < E && c_e > 0) slot_info[act] = make_int4(e, off, c_e, 0);
+  if (e == 0) *n_active = tot;
+  for (int i = tot + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
+  const int mt = (e < E) ? (c_e + BM - 1) / BM : 0;
+  const int tb = block_exclusive_scan(mt, &tot);
+  for (int i = 0; i < mt; ++i) tiles[tb + i] = make_int4(e, off + i * BM, min(BM, c_e - i * BM), 0);
+  if (e == 0) *n_tiles = tot;
+  __syncthreads();
+  for (int s = tid; s < S; s += 1024) {
+    const int t = s / k;
+    const int ex = min(max(ids[s], 0), E - 1);
+    const unsigned long long below = t == 0 ? 0ull : (~0ull >> (WAVE - t));
+    const int p = off_s[ex] + __popcll(mask[ex] & below);
+    perm[p] = s;
+    inv_perm[s] = p;
+    tok_of[p] = t;
+  }
 }
 
 }  // namespace moe
