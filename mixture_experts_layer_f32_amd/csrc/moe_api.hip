@@ -44,6 +44,7 @@ struct moe_plan_s {
   int dec_stream = 0;  // 1: register-resident activations + row-group prefetch variant
   int dec_persist = -1; // >0: persistent decode grid of CUs * dec_persist blocks; <0: by shape
   int dec_wpb = 4;     // wavefronts per decode workgroup
+  int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -83,10 +84,29 @@ int gemm_bm(const moe_plan_s* p, int T) {
   return per >= 96 ? 128 : (per >= 40 ? 64 : 32);
 }
 
+// The MFMA decode addresses activations with 32-bit buffer offsets.
+bool dec_mfma_fits(const moe_plan_s* p, int T) {
+  const long long lim = 1LL << 31;
+  return (long long)T * p->d.d_model * 2 < lim &&
+         (long long)T * p->d.top_k * p->d.d_ff * 2 < lim;
+}
+
+// MFMA tiles for the decode expert stage, except e2m1 with one or two tokens:
+// there an e2m1 weight byte carries two inputs, the activation operand costs
+// twice the registers per weight byte, and the wavefront matvec is faster.
+bool use_dec_mfma(const moe_plan_s* p, int T) {
+  if (path_for(p, T) != MOE_PATH_DECODE || p->dec_kernel != 1 || !dec_mfma_fits(p, T)) return false;
+  return p->d.wfmt == MOE_W_E4M3_B128 || T > 2;
+}
+
+// Rows per entry of the routing stage's tile list: 16-slot entries for the
+// MFMA decode, else the grouped-GEMM tile height.
+int tile_rows(const moe_plan_s* p, int T) { return use_dec_mfma(p, T) ? 16 : gemm_bm(p, T); }
+
 Layout layout(const moe_plan_s* p, int T) {
   const size_t E = p->d.n_experts, k = p->d.top_k, d = p->d.d_model, f = p->d.d_ff;
   const size_t S = (size_t)T * k;
-  const size_t BM = gemm_bm(p, T);
+  const size_t BM = tile_rows(p, T);
   Layout L;
   L.nchunk = (T + WAVE - 1) / WAVE;
   L.max_tiles = (int)((S + BM - 1) / BM + std::min<size_t>(E, S));
@@ -239,7 +259,47 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
     const long long per_wave = items / (6LL * 4 * p->cus);
     persist = (per_wave >= 2 && per_wave <= 8) ? 6 : 0;
   }
-  if (path_for(p, T) == MOE_PATH_DECODE && persist > 0) {
+  if (use_dec_mfma(p, T)) {
+    const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
+    const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
+    const long long S = (long long)T * p->d.top_k;
+    const uint32_t x_bytes = (uint32_t)((size_t)T * d * 2);
+    const uint32_t h_bytes = (uint32_t)((size_t)S * f * 2);
+    // Tile height: 16-row groups per tile (more rows share one activation
+    // operand), taken larger only while the tile list stays several times the
+    // persistent grid (upper bound of the list: one entry per expert hit plus
+    // one per further 16 slots).
+    const long long entries = std::min<long long>(p->d.n_experts, S) + (T > 16 ? S / 16 : 0);
+    auto big = [&](int N, int rows) { return entries * ((N + rows - 1) / rows) >= 4LL * 3 * p->cus; };
+    auto run = [&](bool gateup) {
+      const int K = gateup ? d : f;
+      const int ku = FMT == FMT_E4M3 ? 128 : 256;
+      const int ks = std::min(4, (K + ku - 1) / ku);
+      const dim3 blk(WAVE * ks);
+      const bool tall = FMT == FMT_E4M3 && big(gateup ? f : d, gateup ? 32 : 64);
+      if (gateup) {
+        if constexpr (FMT == FMT_E4M3)
+          if (tall) {
+            dec_mfma<FMT, true, 2, 3><<<p->cus * 2, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
+            return;
+          }
+        dec_mfma<FMT, true, 1, 2><<<p->cus * 3, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
+      } else {
+        if constexpr (FMT == FMT_E4M3)
+          if (tall) {
+            dec_mfma<FMT, false, 4, 2><<<p->cus * 2, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+            return;
+          }
+        dec_mfma<FMT, false, 2, 2><<<p->cus * 3, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+      }
+    };
+    mark(p, MOE_STAGE_GATEUP, false, st);
+    run(true);
+    mark(p, MOE_STAGE_GATEUP, true, st);
+    mark(p, MOE_STAGE_DOWN, false, st);
+    run(false);
+    mark(p, MOE_STAGE_DOWN, true, st);
+  } else if (path_for(p, T) == MOE_PATH_DECODE && persist > 0) {
     const int32_t* n_act = reinterpret_cast<const int32_t*>(ws + L.n_active);
     const int blocks = p->cus * persist;
     mark(p, MOE_STAGE_GATEUP, false, st);
@@ -368,6 +428,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_PERSIST")) p->dec_persist = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_WPB")) p->dec_wpb = std::max(1, std::min(16, std::atoi(v)));
+  if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "
@@ -542,7 +603,7 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                                      reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots,     \
                                      reinterpret_cast<int4*>(ws + L.tiles),                      \
                                      reinterpret_cast<int32_t*>(ws + L.n_tiles), T, E, k,        \
-                                     p->d.renorm, gemm_bm(p, T))
+                                     p->d.renorm, tile_rows(p, T))
     switch (ngp) {
       case 1: MOE_SMALL(1); break;
       case 2: MOE_SMALL(2); break;
@@ -573,7 +634,7 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   permute_scan<<<1, 1024, 0, s>>>(hist, base, cnt, off, reinterpret_cast<int4*>(ws + L.slot_info),
                                   reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots, reinterpret_cast<int4*>(ws + L.tiles),
                                   reinterpret_cast<int32_t*>(ws + L.n_tiles), L.nchunk, E, S,
-                                  gemm_bm(p, T));
+                                  tile_rows(p, T));
   permute_scatter<<<(S + 255) / 256, 256, 0, s>>>(ids, rank, base, off, prm, inv,
                                                   reinterpret_cast<int32_t*>(ws + L.tok_of), S, E,
                                                   k);

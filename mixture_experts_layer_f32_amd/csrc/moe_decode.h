@@ -379,6 +379,272 @@ __global__ __launch_bounds__(256) void dec_down_persist(
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA decode.  The expert stage for few tokens per expert as 16 x 16 output
+// tiles on v_mfma_f32_16x16x32_bf16: A = 16 weight rows decoded exactly to
+// bf16, B = up to 16 token columns (activation rows; columns past the
+// expert's count read as zero), f32 accumulation.  The work list is the
+// routing stage's tile list built with 16 rows per entry, so every entry
+// holds at most 16 sorted positions of one expert.
+//
+// Lane l of a wavefront owns weight row n0 + (l & 15) and k-slot q = l >> 4.
+// For e4m3 and a 128-input block starting at k0 it supplies, to MFMA a = 0..3,
+// the 8 inputs k0 + 16q + 8a (a < 2) or k0 + 64 + 16q + 8(a - 2) (two 16-byte
+// loads per row and lane); for e2m1 and 256 inputs from k0, to MFMA 4h + a,
+// the inputs k0 + 128h + 32q + 8a (two 16-byte loads); token
+// column (l & 15) takes the activations of the same inputs, so every MFMA sums
+// products of matching (row, input) and (input, token) pairs.  e4m3: the four
+// MFMAs of a block start from zero and their sum is multiplied by the block's
+// scale and added to the running f32 sum (one f32 accumulation per 128 x 128
+// scale block); e2m1: the ue8m0 scale of the lane's 32-input group is applied
+// exactly inside the conversion.
+//
+// Persistent grid: workgroup b takes tiles b, b + G, b + 2G, ... (so the tiles
+// in flight at any time are neighbours in HBM); its KS wavefronts split each
+// tile's 128-input blocks (wave w: blocks w, w + KS, ...) and sum their
+// partial tiles through LDS in wave order.  Each wavefront streams its
+// (tile, block) units with D units of loads in flight.  All loads are buffer
+// loads: a unit past the end, an input past K or a token column past the
+// count uses an out-of-range offset and reads zeros without a memory access.
+constexpr uint32_t BUF_OOB = 0x80000000u;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, int imm) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, imm, 0));
+}
+__device__ __forceinline__ bf16x8 pack_bf16x8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  const u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                   __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// 8 e4m3 codes (two words, low byte first) -> 8 bf16
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return pack_bf16x8(e4m3x2_to_bf16<false>(lo), e4m3x2_to_bf16<true>(lo),
+                     e4m3x2_to_bf16<false>(hi), e4m3x2_to_bf16<true>(hi));
+}
+// 8 e2m1 codes (one word, low nibble first) times their power-of-two scale -> 8 bf16
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w, float sc) {
+  return pack_bf16x8(e2m1x2_to_bf16<0>(w, sc), e2m1x2_to_bf16<1>(w, sc),
+                     e2m1x2_to_bf16<2>(w, sc), e2m1x2_to_bf16<3>(w, sc));
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One unit = one (tile, k-range) step of a wavefront: per matrix and 16-row
+// group, two 16-byte weight loads per lane (e4m3: 128 inputs, one scale
+// block; e2m1: 256 inputs, the lane's two 32-input groups at k0 + 32q and
+// k0 + 128 + 32q), and the activations of those inputs, shared by all of the
+// unit's row groups and matrices.
+template <int FMT> struct DecUnitW;
+template <> struct DecUnitW<FMT_E4M3> { u32x4 w[2]; };
+template <> struct DecUnitW<FMT_E2M1> { u32x4 w[2]; uint32_t sb[2]; };
+template <int FMT> constexpr int dec_unit_k() { return FMT == FMT_E4M3 ? 128 : 256; }
+template <int FMT> constexpr int dec_unit_x() { return FMT == FMT_E4M3 ? 4 : 8; }
+
+// GATEUP: h[p][n] = bf16(silu(g) * u) for the f rows n of gate/up (K = d,
+// activations x[tok_of[p]]); else y[p][m] (f32) for the d rows of down
+// (K = f, activations h[p]).  A tile is RT groups of 16 rows; D units of
+// loads in flight per wavefront.  act_bytes: extent of the activation buffer.
+template <int FMT, bool GATEUP, int RT, int D>
+__global__ __launch_bounds__(256) void dec_mfma(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, DMat A, DMat B,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles_p,
+    const int32_t* __restrict__ tok_of, void* __restrict__ outp, int N, int K, int T) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int KU = dec_unit_k<FMT>(), NX = dec_unit_x<FMT>();
+  constexpr int TR = 16 * RT;  // rows per tile
+  __shared__ f32x4 red[2][3][NM * RT][WAVE];
+  const int KS = blockDim.x / WAVE;
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int r = lane & 15, q = lane >> 4;
+  const int tpe = (N + TR - 1) / TR;
+  const int n_tiles = *n_tiles_p * tpe;
+  const int G = gridDim.x, b = blockIdx.x;
+  if (b >= n_tiles) return;
+  const int my_tiles = (n_tiles - b + G - 1) / G;
+  const int nkb = (K + KU - 1) / KU;
+  const int nu = (nkb - w + KS - 1) / KS;  // units per tile for this wavefront (>= 1)
+  const int units = my_tiles * nu;
+  const uint32_t rb = FMT == FMT_E4M3 ? (uint32_t)K : (uint32_t)K / 2;
+  const uint32_t q_bytes = (uint32_t)N * rb, s_bytes = (uint32_t)N * (uint32_t)(K >> 5);
+  const __amdgpu_buffer_rsrc_t ar = buf_rsrc(act, act_bytes);
+  const DMat M[2] = {A, B};
+
+  struct Unit {
+    DecUnitW<FMT> wv[NM][RT];
+    u32x4 x[NX];
+    float sc[NM];
+  };
+  auto issue = [&](Unit& s, int u) {
+    const int jt = u / nu;
+    const int kb = w + KS * (u - jt * nu);
+    const int tile = b + jt * G;
+    const int ti = tile / tpe, n0 = (tile - ti * tpe) * TR;
+    const int4 info = tiles[ti];
+    const int e = info.x, p0 = info.y, cnt = info.z;
+    const int k0 = kb * KU;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc(M[m].q + e * M[m].qs, q_bytes);
+      if constexpr (FMT == FMT_E4M3) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int n = n0 + 16 * t + r;
+          const uint32_t off = n < N ? (uint32_t)n * rb + k0 + 16 * q : BUF_OOB;
+          s.wv[m][t].w[0] = buf_load16(wr, off, 0);
+          s.wv[m][t].w[1] = buf_load16(wr, off, 64);
+        }
+        s.sc[m] = reinterpret_cast<const float*>(M[m].s + e * M[m].ss)[(n0 >> 7) * (K >> 7) + kb];
+      } else {
+        const __amdgpu_buffer_rsrc_t sr = buf_rsrc(M[m].s + e * M[m].ss, s_bytes);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int n = n0 + 16 * t + r;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int k = k0 + 128 * h + 32 * q;
+            const bool in = n < N && k < K;
+            s.wv[m][t].w[h] = buf_load16(wr, in ? (uint32_t)n * rb + k / 2 : BUF_OOB, 0);
+            s.wv[m][t].sb[h] = __builtin_amdgcn_raw_buffer_load_b8(
+                sr, in ? (uint32_t)n * (K >> 5) + (k >> 5) : BUF_OOB, 0, 0);
+          }
+        }
+        s.sc[m] = 0.0f;
+      }
+    }
+    // activation row of token column r: gate/up takes the entry's (<= 16)
+    // tokens by scalar loads, lane r keeping entry r; down reads h[p0 + r]
+    uint32_t row = (uint32_t)(p0 + min(r, cnt - 1));
+    if (GATEUP) {
+      const int32_t* tp = tok_of + p0;
+      int t = tp[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) {
+        const int tj = tp[min(j, cnt - 1)];
+        t = r == j ? tj : t;
+      }
+      row = min((uint32_t)t, (uint32_t)(T - 1));
+    }
+    if constexpr (FMT == FMT_E4M3) {
+      const uint32_t off = r < cnt ? (row * K + k0 + 16 * q) * 2 : BUF_OOB;
+      s.x[0] = buf_load16(ar, off, 0);
+      s.x[1] = buf_load16(ar, off, 16);
+      s.x[2] = buf_load16(ar, off, 128);
+      s.x[3] = buf_load16(ar, off, 144);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = k0 + 128 * h + 32 * q;
+        const uint32_t off = r < cnt && k < K ? (row * K + k) * 2 : BUF_OOB;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) s.x[4 * h + a] = buf_load16(ar, off, 16 * a);
+      }
+    }
+  };
+  f32x4 acc[NM][RT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Unit& s) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const DecUnitW<FMT>& wq = s.wv[m][t];
+        if constexpr (FMT == FMT_E4M3) {
+          f32x4 part = mfma16x16x32(e4m3x8_to_bf16(wq.w[0].x, wq.w[0].y),
+                                    __builtin_bit_cast(bf16x8, s.x[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+          part = mfma16x16x32(e4m3x8_to_bf16(wq.w[0].z, wq.w[0].w), __builtin_bit_cast(bf16x8, s.x[1]), part);
+          part = mfma16x16x32(e4m3x8_to_bf16(wq.w[1].x, wq.w[1].y), __builtin_bit_cast(bf16x8, s.x[2]), part);
+          part = mfma16x16x32(e4m3x8_to_bf16(wq.w[1].z, wq.w[1].w), __builtin_bit_cast(bf16x8, s.x[3]), part);
+          const float sc = s.sc[m];
+          acc[m][t] = f32x4{fmaf(part.x, sc, acc[m][t].x), fmaf(part.y, sc, acc[m][t].y),
+                            fmaf(part.z, sc, acc[m][t].z), fmaf(part.w, sc, acc[m][t].w)};
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float sc = ue8m0_to_f32(wq.sb[h]);
+            const u32x4 v = wq.w[h];
+            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.x, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 0]), acc[m][t]);
+            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.y, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 1]), acc[m][t]);
+            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.z, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 2]), acc[m][t]);
+            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.w, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 3]), acc[m][t]);
+          }
+        }
+      }
+  };
+  // Tile done: partial tiles of waves 1..KS-1 through LDS (double-buffered by
+  // tile parity, so one barrier per tile), summed by wave 0 in wave order.
+  // D[i][j] of lane l: rows 4q + i (i = 0..3) of a 16-row group, token column l & 15.
+  auto finish = [&](int jt) {
+    const int par = jt & 1;
+    if (w > 0) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) red[par][w - 1][m * RT + t][lane] = acc[m][t];
+    }
+    __syncthreads();
+    if (w == 0) {
+      for (int v = 0; v < KS - 1; ++v)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int t = 0; t < RT; ++t) {
+            const f32x4 o = red[par][v][m * RT + t][lane];
+            acc[m][t] = f32x4{acc[m][t].x + o.x, acc[m][t].y + o.y, acc[m][t].z + o.z, acc[m][t].w + o.w};
+          }
+      const int tile = b + jt * G;
+      const int ti = tile / tpe, n0 = (tile - ti * tpe) * TR;
+      const int4 info = tiles[ti];
+      if (r < info.z) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int n = n0 + 16 * t + 4 * q;
+          if (n < N) {
+            const size_t o = (size_t)(info.y + r) * N + n;
+            if (GATEUP) {
+              const f32x4 g = acc[0][t], u = acc[NM - 1][t];
+              const uint32_t h0 = f32_to_bf16_rne(silu(g.x) * u.x), h1 = f32_to_bf16_rne(silu(g.y) * u.y);
+              const uint32_t h2 = f32_to_bf16_rne(silu(g.z) * u.z), h3 = f32_to_bf16_rne(silu(g.w) * u.w);
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(outp) + o) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
+            } else {
+              *reinterpret_cast<f32x4*>(static_cast<float*>(outp) + o) = acc[0][t];
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Software pipeline over the unit stream; loads past the end are not issued
+  // (uniform branches), so the tail computes from units already in flight.
+  Unit st[D];
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s)
+    if (s < units) issue(st[s], s);
+  for (int u0 = 0; u0 < units; u0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (u0 + s + D - 1 < units) issue(st[(s + D - 1) % D], u0 + s + D - 1);
+      const int u = u0 + s;
+      if (u < units) {
+        compute(st[s]);
+        const int jt = u / nu;
+        if (u - jt * nu == nu - 1) finish(jt);
+      }
+    }
+  }
+}
+
 // out[t][m] = sum over j ascending of w[t][j] * y[inv_perm[t*k+j]][m]: a
 // gather in router order, so every output has one fixed summation order
 // (WARP BACKENDS.md, "Coherent memory": partials reduced in router order).
