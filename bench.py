@@ -136,7 +136,7 @@ def main():
                                                          "COPY_WRITE_CSV"),
                     help="write --traffic from rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--traffic-key", default="olmoe-decode/T=8/decode/gateup")
-    ap.add_argument("--traffic-kernel", default="dec_gateup")
+    ap.add_argument("--traffic-kernel", default="dec_mfma<0, true")
     args = ap.parse_args()
 
     if args.write_traffic:

@@ -45,6 +45,7 @@ struct moe_plan_s {
   int dec_persist = -1; // >0: persistent decode grid of CUs * dec_persist blocks; <0: by shape
   int dec_wpb = 4;     // wavefronts per decode workgroup
   int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
+  int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -91,12 +92,14 @@ bool dec_mfma_fits(const moe_plan_s* p, int T) {
          (long long)T * p->d.top_k * p->d.d_ff * 2 < lim;
 }
 
-// MFMA tiles for the decode expert stage, except e2m1 with one or two tokens:
-// there an e2m1 weight byte carries two inputs, the activation operand costs
-// twice the registers per weight byte, and the wavefront matvec is faster.
+// MFMA tiles for the decode expert stage from dec_mfma_min_t tokens; for a
+// single token the wavefront matvec is faster (measured, both formats): each
+// expert then has one slot, 15 of the MFMA's 16 token columns are empty, and
+// the matvec's single batch of loads per wavefront has the shorter latency
+// chain.
 bool use_dec_mfma(const moe_plan_s* p, int T) {
   if (path_for(p, T) != MOE_PATH_DECODE || p->dec_kernel != 1 || !dec_mfma_fits(p, T)) return false;
-  return p->d.wfmt == MOE_W_E4M3_B128 || T > 2;
+  return T >= p->dec_mfma_min_t;
 }
 
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
@@ -429,6 +432,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_PERSIST")) p->dec_persist = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_WPB")) p->dec_wpb = std::max(1, std::min(16, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
+  if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "
