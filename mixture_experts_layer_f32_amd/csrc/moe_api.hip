@@ -46,6 +46,7 @@ struct moe_plan_s {
   int dec_wpb = 4;     // wavefronts per decode workgroup
   int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
+  int gemm_kernel = 1;    // grouped expert stage: 1 = register-weight tiles (e4m3), 0 = LDS weight tiles
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -104,7 +105,11 @@ bool use_dec_mfma(const moe_plan_s* p, int T) {
 
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
 // MFMA decode, else the grouped-GEMM tile height.
-int tile_rows(const moe_plan_s* p, int T) { return use_dec_mfma(p, T) ? 16 : gemm_bm(p, T); }
+int tile_rows(const moe_plan_s* p, int T) {
+  if (use_dec_mfma(p, T)) return 16;
+  if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel >= 1) return 64;
+  return gemm_bm(p, T);
+}
 
 Layout layout(const moe_plan_s* p, int T) {
   const size_t E = p->d.n_experts, k = p->d.top_k, d = p->d.d_model, f = p->d.d_ff;
@@ -229,10 +234,45 @@ void launch_dec(moe_plan_s* p, int T, int n_slots, int N, int K, const uint16_t*
 
 // Grouped GEMM launch: grid (column blocks of N, tile-list entries), LDS
 // sized per configuration (above the 64 KB static limit, set once).
+// Super-block order of the grouped kernels: about the workgroups one XCD
+// holds at once (2 per CU).
+struct GemmOrder {
+  int nb, gc, gt, ntb;
+  long long grid;
+};
+GemmOrder gemm_order(const moe_plan_s* p, int max_tiles, int N, int bnm) {
+  GemmOrder o;
+  o.nb = (N + bnm - 1) / bnm;
+  o.gc = std::max(1, std::min(4, (o.nb + 7) / 8));
+  o.gt = std::max(1, (p->cus / 8) * 2 / o.gc);
+  o.ntb = (max_tiles + o.gt - 1) / o.gt;
+  const int ncb = (o.nb + 8 * o.gc - 1) / (8 * o.gc);
+  o.grid = 8LL * o.gc * o.gt * o.ntb * ncb;
+  return o;
+}
+
+template <int FMT, bool GATEUP, int TNW>
+void launch_dma(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
+                DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
+                void* out, hipStream_t st) {
+  const GemmOrder o = gemm_order(p, max_tiles, N, DmaCfg<FMT, GATEUP, TNW>::BNM);
+  gemm_dma<FMT, GATEUP, TNW><<<dim3((unsigned)o.grid), 256, 0, st>>>(
+      act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
+}
+
+template <int FMT, bool GATEUP, int TNW, int PD>
+void launch_rw(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
+               DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
+               void* out, hipStream_t st) {
+  const GemmOrder o = gemm_order(p, max_tiles, N, RWCfg<FMT, GATEUP, TNW>::BNM);
+  gemm_rw<FMT, GATEUP, TNW, PD><<<dim3((unsigned)o.grid), 256, 0, st>>>(
+      act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
+}
+
 template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK, int PF>
-void launch_gemm(int max_tiles, int N, int K, int T, const uint16_t* act, DMat W0, DMat W1,
-                 const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of, void* out,
-                 hipStream_t st) {
+void launch_gemm(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
+                 DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles,
+                 const int32_t* tok_of, void* out, hipStream_t st) {
   using C = G2<FMT, GATEUP ? 2 : 1, BM, WM, TN, BK>;
   auto kern = &gemm_expert<FMT, GATEUP, BM, WM, TN, BK, PF>;
   static bool attr_set = false;
@@ -241,8 +281,9 @@ void launch_gemm(int max_tiles, int N, int K, int T, const uint16_t* act, DMat W
                               hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
     attr_set = true;
   }
-  const dim3 g((N + C::BNM - 1) / C::BNM, max_tiles);
-  kern<<<g, 256, C::SMEM, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T);
+  const GemmOrder o = gemm_order(p, max_tiles, N, C::BNM);
+  kern<<<dim3((unsigned)o.grid), 256, C::SMEM, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K,
+                                                     T, o.nb, o.gc, o.gt, o.ntb);
 }
 
 template <int FMT>
@@ -332,26 +373,44 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
     const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
     const int bm = gemm_bm(p, T);
+    if (p->gemm_kernel == 2) {
+      mark(p, MOE_STAGE_GATEUP, false, st);
+      launch_dma<FMT, true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
+      mark(p, MOE_STAGE_GATEUP, true, st);
+      mark(p, MOE_STAGE_DOWN, false, st);
+      launch_dma<FMT, false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
+      mark(p, MOE_STAGE_DOWN, true, st);
+      return MOE_OK;
+    }
+    if (p->gemm_kernel == 1) {
+      mark(p, MOE_STAGE_GATEUP, false, st);
+      launch_rw<FMT, true, 1, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
+      mark(p, MOE_STAGE_GATEUP, true, st);
+      mark(p, MOE_STAGE_DOWN, false, st);
+      launch_rw<FMT, false, 2, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
+      mark(p, MOE_STAGE_DOWN, true, st);
+      return MOE_OK;
+    }
     mark(p, MOE_STAGE_GATEUP, false, st);
     if (bm == 128)
-      launch_gemm<FMT, true, 128, 2, 1, 64, 1>(L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
+      launch_gemm<FMT, true, 128, 2, 1, 64, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
                                                tok_of, h, st);
     else if (bm == 64)
-      launch_gemm<FMT, true, 64, 2, 1, 64, 1>(L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
+      launch_gemm<FMT, true, 64, 2, 1, 64, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
                                               tok_of, h, st);
     else
-      launch_gemm<FMT, true, 32, 1, 1, 64, 1>(L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
+      launch_gemm<FMT, true, 32, 1, 1, 64, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
                                               tok_of, h, st);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
     if (bm == 128)
-      launch_gemm<FMT, false, 128, 2, 2, 64, 1>(L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
+      launch_gemm<FMT, false, 128, 2, 2, 64, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
                                                 tok_of, y, st);
     else if (bm == 64)
-      launch_gemm<FMT, false, 64, 2, 2, 64, 1>(L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
+      launch_gemm<FMT, false, 64, 2, 2, 64, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
                                                tok_of, y, st);
     else
-      launch_gemm<FMT, false, 32, 1, 1, 64, 1>(L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
+      launch_gemm<FMT, false, 32, 1, 1, 64, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
                                                tok_of, y, st);
     mark(p, MOE_STAGE_DOWN, true, st);
   }
@@ -433,6 +492,10 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_WPB")) p->dec_wpb = std::max(1, std::min(16, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
+  // register-weight tiles measured faster for e4m3; for e2m1 at its grouped
+  // sizes (tens of slots per expert) the 64-token tile is mostly empty
+  p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 1 : 0;
+  if (const char* v = std::getenv("MOE_GEMM")) p->gemm_kernel = std::max(0, std::min(2, std::atoi(v)));
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "

@@ -1,7 +1,7 @@
 // Grouped variant of the expert stage: for many tokens per expert, each
 // expert's rows (in sorted-slot order) form the M dimension of GEMM tiles.
-// Weight tiles are read from HBM once per M-tile, decoded exactly to bf16 in
-// LDS, and multiplied with bf16 MFMA (v_mfma_f32_32x32x16_bf16) into f32.
+// Weight tiles are decoded exactly to bf16 in LDS and multiplied with bf16
+// MFMA (v_mfma_f32_32x32x16_bf16) into f32.
 //   e4m3: one f32 scale per 128x128 block; the MFMA sums of each 128-deep K
 //         block go to a fresh f32 partial that is then added to the running
 //         sum times the block's scale (dragon.c page, section 8 Round 3: the
@@ -64,22 +64,33 @@ __device__ __forceinline__ int acc_row(int v, int lane) {
   return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// grid.x: BNM-wide column block of N; grid.y: tile index (blocks past
-// *n_tiles exit).  GATEUP: act = x [T][K], out = h bf16 [S][N] (N = f,
+// Block order (1-D grid, XCD-aware).  Workgroup L is dispatched to XCD
+// L % 8; XCD x takes the BNM-wide column blocks c = x (mod 8) of N and walks
+// super-blocks of gt tile-list entries x gc of its column blocks (about the
+// workgroups one XCD holds at once): inside a super-block the gc column
+// blocks of one tile are neighbours (they share the tile's activation rows),
+// and the M tiles of one expert sit next to each other in the tile list (they
+// share the weight tile), so both are read from HBM about once per XCD
+// through its L2.  Blocks past *n_tiles or past nb
+// column blocks exit.  GATEUP: act = x [T][K], out = h bf16 [S][N] (N = f,
 // K = d); otherwise act = h [S][K], out = y f32 [S][N] (N = d, K = f).
 template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK_, int PF>
 __global__ __launch_bounds__(256, 2) void gemm_expert(
     const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
-    void* __restrict__ out, int N, int K, int T) {
+    void* __restrict__ out, int N, int K, int T, int nb, int gc, int gt, int ntb) {
   constexpr int NMAT = GATEUP ? 2 : 1;
   using C = G2<FMT, NMAT, BM, WM, TN, BK_>;
   constexpr int BK = C::BK, LDK = C::LDK, TM = C::TM, BNM = C::BNM;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  if ((int)blockIdx.y >= *n_tiles) return;
-  const int4 tile = tiles[blockIdx.y];
+  const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
+  const int sbsz = gc * gt, sb = sq / sbsz, wi = sq - sb * sbsz;
+  const int tb = sb % ntb, cb = sb / ntb;
+  const int ti = tb * gt + wi / gc, cblk = xcd + 8 * (cb * gc + wi % gc);
+  if (ti >= *n_tiles || cblk >= nb) return;
+  const int4 tile = tiles[ti];
   const int e = tile.x, p_start = tile.y, rows = tile.z;
-  const int n0 = blockIdx.x * BNM;
+  const int n0 = cblk * BNM;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int wm0 = (wv / C::WN) * (BM / WM), wn0 = (wv % C::WN) * 32 * TN;
 
@@ -120,11 +131,11 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
   // k-block kb held by lane kb % 64 of register kb / 64, read with v_readlane
   float scv[NMAT][2];
   if (FMT == FMT_E4M3) {
-    const int nb = min(n0, N - 1) >> 7, kbs = K >> 7;
+    const int nrb = min(n0, N - 1) >> 7, kbs = K >> 7;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
       const DMat& W = (m == 0) ? W0 : W1;
-      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)nb * kbs;
+      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)nrb * kbs;
       scv[m][0] = lane < kbs ? sf[lane] : 0.0f;
       scv[m][1] = lane + 64 < kbs ? sf[lane + 64] : 0.0f;
     }
@@ -147,7 +158,9 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
       const int c = (tid + 256 * i) % C::B_CPR;
       if (bq[i] != nullptr && k0 + c * C::B_EPC < K) {
         const int64_t off = FMT == FMT_E4M3 ? k0 : k0 / 2;
-        rb[set][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(bq[i] + off));
+        // a stage reads 64 (e4m3) or 32 (e2m1) bytes of a 128-byte row segment;
+        // ordinary loads keep the line in L2 for the next stage's part
+        rb[set][i] = *reinterpret_cast<const u32x4*>(bq[i] + off);
         if (FMT == FMT_E2M1) rsc[set][i] = ue8m0_to_f32(bsr[i][k0 / 32]);
       }
     }
@@ -264,6 +277,467 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
           if (GATEUP)
             reinterpret_cast<uint16_t*>(out)[(size_t)(p_start + m) * N + n] =
                 (uint16_t)f32_to_bf16_rne(silu(acc[i][j][v]) * acc[i][TN + j][v]);
+          else
+            reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = acc[i][j][v];
+        }
+      }
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Register-weight grouped GEMM.  Same product as gemm_expert, with the weights
+// kept out of LDS: each wavefront owns TNW 32-row weight tiles per matrix and
+// loads, decodes and feeds them to the MFMA from its own registers; only the
+// 64-token activation tile goes through LDS, where the four wavefronts share
+// it.  Per 16-deep MFMA step a wavefront reads 2 activation fragments from
+// LDS for 2 * NMAT * TNW MFMAs.
+//
+// v_mfma_f32_32x32x16_bf16: A = tokens (lane l: row l % 32, inputs of k-slot
+// h = l / 32), B = weight rows (lane l: row l % 32, k-slot h).  A 64-input
+// stage from k0: lane (r, h) loads the 32 weight inputs k0 + 32h .. k0 + 32h
+// + 31 of its row (e4m3: 32 bytes; e2m1: 16 bytes and the row's ue8m0 byte
+// of that 32-input group); MFMA step s = 0..3 takes inputs k0 + 32h + 8s ..
+// + 7 from both operands.
+template <int FMT, bool GATEUP, int TNW>
+struct RWCfg {
+  static constexpr int NMAT = GATEUP ? 2 : 1;
+  static constexpr int BM = 64, BK = 64, LDK = BK + 8;  // tokens, stage depth, padded LDS row
+  static constexpr int TM = BM / 32;
+  static constexpr int NW = NMAT * TNW;                 // 32-row weight tiles per wavefront
+  static constexpr int BNM = 4 * 32 * TNW;              // weight rows per matrix per workgroup
+  static_assert(128 % (32 * TNW) == 0, "a wavefront's rows lie in one 128-row scale block");
+};
+
+template <int FMT> struct RWRaw;
+template <> struct RWRaw<FMT_E4M3> { u32x4 w[2]; };
+template <> struct RWRaw<FMT_E2M1> { u32x4 w; float sc; };
+
+// GATEUP: act = x [T][K], out = h bf16 [S][N] (N = f, K = d); else act = h
+// [S][K], out = y f32 [S][N] (N = d, K = f).  Block order as gemm_expert.
+template <int FMT, bool GATEUP, int TNW, int PD>
+__global__ __launch_bounds__(256, 2) void gemm_rw(
+    const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
+    void* __restrict__ out, int N, int K, int T, int nb, int gc, int gt, int ntb) {
+  using C = RWCfg<FMT, GATEUP, TNW>;
+  constexpr int NMAT = C::NMAT, BM = C::BM, BK = C::BK, LDK = C::LDK, NW = C::NW, TM = C::TM;
+  __shared__ __attribute__((aligned(16))) uint16_t As[PD + 1][BM * LDK];
+  const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
+  const int sbsz = gc * gt, sb = sq / sbsz, wi = sq - sb * sbsz;
+  const int tb = sb % ntb, cb = sb / ntb;
+  const int ti = tb * gt + wi / gc, cblk = xcd + 8 * (cb * gc + wi % gc);
+  if (ti >= *n_tiles || cblk >= nb) return;
+  const int4 tile = tiles[ti];
+  const int e = tile.x, p_start = tile.y, rows = tile.z;
+  const int n0 = cblk * C::BNM;
+  const int tid = threadIdx.x, lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nw0 = n0 + 32 * TNW * w;  // this wavefront's first weight row
+
+  // activation tile: 64 rows x 64 inputs = 512 16-byte chunks, 2 per thread
+  const int acol = (tid & 7) * 8;
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (tid + 256 * i) >> 3;
+    arow[i] = nullptr;
+    if (r < rows) {
+      const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + r], (uint32_t)(T - 1))
+                                : (size_t)(p_start + r);
+      arow[i] = act + src * K;
+    }
+  }
+  // weight rows of this lane: tile idx = m * TNW + j holds row nw0 + 32j + r32 of matrix m
+  const int64_t rbytes = FMT == FMT_E4M3 ? (int64_t)K : (int64_t)K / 2;
+  const uint8_t* wrow[NW];
+  const uint8_t* srow[NW];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      const DMat& W = m == 0 ? W0 : W1;
+      const int n = nw0 + 32 * j + r32;
+      wrow[m * TNW + j] = n < N ? W.q + e * W.qs + n * rbytes : nullptr;
+      srow[m * TNW + j] = n < N ? W.s + e * W.ss + (int64_t)n * (K >> 5) : nullptr;
+    }
+  const float* sblk[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    const DMat& W = m == 0 ? W0 : W1;
+    sblk[m] = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * (K >> 7);
+  }
+
+  auto load_a = [&](u32x4 (&ra)[2], int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ra[i] = arow[i] != nullptr && k0 + acol < K
+                  ? *reinterpret_cast<const u32x4*>(arow[i] + k0 + acol) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto load_w = [&](RWRaw<FMT> (&rw)[NW], int k0) {
+    const int k = k0 + 32 * h;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      const bool ok = wrow[t] != nullptr && k < K;
+      if constexpr (FMT == FMT_E4M3) {
+        rw[t].w[0] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k) : u32x4{0u, 0u, 0u, 0u};
+        rw[t].w[1] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k + 16) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        rw[t].w = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k / 2) : u32x4{0u, 0u, 0u, 0u};
+        rw[t].sc = ok ? ue8m0_to_f32(srow[t][k >> 5]) : 1.0f;
+      }
+    }
+  };
+  auto store_a = [&](const u32x4 (&ra)[2], uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<u32x4*>(buf + ((tid + 256 * i) >> 3) * LDK + acol) = ra[i];
+  };
+
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 acc[TM][NW], part[FMT == FMT_E4M3 ? TM : 1][FMT == FMT_E4M3 ? NW : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < NW; ++t) acc[i][t] = zero;
+  if constexpr (FMT == FMT_E4M3) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < NW; ++t) part[i][t] = zero;
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  // One stage: issue the loads of stage ks + PD (clamped to the last stage, so
+  // every stage issues the same loads and the wait counts stay static), run
+  // the MFMAs of stage ks from LDS buffer ks % (PD + 1) and weight set `cur`,
+  // then put stage ks + 1's activations (loaded PD - 1 stages ago) into LDS.
+  constexpr int NB = PD + 1;  // LDS activation buffers and register sets
+  // `even`: ks is even (compile-time after unrolling when NB is even): an
+  // e4m3 scale block (two stages) starts there and ends on the odd stage
+  auto stage = [&](int ks, bool even, const RWRaw<FMT> (&cur)[NW], RWRaw<FMT> (&pf)[NW],
+                   u32x4 (&ra_pf)[2], const u32x4 (&ra_next)[2]) {
+    const int kp = min(ks + PD, nk - 1) * BK;
+    load_a(ra_pf, kp);
+    load_w(pf, kp);
+    const uint16_t* buf = As[ks % NB];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 a[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(buf + (32 * i + r32) * LDK + 32 * h + 8 * s);
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        bf16x8 b;
+        if constexpr (FMT == FMT_E4M3) {
+          const u32x4 v = cur[t].w[s >> 1];
+          b = (s & 1) ? e4m3x8_to_bf16(v.z, v.w) : e4m3x8_to_bf16(v.x, v.y);
+        } else {
+          const u32x4 v = cur[t].w;
+          b = e2m1x8_to_bf16(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, cur[t].sc);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (FMT == FMT_E4M3)
+            part[i][t] = (even && s == 0)
+                             ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, zero, 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, part[i][t], 0, 0, 0);
+          else
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][t], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (FMT == FMT_E4M3) {
+      if (!even || ks == nk - 1) {  // end of a scale block: acc += scale * partial
+        const int kb = ks >> 1;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const float sc = sblk[m][kb];
+#pragma unroll
+          for (int j = 0; j < TNW; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][m * TNW + j][v] += sc * part[i][m * TNW + j][v];
+        }
+      }
+    }
+    if (ks + 1 < nk) store_a(ra_next, As[(ks + 1) % NB]);
+    __syncthreads();
+  };
+
+  // prologue: stages 0 .. PD-1 loaded, stage 0's activations in LDS
+  RWRaw<FMT> wr[NB][NW];
+  u32x4 ra[NB][2];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) {
+    load_a(ra[p], min(p, nk - 1) * BK);
+    load_w(wr[p], min(p, nk - 1) * BK);
+  }
+  store_a(ra[0], As[0]);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (ks + j < nk)
+        stage(ks + j, NB % 2 == 0 ? (j % 2 == 0) : ((ks + j) % 2 == 0), wr[j], wr[(j + PD) % NB],
+              ra[(j + PD) % NB], ra[(j + 1) % NB]);
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 32 * i + acc_row(v, lane);
+        const int n = nw0 + 32 * j + r32;
+        if (m < rows && n < N) {
+          if (GATEUP)
+            reinterpret_cast<uint16_t*>(out)[(size_t)(p_start + m) * N + n] =
+                (uint16_t)f32_to_bf16_rne(silu(acc[i][j][v]) * acc[i][TNW + j][v]);
+          else
+            reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = acc[i][j][v];
+        }
+      }
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS grouped GEMM: as gemm_rw (64 tokens x 4 wavefronts x TNW
+// 32-row weight tiles per matrix), but every tile byte travels from global
+// memory to LDS by global_load_lds_dwordx4 (lane l's 16 bytes land at LDS
+// base + 16 l), so PD stages of loads are in flight without holding VGPRs.
+// Activations: 64 rows x 128 bytes per stage, row r's 16-byte chunk c stored
+// at slot c ^ (r & 7) (the MFMA fragment reads of 8 consecutive rows then hit
+// 8 different bank groups).  Weights: each wavefront parks its own lanes'
+// bytes and reads them back into the same lanes (no sharing, so no barrier
+// for them); one barrier per stage publishes the activations and frees the
+// buffer the next loads go to.  Each pipeline slot is its own LDS array, so
+// a wait for one slot's loads leaves the others in flight.
+template <int FMT, bool GATEUP, int TNW>
+struct DmaCfg {
+  static constexpr int NMAT = GATEUP ? 2 : 1;
+  static constexpr int BM = 64, BK = 64, TM = 2;
+  static constexpr int NW = NMAT * TNW;
+  static constexpr int BNM = 4 * 32 * TNW;
+  static constexpr int WLD = FMT == FMT_E4M3 ? 2 : 1;          // 16-byte weight loads per tile and stage
+  static constexpr int A_V4 = BM * 8;                           // u32x4 per activation stage (8 KB)
+  static constexpr int W_V4 = 4 * NW * WLD * 64;                // u32x4 per weight stage
+  static constexpr int LOADS = 2 + NW * WLD + (FMT == FMT_E2M1 ? NW : 0);  // vector loads per wavefront and stage
+};
+
+// The direct-to-LDS loads and the stage barrier are issued as inline
+// assembly: the compiler cannot tell the pipeline slots apart and would
+// otherwise drain every outstanding load (vmcnt(0)) before each LDS read and
+// each barrier.  The pipeline orders them itself: a wavefront waits until at
+// most one stage of its loads is outstanding (vmcnt), then the barrier makes
+// every wavefront's completed stage visible.
+__device__ __forceinline__ void lds_dma16(const void* g, const u32x4* l) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)l);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int FMT, bool GATEUP, int TNW>
+__global__ __launch_bounds__(256, 2) void gemm_dma(
+    const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
+    void* __restrict__ out, int N, int K, int T, int nb, int gc, int gt, int ntb) {
+  using C = DmaCfg<FMT, GATEUP, TNW>;
+  constexpr int NMAT = C::NMAT, NW = C::NW, TM = C::TM, BK = C::BK, WLD = C::WLD;
+  __shared__ u32x4 sA0[C::A_V4], sA1[C::A_V4], sA2[C::A_V4];
+  __shared__ u32x4 sW0[C::W_V4], sW1[C::W_V4], sW2[C::W_V4];
+  const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
+  const int sbsz = gc * gt, sb = sq / sbsz, wi = sq - sb * sbsz;
+  const int tb = sb % ntb, cb = sb / ntb;
+  const int ti = tb * gt + wi / gc, cblk = xcd + 8 * (cb * gc + wi % gc);
+  if (ti >= *n_tiles || cblk >= nb) return;
+  const int4 tile = tiles[ti];
+  const int e = tile.x, p_start = tile.y, rows = tile.z;
+  const int n0 = cblk * C::BNM;
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nw0 = n0 + 32 * TNW * w;
+
+  // activation loads of this lane: 2 per stage (rows (2w + i) * 8 + lane / 8,
+  // LDS slot lane % 8 holding chunk slot ^ (row & 7)); rows past the tile
+  // repeat its last row (their products only reach outputs that are not stored)
+  const uint16_t* asrc[2];
+  int achunk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (2 * w + i) * 8 + (lane >> 3);
+    const int rr = min(r, rows - 1);
+    const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
+                              : (size_t)(p_start + rr);
+    asrc[i] = act + src * K;
+    achunk[i] = (lane & 7) ^ (r & 7);
+  }
+  // weight rows of this lane (clamped to the matrix; columns past N are not stored)
+  const int64_t rbytes = FMT == FMT_E4M3 ? (int64_t)K : (int64_t)K / 2;
+  const uint8_t* wrow[NW];
+  const uint8_t* srow[NW];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      const DMat& W = m == 0 ? W0 : W1;
+      const int n = min(nw0 + 32 * j + r32, N - 1);
+      wrow[m * TNW + j] = W.q + e * W.qs + n * rbytes;
+      srow[m * TNW + j] = W.s + e * W.ss + (int64_t)n * (K >> 5);
+    }
+  // e4m3: the scale row of this wavefront's 128-row block, k-block kb held by
+  // lane kb % 64 of register kb / 64 (loaded before the pipeline starts)
+  float scv[NMAT][2];
+  if constexpr (FMT == FMT_E4M3) {
+    const int kbs = K >> 7;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const DMat& W = m == 0 ? W0 : W1;
+      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
+      scv[m][0] = lane < kbs ? sf[lane] : 0.0f;
+      scv[m][1] = lane + 64 < kbs ? sf[lane + 64] : 0.0f;
+    }
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  // stage kk's loads into one pipeline slot (stages past the end repeat the
+  // last one so every stage issues the same loads); e2m1: the lanes' ue8m0
+  // scale bytes go to registers
+  auto issue = [&](int kk, const u32x4* sA, const u32x4* sW, float (&scs)[NW]) {
+    const int k0 = min(kk, nk - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int kc = min(k0 + 8 * achunk[i], K - 8);
+      lds_dma16(asrc[i] + kc, sA + (2 * w + i) * 64);
+    }
+    const int kl = min(k0 + 32 * h, K - 32);  // weight inputs of this lane (k-tail clamped; zeroed at decode)
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      if constexpr (FMT == FMT_E4M3) {
+        lds_dma16(wrow[t] + kl, sW + ((w * NW + t) * 2 + 0) * 64);
+        lds_dma16(wrow[t] + kl + 16, sW + ((w * NW + t) * 2 + 1) * 64);
+      } else {
+        lds_dma16(wrow[t] + kl / 2, sW + (w * NW + t) * 64);
+        scs[t] = ue8m0_to_f32(srow[t][kl >> 5]);
+      }
+    }
+  };
+
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 acc[TM][NW], part[FMT == FMT_E4M3 ? TM : 1][FMT == FMT_E4M3 ? NW : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < NW; ++t) acc[i][t] = zero;
+  if constexpr (FMT == FMT_E4M3) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < NW; ++t) part[i][t] = zero;
+  }
+
+  auto compute = [&](int ks, const u32x4* sA, const u32x4* sW, const float (&scs)[NW]) {
+    const bool first = (ks & 1) == 0;
+    const bool ktail = ks * BK + 32 * h >= K;  // e2m1: this lane's inputs past K
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 a[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = 32 * i + r32;
+        a[i] = __builtin_bit_cast(bf16x8, sA[m * 8 + ((4 * h + s) ^ (m & 7))]);
+      }
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        bf16x8 b;
+        if constexpr (FMT == FMT_E4M3) {
+          const u32x4 v = sW[((w * NW + t) * 2 + (s >> 1)) * 64 + lane];
+          b = (s & 1) ? e4m3x8_to_bf16(v.z, v.w) : e4m3x8_to_bf16(v.x, v.y);
+        } else {
+          const u32x4 v = sW[(w * NW + t) * 64 + lane];
+          const uint32_t word = ktail ? 0u : (s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w);
+          b = e2m1x8_to_bf16(word, scs[t]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (FMT == FMT_E4M3)
+            part[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, (first && s == 0) ? zero : part[i][t], 0, 0, 0);
+          else
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][t], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (FMT == FMT_E4M3) {
+      if ((ks & 1) == 1 || ks == nk - 1) {
+        const int kb = ks >> 1;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const float sc = __int_as_float(__builtin_amdgcn_readlane(
+              __float_as_int(kb < 64 ? scv[m][0] : scv[m][1]), kb & 63));
+#pragma unroll
+          for (int j = 0; j < TNW; ++j)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[i][m * TNW + j][v] += sc * part[i][m * TNW + j][v];
+        }
+      }
+    }
+  };
+
+  // three slots, two stages in flight: at stage ks wait for its loads, one
+  // barrier (activations visible; slot of stage ks - 1 free), issue stage ks + 2
+  // into that slot, compute stage ks
+  float sc0[NW], sc1[NW], sc2[NW];
+  constexpr int LD = C::LOADS;
+  issue(0, sA0, sW0, sc0);
+  issue(1, sA1, sW1, sc1);
+  for (int ks = 0; ks < nk; ks += 3) {
+    wait_vm<LD>();
+    stage_barrier();
+    issue(ks + 2, sA2, sW2, sc2);
+    compute(ks, sA0, sW0, sc0);
+    if (ks + 1 >= nk) break;
+    wait_vm<LD>();
+    stage_barrier();
+    issue(ks + 3, sA0, sW0, sc0);
+    compute(ks + 1, sA1, sW1, sc1);
+    if (ks + 2 >= nk) break;
+    wait_vm<LD>();
+    stage_barrier();
+    issue(ks + 4, sA1, sW1, sc1);
+    compute(ks + 2, sA2, sW2, sc2);
+  }
+  // no load may still be writing this workgroup's LDS when it ends
+  wait_vm<0>();
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 32 * i + acc_row(v, lane);
+        const int n = nw0 + 32 * j + r32;
+        if (m < rows && n < N) {
+          if (GATEUP)
+            reinterpret_cast<uint16_t*>(out)[(size_t)(p_start + m) * N + n] =
+                (uint16_t)f32_to_bf16_rne(silu(acc[i][j][v]) * acc[i][TNW + j][v]);
           else
             reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = acc[i][j][v];
         }
