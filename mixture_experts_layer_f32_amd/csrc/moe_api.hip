@@ -46,6 +46,7 @@ struct moe_plan_s {
   int dec_wpb = 4;     // wavefronts per decode workgroup
   int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
+  int dec_tall = -1;      // MFMA decode tiles of 32/64 rows: -1 by shape, 0 never, 1 always
   int gemm_kernel = 1;    // grouped expert stage: 1 = register-weight tiles (e4m3), 0 = LDS weight tiles
   std::string info;
   std::string last_error;
@@ -320,21 +321,23 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
       const int ku = FMT == FMT_E4M3 ? 128 : 256;
       const int ks = std::min(4, (K + ku - 1) / ku);
       const dim3 blk(WAVE * ks);
-      const bool tall = FMT == FMT_E4M3 && big(gateup ? f : d, gateup ? 32 : 64);
+      // e2m1: an input byte holds two weights, so the activation operand
+      // outweighs the weights once the tiles' token columns fill; taller tiles
+      // then share it over more rows (measured: faster at 16 slots per expert,
+      // slower at 4)
+      bool tall = big(gateup ? f : d, gateup ? 32 : 64) &&
+                  (FMT == FMT_E4M3 || S >= 16LL * p->d.n_experts);
+      if (p->dec_tall >= 0) tall = p->dec_tall == 1;
       if (gateup) {
-        if constexpr (FMT == FMT_E4M3)
-          if (tall) {
-            dec_mfma<FMT, true, 2, 3><<<p->cus * 2, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
-            return;
-          }
-        dec_mfma<FMT, true, 1, 2><<<p->cus * 3, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
+        if (tall)
+          dec_mfma<FMT, true, 2, FMT == FMT_E4M3 ? 3 : 2><<<p->cus * 2, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
+        else
+          dec_mfma<FMT, true, 1, 2><<<p->cus * 3, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
       } else {
-        if constexpr (FMT == FMT_E4M3)
-          if (tall) {
-            dec_mfma<FMT, false, 4, 2><<<p->cus * 2, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
-            return;
-          }
-        dec_mfma<FMT, false, 2, 2><<<p->cus * 3, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+        if (tall)
+          dec_mfma<FMT, false, 4, 2><<<p->cus * 2, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+        else
+          dec_mfma<FMT, false, 2, 2><<<p->cus * 3, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
       }
     };
     mark(p, MOE_STAGE_GATEUP, false, st);
@@ -483,8 +486,12 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   p->device = dev;
   p->cus = prop.multiProcessorCount;
   p->arch = prop.gcnArchName;
-  // Decode while the slots per expert stay small: T*k <= 4*E.
-  p->t_decode = std::max(1, 4 * d.n_experts / d.top_k);
+  // Decode (every selected expert's weights streamed once per 16 of its slots)
+  // while the slots per expert stay small; measured crossovers against the
+  // grouped GEMM: T*k about 12*E for e4m3 (OLMoE shape between T = 64 and 128,
+  // the d = 7168 layer between 256 and 512); e2m1 decode was faster at every
+  // size measured, up to T*k = 16*E.
+  p->t_decode = std::max(1, (d.wfmt == MOE_W_E4M3_B128 ? 12 : 16) * d.n_experts / d.top_k);
   // tuning knobs of the decode matvec
   if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
@@ -492,6 +499,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_WPB")) p->dec_wpb = std::max(1, std::min(16, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
+  if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
   // register-weight tiles measured faster for e4m3; for e2m1 at its grouped
   // sizes (tens of slots per expert) the 64-token tile is mostly empty
   p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 1 : 0;
