@@ -78,6 +78,7 @@ def lib():
         L.synth_ue8m0.argtypes = [vp, i64, vp]
         L.synth_quant_e4m3_b128.argtypes = [vp, i64, i64, vp, vp]
         L.synth_quant_e2m1_g32.argtypes = [vp, i64, i64, vp, vp]
+        L.synth_quant_nvfp4_g16.argtypes = [vp, i64, i64, vp, vp]
         L.synth_expert_matrices.argtypes = [u64, u64, i64, i64, i64, i64, ctypes.c_double,
                                             ctypes.c_int, vp, vp]
         _lib = L
@@ -161,6 +162,17 @@ def quant_e2m1_g32(w: np.ndarray):
     return q, s
 
 
+def quant_nvfp4_g16(w: np.ndarray):
+    """[N, K] f32 -> (packed codes uint8 [N, K/2], E4M3 scale codes uint8 [N, K/16])."""
+    w = np.ascontiguousarray(w, np.float32)
+    N, K = w.shape
+    assert K % 16 == 0
+    q = np.empty((N, K // 2), np.uint8)
+    s = np.empty((N, K // 16), np.uint8)
+    lib().synth_quant_nvfp4_g16(_p(w), N, K, _p(q), _p(s))
+    return q, s
+
+
 # ------------------------------------------------------------------ workloads
 
 @dataclass(frozen=True)
@@ -170,7 +182,7 @@ class Workload:
     f: int          # expert FFN width
     E: int          # number of experts
     k: int          # experts per token
-    fmt: str        # "e4m3" (128x128 f32 scales) or "e2m1" (UE8M0 per 32)
+    fmt: str        # "e4m3" (128x128 f32 scales), "e2m1" (UE8M0 per 32), "nvfp4" (E4M3 per 16)
     renorm: bool    # renormalise the k routing weights to sum to 1
     batches: tuple = ()
     skew: bool = False
@@ -185,6 +197,9 @@ WORKLOADS = {
     "large-e4m3": Workload("large-e4m3", 7168, 2048, 256, 8, "e4m3", True, (1, 64, 4096), False,
                            1003),
     "fp4-e2m1": Workload("fp4-e2m1", 4096, 2880, 384, 6, "e2m1", True, (1, 16, 1024), False, 1004),
+    # NVFP4 experts of the Qwen-Flash-Next post: three 2560x640 matrices, top-10 of 512
+    "nvfp4-qwen": Workload("nvfp4-qwen", 2560, 640, 512, 10, "nvfp4", True, (1, 16, 256), False,
+                           1005),
 }
 
 
@@ -192,6 +207,8 @@ def expert_bytes(w: Workload) -> int:
     """Bytes of one expert (three matrices, codes + scales)."""
     if w.fmt == "e4m3":
         return 3 * w.d * w.f + 3 * 4 * (w.d // 128) * (w.f // 128)
+    if w.fmt == "nvfp4":
+        return 3 * w.d * w.f // 2 + 3 * w.d * w.f // 16
     return 3 * w.d * w.f // 2 + 3 * w.d * w.f // 32
 
 
@@ -228,11 +245,16 @@ def _expert_mats(seed, stream_base, E, N, K, stddev, fmt) -> QMat:
         q = np.empty((E, N, K), np.uint8)
         s = np.empty((E, N // 128, K // 128), np.float32)
         f = 0
-    else:
+    elif fmt == "e2m1":
         assert N % 32 == 0 and K % 32 == 0
         q = np.empty((E, N, K // 2), np.uint8)
         s = np.empty((E, N, K // 32), np.uint8)
         f = 1
+    else:
+        assert fmt == "nvfp4" and N % 32 == 0 and K % 32 == 0
+        q = np.empty((E, N, K // 2), np.uint8)
+        s = np.empty((E, N, K // 16), np.uint8)
+        f = 2
     lib().synth_expert_matrices(seed, stream_base, 0, E, N, K, stddev, f, _p(q), _p(s))
     return QMat(q, s, N, K)
 

@@ -258,9 +258,36 @@ void synth_quant_e2m1_g32(const float* w, int64_t N, int64_t K, uint8_t* q, uint
     }
 }
 
+/* Quantise one [N x K] f32 matrix to packed e2m1 codes [N][K/2] with one
+ * E4M3 scale byte per 16 consecutive inputs [N][K/16] (K multiple of 16): the
+ * group's scale is amax/6, stored as its E4M3 code (round to nearest even);
+ * the codes are the e2m1 codes of w / (amax/6), so a value that the rounded
+ * scale pushes past 6 saturates. */
+void synth_quant_nvfp4_g16(const float* w, int64_t N, int64_t K, uint8_t* q, uint8_t* s) {
+  int64_t G = K / 16;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < G; ++g) {
+      const float* src = w + n * K + g * 16;
+      float amax = 0.0f;
+      for (int c = 0; c < 16; ++c) {
+        float a = fabsf(src[c]);
+        if (a > amax) amax = a;
+      }
+      const float scale = amax / 6.0f;
+      s[n * G + g] = enc_e4m3(scale);
+      uint8_t* dst = q + n * (K / 2) + g * 8;
+      for (int c = 0; c < 16; c += 2) {
+        uint8_t lo = (amax == 0.0f) ? 0 : enc_e2m1(src[c] / scale);
+        uint8_t hi = (amax == 0.0f) ? 0 : enc_e2m1(src[c + 1] / scale);
+        dst[c / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+}
+
 /* Draw and quantise the [N x K] matrix of experts e0..e0+ne-1, each from
  * its own stream (stream_base + e), entries ~ N(0, stddev^2) in f32.
- * fmt 0: e4m3 / 128x128 f32 scales; fmt 1: e2m1 / UE8M0 per 32.
+ * fmt 0: e4m3 / 128x128 f32 scales; fmt 1: e2m1 / UE8M0 per 32;
+ * fmt 2: e2m1 / E4M3 per 16.
  * q: codes of the ne experts, contiguous, expert-major; s: their scales.
  * Work is split over (expert, row band); every band is a pure function
  * of its counters, so the output does not depend on the thread count. */
@@ -269,7 +296,7 @@ void synth_expert_matrices(uint64_t seed, uint64_t stream_base, int64_t e0, int6
   const int64_t R = fmt == 0 ? 128 : 32; /* rows per band: one scale-block row for e4m3 */
   int64_t bands = N / R;
   int64_t q_per_e = fmt == 0 ? N * K : N * K / 2;
-  int64_t s_per_e = fmt == 0 ? (N / 128) * (K / 128) : N * (K / 32);
+  int64_t s_per_e = fmt == 0 ? (N / 128) * (K / 128) : (fmt == 1 ? N * (K / 32) : N * (K / 16));
 #pragma omp parallel
   {
     float* buf = (float*)malloc(sizeof(float) * (size_t)R * (size_t)K);
@@ -281,9 +308,12 @@ void synth_expert_matrices(uint64_t seed, uint64_t stream_base, int64_t e0, int6
       if (fmt == 0) {
         synth_quant_e4m3_b128(buf, R, K, q + e * q_per_e + b * R * K,
                               (float*)s + e * s_per_e + b * (K / 128));
-      } else {
+      } else if (fmt == 1) {
         synth_quant_e2m1_g32(buf, R, K, q + e * q_per_e + b * R * (K / 2),
                              (uint8_t*)s + e * s_per_e + b * R * (K / 32));
+      } else {
+        synth_quant_nvfp4_g16(buf, R, K, q + e * q_per_e + b * R * (K / 2),
+                              (uint8_t*)s + e * s_per_e + b * R * (K / 16));
       }
     }
     free(buf);

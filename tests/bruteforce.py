@@ -58,8 +58,18 @@ def dequant_e2m1(q, s):
     return val * np.kron(2.0 ** (s.astype(np.float64) - 127.0), np.ones((1, 32)))
 
 
+def dequant_nvfp4(q, s):
+    N, half = q.shape
+    nib = (q[:, :, None] >> np.array([0, 4], np.uint8)) & 0xF   # low nibble first
+    nib = nib.reshape(N, 2 * half)
+    mag = np.array(_E2M1_POS)[nib & 0x7]
+    val = np.where(nib & 0x8, -mag, mag)
+    sc = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return val * np.kron(sc, np.ones((1, 16)))
+
+
 def dequant(q, s, fmt):
-    return dequant_e4m3(q, s) if fmt == "e4m3" else dequant_e2m1(q, s)
+    return {"e4m3": dequant_e4m3, "e2m1": dequant_e2m1, "nvfp4": dequant_nvfp4}[fmt](q, s)
 
 
 def exact_logits_f32(x_bits, w_router, bias):

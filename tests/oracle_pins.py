@@ -16,6 +16,7 @@ SMALL = {
     "e4m3-nonsquare": synth.Workload("e4m3-nonsquare", 256, 384, 6, 2, "e4m3", False, (5,), False,
                                      2001),
     "e2m1-small": synth.Workload("e2m1-small", 128, 96, 8, 3, "e2m1", True, (5,), False, 2002),
+    "nvfp4-small": synth.Workload("nvfp4-small", 128, 96, 8, 3, "nvfp4", True, (5,), False, 2003),
 }
 
 _CACHE = {}
@@ -287,6 +288,7 @@ FAST_PINS = [
     lambda om: pin_bruteforce(om, "tiny"),
     lambda om: pin_bruteforce(om, "e4m3-nonsquare", biased=True),
     lambda om: pin_bruteforce(om, "e2m1-small"),
+    lambda om: pin_bruteforce(om, "nvfp4-small"),
     pin_onehot, pin_routing_closed_form, pin_router_exact, pin_topk_ties, pin_permute, pin_silu,
     pin_scale_doubling, pin_identical_experts, pin_relabel, pin_zero_input, pin_single_expert,
     pin_lossless_grid, pin_token_subset,

@@ -139,6 +139,35 @@ def test_dequant_e2m1_group_index():
     assert np.all(W[1, :32] == 0.5) and np.all(W[1, 32:] == 8.0)
 
 
+def test_dequant_nvfp4_group_index():
+    # 2 rows x 48 columns: three 16-wide groups per row; E4M3 scale codes with
+    # non-power-of-two values (0x3C = 1.5, 0x44 = 3.0, 0x33 = 0.6875) and a
+    # subnormal one (0x05 = 5 * 2^-9).
+    s = np.array([[0x38, 0x3C, 0x44], [0x30, 0x33, 0x05]], np.uint8)
+    q = np.full((2, 24), 0x22, np.uint8)     # codes (1.0, 1.0)
+    q[1, 16:] = 0xBF                          # low nibble 0xF = -6.0, high nibble 0xB = -1.5
+    W = om.dequant(q, s, "nvfp4", 48)
+    assert np.all(W[0, :16] == 1.0) and np.all(W[0, 16:32] == 1.5) and np.all(W[0, 32:] == 3.0)
+    assert np.all(W[1, :16] == 0.5) and np.all(W[1, 16:32] == 0.6875)
+    sub = 5 * 2.0 ** -9
+    assert np.all(W[1, 32::2] == -6.0 * sub) and np.all(W[1, 33::2] == -1.5 * sub)
+
+
+def test_generator_nvfp4_layout():
+    import synth
+    w = (np.arange(2 * 64, dtype=np.float32).reshape(2, 64) - 40.0) / 7.0
+    q, s = synth.quant_nvfp4_g16(w)
+    assert q.shape == (2, 32) and s.shape == (2, 4)
+    # group scale = E4M3 code of amax/6; codes within the group saturate at 6
+    amax = np.abs(w.reshape(2, 4, 16)).max(axis=2)
+    assert np.array_equal(s, synth.enc_e4m3((amax / 6.0).astype(np.float32)))
+    W = om.dequant(q, s, "nvfp4", 64)
+    err = np.abs(W - w)
+    # half an e2m1 step (at most one scale unit) plus the scale's own rounding
+    # (codes are taken against amax/6, the stored scale is its E4M3 rounding)
+    assert np.all(err <= np.repeat(om.E4M3[s], 16, axis=1) * 1.5)
+
+
 # ---------------------------------------------------------------- generator encoders
 
 

@@ -41,6 +41,20 @@ def m_e2m1_bias(q, s, fmt, K):
     return _orig["dequant"](q, s, fmt, K)
 
 
+def m_nvfp4_group32(q, s, fmt, K):
+    if fmt == "nvfp4":
+        codes = om.unpack_e2m1(q, K)
+        return om.E2M1[codes] * np.repeat(om.E4M3[s[:, ::2]], 32, axis=1)
+    return _orig["dequant"](q, s, fmt, K)
+
+
+def m_nvfp4_scale_as_ue8m0(q, s, fmt, K):
+    if fmt == "nvfp4":
+        codes = om.unpack_e2m1(q, K)
+        return om.E2M1[codes] * np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 16, axis=1)
+    return _orig["dequant"](q, s, fmt, K)
+
+
 def m_no_renorm(logits, ids, renorm):
     return _orig["routing_weights"](logits, ids, False)
 
@@ -122,6 +136,8 @@ MUTATIONS = {
     "scale_block_transposed": ("dequant", m_scale_transposed),
     "scale_divided": ("dequant", m_scale_divided),
     "e2m1_scale_bias": ("dequant", m_e2m1_bias),
+    "nvfp4_scale_group_32": ("dequant", m_nvfp4_group32),
+    "nvfp4_scale_read_as_ue8m0": ("dequant", m_nvfp4_scale_as_ue8m0),
     "dropped_renorm": ("routing_weights", m_no_renorm),
     "softmax_over_selected": ("routing_weights", m_softmax_over_selected),
     "bf16_router": ("router_logits", m_bf16_router),
