@@ -45,9 +45,10 @@ def expert_stage_bytes(wl, U, T):
     if wl.fmt == "e4m3":
         gu = 2 * (f * d + 4 * (f // 128) * (d // 128))
         dn = d * f + 4 * (d // 128) * (f // 128)
-    else:
-        gu = 2 * (f * d // 2 + f * d // 32)
-        dn = d * f // 2 + d * f // 32
+    else:  # fp4 codes + one scale byte per 32 (e2m1) or per 16 (nvfp4) inputs
+        g = 32 if wl.fmt == "e2m1" else 16
+        gu = 2 * (f * d // 2 + f * d // g)
+        dn = d * f // 2 + d * f // g
     gateup = U * gu + T * d * 2 + S * f * 2          # weights, x rows, h (bf16) out
     down = U * dn + S * f * 2 + S * d * 4            # weights, h in, y (f32) out
     return gateup, down
@@ -183,6 +184,12 @@ def main():
     run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path)
     outs = run.outputs(T)
     used_path = "decode" if moe.moe_plan_path(run.plan, T) == moe.MOE_PATH_DECODE else "grouped"
+    # expert-stage arithmetic (the router is f32 throughout): bf16 products
+    # into f32, by MFMA except in the decode matvec, which the plan picks for
+    # one token (or always, under MOE_DEC_KERNEL=0)
+    mfma = used_path == "grouped" or (os.environ.get("MOE_DEC_KERNEL", "1") != "0"
+                                      and T >= int(os.environ.get("MOE_DEC_MFMA_MIN_T", "2")))
+    dtype = "bf16-mfma/f32-acc" if mfma else "bf16-dot2/f32-acc"
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -281,15 +288,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if used_path == "decode" else "bf16-mfma/f32-acc",
+        "dtype": dtype,
         "data": "synthetic (seeded; random-init weights quantised to the workload's format)",
         "config": {
             "workload": f"{wl.name}: d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.fmt} "
                         f"renorm={int(wl.renorm)}, T={T} tokens per step",
             "tokens_per_step": T,
             "path": used_path,
-            "weights": "e4m3 + f32 128x128 block scales" if wl.fmt == "e4m3"
-                       else "e2m1 + ue8m0 per 32",
+            "weights": {"e4m3": "e4m3 + f32 128x128 block scales",
+                        "e2m1": "e2m1 + ue8m0 per 32",
+                        "nvfp4": "e2m1 + e4m3 per 16 (nvfp4)"}[wl.fmt],
             "activations": "bf16",
             "distinct_experts_per_step": U,
             "weight_copies_rotated": copies,

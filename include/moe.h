@@ -62,7 +62,12 @@ typedef enum {
   /* OCP E2M1 codes, two per byte, element 2i in the low nibble; one UE8M0
    * byte (scale 2^(b-127)) per 32 contiguous inputs of a row.
    * Requires d_model % 32 == 0 and d_ff % 32 == 0. */
-  MOE_W_E2M1_UE8M0_G32 = 1
+  MOE_W_E2M1_UE8M0_G32 = 1,
+  /* NVFP4: OCP E2M1 codes packed as above; one OCP E4M3FN scale byte per 16
+   * contiguous inputs of a row (the value is code times scale; no second,
+   * per-tensor scale).  Qwen-Flash-Next post, the NVFP4 expert weights.
+   * Requires d_model % 32 == 0 and d_ff % 32 == 0. */
+  MOE_W_E2M1_E4M3_G16 = 2
 } moe_wfmt;
 
 /* Which variant of the one GPU path runs the expert stage. */
@@ -89,10 +94,12 @@ typedef struct moe_plan_s* moe_plan_t;
  * down: N = d_model, K = d_ff).  Rows are K-contiguous.
  *   e4m3: q is uint8 [E][N][K]; scale is f32 [E][N/128][K/128].
  *   e2m1: q is uint8 [E][N][K/2]; scale is uint8 [E][N][K/32].
+ *   nvfp4: q is uint8 [E][N][K/2]; scale is uint8 (e4m3 codes) [E][N][K/16].
  * q_expert_stride / s_expert_stride: bytes from expert e to expert e+1, so
  * both one buffer per matrix and one block per expert can be described.
  * Alignment: q and q_expert_stride 16 bytes; e4m3 scale and s_expert_stride
- * 4 bytes; e2m1 scales 1 byte. */
+ * 4 bytes; nvfp4 scale and s_expert_stride 2 bytes (a 32-input step reads
+ * its two group scales as one 16-bit word); e2m1 scales 1 byte. */
 typedef struct {
   const void* q;
   const void* scale;

@@ -17,10 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_NULL_ARG, MOE_ERR_BAD_SHAPE, MOE_ERR_UNSUPPORTED = 0, 1, 2, 3
 MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
-MOE_W_E4M3_B128, MOE_W_E2M1_UE8M0_G32 = 0, 1
+MOE_W_E4M3_B128, MOE_W_E2M1_UE8M0_G32, MOE_W_E2M1_E4M3_G16 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
 STAGES = ("router", "topk", "permute", "gateup", "down", "combine")
-WFMT = {"e4m3": MOE_W_E4M3_B128, "e2m1": MOE_W_E2M1_UE8M0_G32}
+WFMT = {"e4m3": MOE_W_E4M3_B128, "e2m1": MOE_W_E2M1_UE8M0_G32, "nvfp4": MOE_W_E2M1_E4M3_G16}
 
 
 class moe_desc(ctypes.Structure):

@@ -428,6 +428,8 @@ moe_status check_mat(const moe_plan_s* p, const moe_mat* m) {
   if (!aligned(m->q, 16) || m->q_expert_stride % 16) return MOE_ERR_ALIGNMENT;
   if (p->d.wfmt == MOE_W_E4M3_B128 && (!aligned(m->scale, 4) || m->s_expert_stride % 4))
     return MOE_ERR_ALIGNMENT;
+  if (p->d.wfmt == MOE_W_E2M1_E4M3_G16 && (!aligned(m->scale, 2) || m->s_expert_stride % 2))
+    return MOE_ERR_ALIGNMENT;
   return MOE_OK;
 }
 
@@ -462,7 +464,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (d.wfmt == MOE_W_E4M3_B128) {
     if (d.d_model % 128 || d.d_ff % 128) return MOE_ERR_UNSUPPORTED;
     if (d.d_model > 128 * MAX_KBLK || d.d_ff > 128 * MAX_KBLK) return MOE_ERR_UNSUPPORTED;
-  } else if (d.wfmt == MOE_W_E2M1_UE8M0_G32) {
+  } else if (d.wfmt == MOE_W_E2M1_UE8M0_G32 || d.wfmt == MOE_W_E2M1_E4M3_G16) {
     if (d.d_model % 32 || d.d_ff % 32) return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_UNSUPPORTED;
@@ -490,7 +492,8 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   // while the slots per expert stay small; measured crossovers against the
   // grouped GEMM: T*k about 12*E for e4m3 (OLMoE shape between T = 64 and 128,
   // the d = 7168 layer between 256 and 512); e2m1 decode was faster at every
-  // size measured, up to T*k = 16*E.
+  // size measured, up to T*k = 16*E (NVFP4: the same fp4 codes, so the same
+  // crossover).
   p->t_decode = std::max(1, (d.wfmt == MOE_W_E4M3_B128 ? 12 : 16) * d.n_experts / d.top_k);
   // tuning knobs of the decode matvec
   if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
@@ -500,7 +503,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
   if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
-  // register-weight tiles measured faster for e4m3; for e2m1 at its grouped
+  // register-weight tiles measured faster for e4m3; for fp4 at its grouped
   // sizes (tens of slots per expert) the 64-token tile is mostly empty
   p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 1 : 0;
   if (const char* v = std::getenv("MOE_GEMM")) p->gemm_kernel = std::max(0, std::min(2, std::atoi(v)));
@@ -511,7 +514,8 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
                 "decode matvec (row groups per wave %d, 0=auto); grouped MFMA 32x32x16 bf16, "
                 "BM 32/64/128 by slots per expert, BK 64 double-buffered",
                 dev, p->arch.c_str(), p->cus, d.d_model, d.d_ff, d.n_experts, d.top_k,
-                d.wfmt == MOE_W_E4M3_B128 ? "e4m3/128x128" : "e2m1/ue8m0x32", d.renorm,
+                d.wfmt == MOE_W_E4M3_B128 ? "e4m3/128x128"
+                : d.wfmt == MOE_W_E2M1_UE8M0_G32 ? "e2m1/ue8m0x32" : "e2m1/e4m3x16", d.renorm,
                 d.path == MOE_PATH_AUTO ? "auto" : (d.path == MOE_PATH_DECODE ? "decode" : "grouped"),
                 p->t_decode, GEMV_MAX_T, p->dec_nrg);
   p->info = buf;
@@ -725,9 +729,9 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                up->q_expert_stride, up->s_expert_stride};
   const DMat D{static_cast<const uint8_t*>(down->q), static_cast<const uint8_t*>(down->scale),
                down->q_expert_stride, down->s_expert_stride};
-  st = p->d.wfmt == MOE_W_E4M3_B128
-           ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, s)
-           : launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, s);
+  st = p->d.wfmt == MOE_W_E4M3_B128       ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, s)
+       : p->d.wfmt == MOE_W_E2M1_UE8M0_G32 ? launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, s)
+                                           : launch_expert_stage<FMT_NVFP4>(p, T, x, G, U, D, L, ws, s);
   if (st != MOE_OK) return st;
 
   // a6: fixed-order combine

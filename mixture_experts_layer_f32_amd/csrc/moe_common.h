@@ -59,6 +59,24 @@ __device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
 }
 
+// One OCP e4m3 code (low byte of b) -> its exact f32 value.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(b, false)[0];
+}
+
+// Two e2m1 codes (byte `sel` of w, low nibble first) times an e4m3 scale
+// value -> bf16x2, exact.  The scaled conversion above applies only the
+// exponent of its scale operand, so a non-power-of-two scale is applied here:
+// decode at scale 1, multiply in f32 (e2m1 has at most 2 significant bits and
+// e4m3 at most 4, so the product is exact and has at most 6), and keep the top
+// 16 bits of each product, which for such a value is the bf16 value itself.
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2_times_to_bf16(uint32_t w, float scale) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  const uint32_t a = __float_as_uint(v.x * scale), b = __float_as_uint(v.y * scale);
+  return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(b, a, 0x07060302u));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));

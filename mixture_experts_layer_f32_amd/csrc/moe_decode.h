@@ -11,7 +11,9 @@
 
 namespace moe {
 
-enum : int { FMT_E4M3 = 0, FMT_E2M1 = 1 };
+// Weight formats: e4m3 + f32 scale per 128x128 block; e2m1 + UE8M0 scale per
+// 32 inputs of a row; NVFP4 = e2m1 + e4m3 scale per 16 inputs of a row.
+enum : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_NVFP4 = 2 };
 
 // One expert matrix family on the device: byte pointers and expert strides.
 struct DMat {
@@ -24,7 +26,7 @@ struct DMat {
 // A "chunk" is 16 consecutive inputs of one weight row: 16 bytes of e4m3
 // codes or 8 bytes of e2m1 codes.  A chunk is decoded once into 8 exact bf16
 // pairs (e4m3 values are bf16 values; an e2m1 value times its power-of-two
-// scale is a bf16 value) and dotted with each token's 16 bf16 activations by
+// UE8M0 scale or its e4m3 scale is a bf16 value) and dotted with each token's 16 bf16 activations by
 // v_dot2_f32_bf16, whose products are exact in f32.
 template <int FMT>
 struct Chunk;
@@ -70,6 +72,29 @@ struct Chunk<FMT_E2M1> {
     o[5] = e2m1x2_to_bf16<1>(w.y, sc);
     o[6] = e2m1x2_to_bf16<2>(w.y, sc);
     o[7] = e2m1x2_to_bf16<3>(w.y, sc);
+  }
+};
+
+template <>
+struct Chunk<FMT_NVFP4> {
+  typedef u32x2 raw;
+  static constexpr bool kPostScale = false;  // scale applied exactly in the decode
+  static __device__ __forceinline__ raw load(const uint8_t* row, int c) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row) + c);
+  }
+  // e4m3 scale byte of the 16-input group that is chunk c of row n
+  static __device__ __forceinline__ float scale(const uint8_t* s, int n, int c, int K) {
+    return e4m3_to_f32(s[(size_t)n * (K >> 4) + c]);
+  }
+  static __device__ __forceinline__ void decode(raw w, float sc, bf16x2 (&o)[8]) {
+    o[0] = e2m1x2_times_to_bf16<0>(w.x, sc);
+    o[1] = e2m1x2_times_to_bf16<1>(w.x, sc);
+    o[2] = e2m1x2_times_to_bf16<2>(w.x, sc);
+    o[3] = e2m1x2_times_to_bf16<3>(w.x, sc);
+    o[4] = e2m1x2_times_to_bf16<0>(w.y, sc);
+    o[5] = e2m1x2_times_to_bf16<1>(w.y, sc);
+    o[6] = e2m1x2_times_to_bf16<2>(w.y, sc);
+    o[7] = e2m1x2_times_to_bf16<3>(w.y, sc);
   }
 };
 
@@ -430,6 +455,11 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w, float sc) {
   return pack_bf16x8(e2m1x2_to_bf16<0>(w, sc), e2m1x2_to_bf16<1>(w, sc),
                      e2m1x2_to_bf16<2>(w, sc), e2m1x2_to_bf16<3>(w, sc));
 }
+// 8 e2m1 codes (one word) times an e4m3 scale value -> 8 bf16, exact
+__device__ __forceinline__ bf16x8 nvfp4x8_to_bf16(uint32_t w, float sc) {
+  return pack_bf16x8(e2m1x2_times_to_bf16<0>(w, sc), e2m1x2_times_to_bf16<1>(w, sc),
+                     e2m1x2_times_to_bf16<2>(w, sc), e2m1x2_times_to_bf16<3>(w, sc));
+}
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -442,6 +472,8 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 template <int FMT> struct DecUnitW;
 template <> struct DecUnitW<FMT_E4M3> { u32x4 w[2]; };
 template <> struct DecUnitW<FMT_E2M1> { u32x4 w[2]; uint32_t sb[2]; };
+// NVFP4: sb[h] holds the two e4m3 scale bytes of the load's two 16-input groups
+template <> struct DecUnitW<FMT_NVFP4> { u32x4 w[2]; uint32_t sb[2]; };
 template <int FMT> constexpr int dec_unit_k() { return FMT == FMT_E4M3 ? 128 : 256; }
 template <int FMT> constexpr int dec_unit_x() { return FMT == FMT_E4M3 ? 4 : 8; }
 
@@ -470,7 +502,8 @@ __global__ __launch_bounds__(256) void dec_mfma(
   const int nu = (nkb - w + KS - 1) / KS;  // units per tile for this wavefront (>= 1)
   const int units = my_tiles * nu;
   const uint32_t rb = FMT == FMT_E4M3 ? (uint32_t)K : (uint32_t)K / 2;
-  const uint32_t q_bytes = (uint32_t)N * rb, s_bytes = (uint32_t)N * (uint32_t)(K >> 5);
+  const uint32_t sgroups = FMT == FMT_NVFP4 ? (uint32_t)(K >> 4) : (uint32_t)(K >> 5);
+  const uint32_t q_bytes = (uint32_t)N * rb, s_bytes = (uint32_t)N * sgroups;
   const __amdgpu_buffer_rsrc_t ar = buf_rsrc(act, act_bytes);
   const DMat M[2] = {A, B};
 
@@ -509,8 +542,12 @@ __global__ __launch_bounds__(256) void dec_mfma(
             const int k = k0 + 128 * h + 32 * q;
             const bool in = n < N && k < K;
             s.wv[m][t].w[h] = buf_load16(wr, in ? (uint32_t)n * rb + k / 2 : BUF_OOB, 0);
-            s.wv[m][t].sb[h] = __builtin_amdgcn_raw_buffer_load_b8(
-                sr, in ? (uint32_t)n * (K >> 5) + (k >> 5) : BUF_OOB, 0, 0);
+            if constexpr (FMT == FMT_NVFP4)  // the two adjacent group scales (2-byte aligned)
+              s.wv[m][t].sb[h] = __builtin_amdgcn_raw_buffer_load_b16(
+                  sr, in ? (uint32_t)n * sgroups + (k >> 4) : BUF_OOB, 0, 0);
+            else
+              s.wv[m][t].sb[h] = __builtin_amdgcn_raw_buffer_load_b8(
+                  sr, in ? (uint32_t)n * sgroups + (k >> 5) : BUF_OOB, 0, 0);
           }
         }
         s.sc[m] = 0.0f;
@@ -568,12 +605,25 @@ __global__ __launch_bounds__(256) void dec_mfma(
         } else {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const float sc = ue8m0_to_f32(wq.sb[h]);
             const u32x4 v = wq.w[h];
-            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.x, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 0]), acc[m][t]);
-            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.y, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 1]), acc[m][t]);
-            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.z, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 2]), acc[m][t]);
-            acc[m][t] = mfma16x16x32(e2m1x8_to_bf16(v.w, sc), __builtin_bit_cast(bf16x8, s.x[4 * h + 3]), acc[m][t]);
+            bf16x8 a0, a1, a2, a3;
+            if constexpr (FMT == FMT_NVFP4) {  // words x, y: first 16-input group; z, w: second
+              const float s0 = e4m3_to_f32(wq.sb[h] & 0xFF), s1 = e4m3_to_f32(wq.sb[h] >> 8);
+              a0 = nvfp4x8_to_bf16(v.x, s0);
+              a1 = nvfp4x8_to_bf16(v.y, s0);
+              a2 = nvfp4x8_to_bf16(v.z, s1);
+              a3 = nvfp4x8_to_bf16(v.w, s1);
+            } else {
+              const float sc = ue8m0_to_f32(wq.sb[h]);
+              a0 = e2m1x8_to_bf16(v.x, sc);
+              a1 = e2m1x8_to_bf16(v.y, sc);
+              a2 = e2m1x8_to_bf16(v.z, sc);
+              a3 = e2m1x8_to_bf16(v.w, sc);
+            }
+            acc[m][t] = mfma16x16x32(a0, __builtin_bit_cast(bf16x8, s.x[4 * h + 0]), acc[m][t]);
+            acc[m][t] = mfma16x16x32(a1, __builtin_bit_cast(bf16x8, s.x[4 * h + 1]), acc[m][t]);
+            acc[m][t] = mfma16x16x32(a2, __builtin_bit_cast(bf16x8, s.x[4 * h + 2]), acc[m][t]);
+            acc[m][t] = mfma16x16x32(a3, __builtin_bit_cast(bf16x8, s.x[4 * h + 3]), acc[m][t]);
           }
         }
       }

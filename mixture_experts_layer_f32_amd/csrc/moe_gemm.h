@@ -9,6 +9,8 @@
 //         inner loop).
 //   e2m1: the power-of-two scale is applied exactly inside the fp4 -> bf16
 //         conversion, so MFMA accumulates straight into the running sum.
+//   NVFP4: each 16-input group's e4m3 scale multiplies the decoded values in
+//         f32 (exact), so MFMA again accumulates straight into the sum.
 // The A rows of the gate/up GEMM are the tokens' own activation rows, read
 // through the permutation and never copied (Trochilus README, "How it keeps
 // up": gate and up read a token's row through a map instead of gathered
@@ -123,7 +125,10 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
     const int n = n0 + r;
     const bool ok = q < C::B_TOTAL && n < N;
     bq[i] = ok ? W.q + e * W.qs + n * rbytes + c * 16 : nullptr;
-    bsr[i] = ok ? W.s + e * W.ss + (size_t)n * (K / 32) + c : nullptr;  // e2m1 group of the chunk
+    // scale byte(s) of the chunk: one UE8M0 group (e2m1) or two e4m3 groups (NVFP4)
+    bsr[i] = !ok ? nullptr
+             : FMT == FMT_NVFP4 ? W.s + e * W.ss + (size_t)n * (K / 16) + 2 * c
+                                : W.s + e * W.ss + (size_t)n * (K / 32) + c;
     bdst[i] = q < C::B_TOTAL ? C::A_ELEMS + (m * BNM + r) * LDK + c * C::B_EPC : -1;
   }
 
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
 
   // PF register sets of global loads in flight
   u32x4 ra[PF][C::A_CHUNKS], rb[PF][C::B_CHUNKS];
-  float rsc[PF][C::B_CHUNKS];
+  float rsc[PF][C::B_CHUNKS][2];
   auto gload = [&](int set, int k0) {
 #pragma unroll
     for (int i = 0; i < C::A_CHUNKS; ++i) {
@@ -154,14 +159,20 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
 #pragma unroll
     for (int i = 0; i < C::B_CHUNKS; ++i) {
       rb[set][i] = u32x4{0u, 0u, 0u, 0u};
-      rsc[set][i] = 1.0f;
+      rsc[set][i][0] = rsc[set][i][1] = 1.0f;
       const int c = (tid + 256 * i) % C::B_CPR;
       if (bq[i] != nullptr && k0 + c * C::B_EPC < K) {
         const int64_t off = FMT == FMT_E4M3 ? k0 : k0 / 2;
         // a stage reads 64 (e4m3) or 32 (e2m1) bytes of a 128-byte row segment;
         // ordinary loads keep the line in L2 for the next stage's part
         rb[set][i] = *reinterpret_cast<const u32x4*>(bq[i] + off);
-        if (FMT == FMT_E2M1) rsc[set][i] = ue8m0_to_f32(bsr[i][k0 / 32]);
+        if constexpr (FMT == FMT_E2M1) {
+          rsc[set][i][0] = ue8m0_to_f32(bsr[i][k0 / 32]);
+        } else if constexpr (FMT == FMT_NVFP4) {
+          const uint32_t sb = *reinterpret_cast<const uint16_t*>(bsr[i] + k0 / 16);
+          rsc[set][i][0] = e4m3_to_f32(sb & 0xFF);
+          rsc[set][i][1] = e4m3_to_f32(sb >> 8);
+        }
       }
     }
   };
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
       if (bdst[i] < 0) continue;
       const uint32_t w[4] = {rb[set][i].x, rb[set][i].y, rb[set][i].z, rb[set][i].w};
       u32x4* dst = reinterpret_cast<u32x4*>(st + bdst[i]);
-      if (FMT == FMT_E4M3) {
+      if constexpr (FMT == FMT_E4M3) {
         bf16x2 o[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -186,8 +197,19 @@ __global__ __launch_bounds__(256, 2) void gemm_expert(
         }
         dst[0] = pack4(o[0], o[1], o[2], o[3]);
         dst[1] = pack4(o[4], o[5], o[6], o[7]);
+      } else if constexpr (FMT == FMT_NVFP4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // words 0-1: first 16-input group, 2-3: second
+          const float sc = rsc[set][i][j >> 1];
+          bf16x2 o[4];
+          o[0] = e2m1x2_times_to_bf16<0>(w[j], sc);
+          o[1] = e2m1x2_times_to_bf16<1>(w[j], sc);
+          o[2] = e2m1x2_times_to_bf16<2>(w[j], sc);
+          o[3] = e2m1x2_times_to_bf16<3>(w[j], sc);
+          dst[j] = pack4(o[0], o[1], o[2], o[3]);
+        }
       } else {
-        const float sc = rsc[set][i];
+        const float sc = rsc[set][i][0];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           bf16x2 o[4];
@@ -299,7 +321,8 @@ namespace moe {
 // h = l / 32), B = weight rows (lane l: row l % 32, k-slot h).  A 64-input
 // stage from k0: lane (r, h) loads the 32 weight inputs k0 + 32h .. k0 + 32h
 // + 31 of its row (e4m3: 32 bytes; e2m1: 16 bytes and the row's ue8m0 byte
-// of that 32-input group); MFMA step s = 0..3 takes inputs k0 + 32h + 8s ..
+// of that 32-input group; NVFP4: 16 bytes and the two e4m3 bytes of its
+// 16-input groups); MFMA step s = 0..3 takes inputs k0 + 32h + 8s ..
 // + 7 from both operands.
 template <int FMT, bool GATEUP, int TNW>
 struct RWCfg {
@@ -314,6 +337,7 @@ struct RWCfg {
 template <int FMT> struct RWRaw;
 template <> struct RWRaw<FMT_E4M3> { u32x4 w[2]; };
 template <> struct RWRaw<FMT_E2M1> { u32x4 w; float sc; };
+template <> struct RWRaw<FMT_NVFP4> { u32x4 w; float sc[2]; };
 
 // GATEUP: act = x [T][K], out = h bf16 [S][N] (N = f, K = d); else act = h
 // [S][K], out = y f32 [S][N] (N = d, K = f).  Block order as gemm_expert.
@@ -361,7 +385,8 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
       const DMat& W = m == 0 ? W0 : W1;
       const int n = nw0 + 32 * j + r32;
       wrow[m * TNW + j] = n < N ? W.q + e * W.qs + n * rbytes : nullptr;
-      srow[m * TNW + j] = n < N ? W.s + e * W.ss + (int64_t)n * (K >> 5) : nullptr;
+      srow[m * TNW + j] = n < N ? W.s + e * W.ss + (int64_t)n * (FMT == FMT_NVFP4 ? K >> 4 : K >> 5)
+                                : nullptr;
     }
   const float* sblk[NMAT];
 #pragma unroll
@@ -384,6 +409,11 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
       if constexpr (FMT == FMT_E4M3) {
         rw[t].w[0] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k) : u32x4{0u, 0u, 0u, 0u};
         rw[t].w[1] = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k + 16) : u32x4{0u, 0u, 0u, 0u};
+      } else if constexpr (FMT == FMT_NVFP4) {
+        rw[t].w = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k / 2) : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t sb = ok ? *reinterpret_cast<const uint16_t*>(srow[t] + (k >> 4)) : 0u;
+        rw[t].sc[0] = e4m3_to_f32(sb & 0xFF);
+        rw[t].sc[1] = e4m3_to_f32(sb >> 8);
       } else {
         rw[t].w = ok ? *reinterpret_cast<const u32x4*>(wrow[t] + k / 2) : u32x4{0u, 0u, 0u, 0u};
         rw[t].sc = ok ? ue8m0_to_f32(srow[t][k >> 5]) : 1.0f;
@@ -435,6 +465,9 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
         if constexpr (FMT == FMT_E4M3) {
           const u32x4 v = cur[t].w[s >> 1];
           b = (s & 1) ? e4m3x8_to_bf16(v.z, v.w) : e4m3x8_to_bf16(v.x, v.y);
+        } else if constexpr (FMT == FMT_NVFP4) {
+          const u32x4 v = cur[t].w;
+          b = nvfp4x8_to_bf16(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, cur[t].sc[s >> 1]);
         } else {
           const u32x4 v = cur[t].w;
           b = e2m1x8_to_bf16(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w, cur[t].sc);
@@ -530,7 +563,7 @@ struct DmaCfg {
   static constexpr int WLD = FMT == FMT_E4M3 ? 2 : 1;          // 16-byte weight loads per tile and stage
   static constexpr int A_V4 = BM * 8;                           // u32x4 per activation stage (8 KB)
   static constexpr int W_V4 = 4 * NW * WLD * 64;                // u32x4 per weight stage
-  static constexpr int LOADS = 2 + NW * WLD + (FMT == FMT_E2M1 ? NW : 0);  // vector loads per wavefront and stage
+  static constexpr int LOADS = 2 + NW * WLD + (FMT != FMT_E4M3 ? NW : 0);  // vector loads per wavefront and stage
 };
 
 // The direct-to-LDS loads and the stage barrier are issued as inline
@@ -598,7 +631,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
       const DMat& W = m == 0 ? W0 : W1;
       const int n = min(nw0 + 32 * j + r32, N - 1);
       wrow[m * TNW + j] = W.q + e * W.qs + n * rbytes;
-      srow[m * TNW + j] = W.s + e * W.ss + (int64_t)n * (K >> 5);
+      srow[m * TNW + j] = W.s + e * W.ss + (int64_t)n * (FMT == FMT_NVFP4 ? K >> 4 : K >> 5);
     }
   // e4m3: the scale row of this wavefront's 128-row block, k-block kb held by
   // lane kb % 64 of register kb / 64 (loaded before the pipeline starts)
@@ -616,9 +649,9 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
 
   const int nk = (K + BK - 1) / BK;
   // stage kk's loads into one pipeline slot (stages past the end repeat the
-  // last one so every stage issues the same loads); e2m1: the lanes' ue8m0
-  // scale bytes go to registers
-  auto issue = [&](int kk, const u32x4* sA, const u32x4* sW, float (&scs)[NW]) {
+  // last one so every stage issues the same loads); e2m1 and NVFP4: the
+  // lanes' scale bytes (one UE8M0 or two e4m3) go to registers
+  auto issue = [&](int kk, const u32x4* sA, const u32x4* sW, float (&scs)[NW][2]) {
     const int k0 = min(kk, nk - 1) * BK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -633,7 +666,13 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
         lds_dma16(wrow[t] + kl + 16, sW + ((w * NW + t) * 2 + 1) * 64);
       } else {
         lds_dma16(wrow[t] + kl / 2, sW + (w * NW + t) * 64);
-        scs[t] = ue8m0_to_f32(srow[t][kl >> 5]);
+        if constexpr (FMT == FMT_NVFP4) {
+          const uint32_t sb = *reinterpret_cast<const uint16_t*>(srow[t] + (kl >> 4));
+          scs[t][0] = e4m3_to_f32(sb & 0xFF);
+          scs[t][1] = e4m3_to_f32(sb >> 8);
+        } else {
+          scs[t][0] = ue8m0_to_f32(srow[t][kl >> 5]);
+        }
       }
     }
   };
@@ -651,7 +690,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
       for (int t = 0; t < NW; ++t) part[i][t] = zero;
   }
 
-  auto compute = [&](int ks, const u32x4* sA, const u32x4* sW, const float (&scs)[NW]) {
+  auto compute = [&](int ks, const u32x4* sA, const u32x4* sW, const float (&scs)[NW][2]) {
     const bool first = (ks & 1) == 0;
     const bool ktail = ks * BK + 32 * h >= K;  // e2m1: this lane's inputs past K
 #pragma unroll
@@ -671,7 +710,10 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
         } else {
           const u32x4 v = sW[(w * NW + t) * 64 + lane];
           const uint32_t word = ktail ? 0u : (s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w);
-          b = e2m1x8_to_bf16(word, scs[t]);
+          if constexpr (FMT == FMT_NVFP4)
+            b = nvfp4x8_to_bf16(word, scs[t][s >> 1]);
+          else
+            b = e2m1x8_to_bf16(word, scs[t][0]);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -703,7 +745,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
   // three slots, two stages in flight: at stage ks wait for its loads, one
   // barrier (activations visible; slot of stage ks - 1 free), issue stage ks + 2
   // into that slot, compute stage ks
-  float sc0[NW], sc1[NW], sc2[NW];
+  float sc0[NW][2], sc1[NW][2], sc2[NW][2];
   constexpr int LD = C::LOADS;
   issue(0, sA0, sW0, sc0);
   issue(1, sA1, sW1, sc1);

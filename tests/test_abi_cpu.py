@@ -38,6 +38,7 @@ def test_status_strings():
     (dict(path=5), 2), (dict(n_experts=2048, top_k=2), 3), (dict(top_k=17, n_experts=64), 3),
     (dict(d_model=200), 3), (dict(d_ff=96), 3), (dict(wfmt=7), 3),
     (dict(wfmt=1, d_model=48), 3), (dict(wfmt=1, d_ff=80), 3),
+    (dict(wfmt=2, d_model=48), 3), (dict(wfmt=2, d_ff=80), 3), (dict(wfmt=3), 3),
 ])
 def test_descriptor_validation_before_device(fields, status):
     import mixture_experts_layer_f32_amd as m

@@ -12,6 +12,7 @@ pytestmark = pytest.mark.gpu
 
 WL = synth.Workload("edge-e4m3", 256, 384, 6, 2, "e4m3", True, (9,), False, 4001)
 WL4 = synth.Workload("edge-e2m1", 128, 96, 8, 3, "e2m1", False, (9,), False, 4002)
+WLN = synth.Workload("edge-nvfp4", 128, 96, 8, 3, "nvfp4", False, (9,), False, 4003)
 _cache = {}
 
 
@@ -68,7 +69,7 @@ def test_argument_errors_launch_nothing():
     assert m.moe_workspace_size(run.plan, 0) == 0
 
 
-@pytest.mark.parametrize("wl", [WL, WL4], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [WL, WL4, WLN], ids=lambda w: w.name)
 @pytest.mark.parametrize("path", [1, 2])
 def test_all_tokens_on_one_expert(wl, path):
     """A large bias on expert 3 sends every token there: one expert gets all T
@@ -127,7 +128,7 @@ def test_max_tokens_boundary():
     check_out(g["out"], ref.out)
 
 
-@pytest.mark.parametrize("wl", [WL, WL4], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [WL, WL4, WLN], ids=lambda w: w.name)
 def test_one_block_per_expert_layout(wl):
     """Each expert's gate | up | down codes and scales packed in one block,
     described by expert strides: same bits as the one-buffer-per-matrix layout."""
@@ -154,6 +155,28 @@ def test_one_block_per_expert_layout(wl):
                   outs["out"], workspace=run.workspace)
     torch.cuda.synchronize()
     assert np.array_equal(outs["out"].cpu().numpy().view(np.uint32), a["out"].view(np.uint32))
+
+
+def test_nvfp4_scale_alignment():
+    """NVFP4 reads a row's two 16-input group scales as one 16-bit word: an
+    odd scale pointer or expert stride is rejected before any launch."""
+    import torch
+    import mixture_experts_layer_f32_amd as m
+    from mixture_experts_layer_f32_amd.device import to_dev
+    L, W = get(WLN)
+    run = runner(WLN, 4)
+    batch = synth.make_batch(WLN, L, 4)
+    outs = run.outputs(4)
+    outs["out"].fill_(7.0)
+    g, u, d = W.mats()
+    for bad in (m.moe_mat(g.q, g.scale + 1, g.q_expert_stride, g.s_expert_stride),
+                m.moe_mat(g.q, g.scale, g.q_expert_stride, g.s_expert_stride + 1)):
+        with pytest.raises(m.MoeError) as e:
+            m.moe_forward(run.plan, 4, to_dev(batch.x), W.w_router, None, bad, u, d, outs["out"],
+                          workspace=run.workspace)
+        assert e.value.status == m.MOE_ERR_ALIGNMENT
+    torch.cuda.synchronize()
+    assert torch.all(outs["out"] == 7.0)
 
 
 def test_nonfinite_input_row_does_not_fault():

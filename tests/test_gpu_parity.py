@@ -20,6 +20,8 @@ SMALL = {
     "e4m3-ragged": synth.Workload("e4m3-ragged", 256, 384, 6, 2, "e4m3", False, (37,), False, 3001),
     # f = 96 and d = 160: N and K tails against the 64-wide fp4 tiles
     "e2m1-ragged": synth.Workload("e2m1-ragged", 160, 96, 8, 3, "e2m1", True, (5, 70), False, 3002),
+    # NVFP4 (e4m3 scale per 16 inputs) on the same tails
+    "nvfp4-ragged": synth.Workload("nvfp4-ragged", 160, 96, 8, 3, "nvfp4", True, (5, 70), False, 3003),
 }
 
 
@@ -43,7 +45,8 @@ def small(name):
 
 @pytest.mark.parametrize("path", [AUTO, DECODE, GROUPED])
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("e4m3-ragged", 37), ("e4m3-ragged", 1),
-                                    ("e2m1-ragged", 5), ("e2m1-ragged", 70)])
+                                    ("e2m1-ragged", 5), ("e2m1-ragged", 70),
+                                    ("nvfp4-ragged", 1), ("nvfp4-ragged", 5), ("nvfp4-ragged", 70)])
 def test_small_parity(name, T, path):
     wl, layer, W = small(name)
     batch = synth.make_batch(wl, layer, T)

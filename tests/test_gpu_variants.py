@@ -2,7 +2,7 @@
 pick for these shapes but that a plan can be switched to (MOE_GEMM for the
 grouped path, MOE_DEC_KERNEL / MOE_DEC_MFMA_MIN_T for the decode path): each
 one against the CPU oracle with the same bars as the default path.  The
-shapes carry the tails the kernels guard: K = 160 (an e2m1 k-tail of 32
+shapes carry the tails the kernels guard: K = 160 (an fp4 k-tail of 32
 inputs against 64-input stages), N = 96 and 384 (partial 128- and 256-row
 column blocks), 37 and 70 tokens (partial 64-token tiles), and one expert
 holding every slot (several 64-token tiles of one expert)."""
@@ -21,6 +21,7 @@ DECODE, GROUPED = 1, 2
 WLS = {
     "e4m3": synth.Workload("var-e4m3", 256, 384, 6, 2, "e4m3", False, (37,), False, 5001),
     "e2m1": synth.Workload("var-e2m1", 160, 96, 8, 3, "e2m1", True, (70,), False, 5002),
+    "nvfp4": synth.Workload("var-nvfp4", 160, 96, 8, 3, "nvfp4", True, (70,), False, 5003),
 }
 _cache = {}
 
@@ -55,7 +56,7 @@ def check_all(g, ref):
     check_out(g["out"], ref.out)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
 @pytest.mark.parametrize("gemm", ["0", "1", "2"])
 def test_grouped_kernels(fmt, gemm):
     wl, layer, W = get(fmt)
@@ -65,7 +66,7 @@ def test_grouped_kernels(fmt, gemm):
     check_all(run_with_env({"MOE_GEMM": gemm}, wl, W, batch, GROUPED), ref)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
 @pytest.mark.parametrize("gemm", ["0", "1", "2"])
 def test_grouped_kernels_one_expert_many_tiles(fmt, gemm):
     """A large bias on expert 1 sends all 150 tokens there: that expert spans
@@ -81,7 +82,7 @@ def test_grouped_kernels_one_expert_many_tiles(fmt, gemm):
     check_all(run_with_env({"MOE_GEMM": gemm}, wl, W, batch, GROUPED), ref)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
 @pytest.mark.parametrize("T", [2, 37])
 def test_decode_matvec_kernel(fmt, T):
     """The wavefront matvec (default only for one token) on several tokens."""
@@ -91,7 +92,7 @@ def test_decode_matvec_kernel(fmt, T):
     check_all(run_with_env({"MOE_DEC_KERNEL": "0"}, wl, W, batch, DECODE), ref)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
 def test_decode_mfma_one_token(fmt):
     """The MFMA decode tiles (default from two tokens) on a single token."""
     wl, layer, W = get(fmt)
