@@ -33,10 +33,10 @@ layer's code, so each step states the plainest reading):
               everything": FP4 experts with scales; UE8M0 = a biased power-of-
               two exponent byte; element 2i in the low nibble, reading R11).
         nvfp4: W[n,c] = dec_e2m1(nibble(n,c)) * dec_e4m3(S[n, c//16])
-              (dev.to page, Qwen-Flash-Next NVFP4 post: experts of three
-              2560x640 matrices "in NVFP4 with scales", 2,764,800 bytes per
-              expert block = codes + one e4m3 scale byte per 16 codes, reading
-              R18; no second-level per-tensor scale is on the page, reading R19).
+              (dev.to page, post "Running a 133 GB MoE model on an 8 GB GPU
+              at 11 tokens/s", "The engine", item 4: expert weights in NVFP4;
+              one e4m3 scale byte per 16 codes, reading R18; no second-level
+              per-tensor scale is on the page, reading R19).
   O8  Per slot s routed to expert e: g = W_gate x, u = W_up x,
       h = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g))  (SwiGLU experts:
       Trochilus README "How it keeps up" and the dev.to NVFP4 post "The

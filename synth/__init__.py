@@ -197,9 +197,9 @@ WORKLOADS = {
     "large-e4m3": Workload("large-e4m3", 7168, 2048, 256, 8, "e4m3", True, (1, 64, 4096), False,
                            1003),
     "fp4-e2m1": Workload("fp4-e2m1", 4096, 2880, 384, 6, "e2m1", True, (1, 16, 1024), False, 1004),
-    # NVFP4 experts of the Qwen-Flash-Next post: three 2560x640 matrices, top-10 of 512
-    "nvfp4-qwen": Workload("nvfp4-qwen", 2560, 640, 512, 10, "nvfp4", True, (1, 16, 256), False,
-                           1005),
+    # the FP4 layer's shape with NVFP4 weights (e4m3 scale per 16 inputs)
+    "fp4-nvfp4": Workload("fp4-nvfp4", 4096, 2880, 384, 6, "nvfp4", True, (1, 16, 1024), False,
+                          1005),
 }
 
 

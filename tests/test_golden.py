@@ -38,21 +38,6 @@ def test_generated_fp4_layout_sizes():
     assert per_expert == 18_800_640
 
 
-def test_nvfp4_block_bytes_fact():
-    """Recorded for the NVFP4 variant: e2m1 codes with one fp8 scale per 16 inputs
-    give the page's 2,764,800-byte expert block for three 2560x640 matrices."""
-    import synth
-    F = facts()["nvfp4_expert_block_bytes"]
-    n, k = F["shape"]
-    assert 3 * n * k // 2 + 3 * n * k // 16 == F["value"]
-    wl = synth.WORKLOADS["nvfp4-qwen"]
-    assert (wl.d, wl.f) == (n, k) and synth.expert_bytes(wl) == F["value"]
-    # the generated layout of one expert has exactly that many bytes
-    small = synth.Workload("nvfp4-one", n, k, 1, 1, "nvfp4", True, (1,), False, 7)
-    L = synth.make_layer(small)
-    assert sum(m.q.nbytes + m.s.nbytes for m in (L.gate, L.up, L.down)) == F["value"]
-
-
 def test_e4m3_code_count():
     import oracle.moe_oracle as om
     assert om.E4M3.size == facts()["e4m3_code_count"]["value"]

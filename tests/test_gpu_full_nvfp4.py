@@ -1,9 +1,9 @@
-"""Full-size parity, NVFP4 expert layer (the Qwen-Flash-Next post's expert
-shape): d=2560, f=640, 512 experts, top-10 renormalised, e2m1 codes with one
-e4m3 scale per 16 inputs (2.64 MiB per expert), at 1, 16 and 256 tokens.
-Routing (ids, counts, offsets, permutation) is compared bit for bit over
-every token; the outputs of a seeded sample of tokens are compared with the
-oracle, which evaluates those tokens one by one."""
+"""Full-size parity, NVFP4 expert layer: the FP4 layer's shape (d=4096,
+f=2880, 384 experts, top-6 renormalised) with e2m1 codes and one e4m3 scale
+per 16 inputs (19.9 MB per expert), at 1, 16 and 1024 tokens.  Routing (ids,
+counts, offsets, permutation) is compared bit for bit over every token; the
+outputs of a seeded sample of tokens are compared with the oracle, which
+evaluates those tokens one by one."""
 import numpy as np
 import pytest
 
@@ -12,12 +12,12 @@ from gpu_util import check_out, check_routing, device_weights, gpu_run, log, ora
 
 pytestmark = pytest.mark.gpu
 
-WL = synth.WORKLOADS["nvfp4-qwen"]
+WL = synth.WORKLOADS["fp4-nvfp4"]
 
 
 @pytest.fixture(scope="module")
 def layer():
-    log("generating nvfp4-qwen layer (1.4 GB)")
+    log("generating fp4-nvfp4 layer (7.6 GB)")
     L = synth.make_layer(WL)
     log("uploading")
     W = device_weights(L)
@@ -32,12 +32,12 @@ def sample_tokens(T, n=6):
     return sorted({0, T - 1, *rng.choice(T, n - 2, replace=False).tolist()})
 
 
-@pytest.mark.parametrize("T,path", [(1, 0), (16, 0), (256, 0), (16, 2), (256, 2)])
-def test_nvfp4_qwen(layer, T, path):
+@pytest.mark.parametrize("T,path", [(1, 0), (16, 0), (1024, 0), (16, 2), (1024, 2)])
+def test_fp4_nvfp4(layer, T, path):
     L, W = layer
     batch = synth.make_batch(WL, L, T)
     toks = sample_tokens(T)
-    log(f"nvfp4-qwen T={T} path={path}: oracle on tokens {toks}")
+    log(f"fp4-nvfp4 T={T} path={path}: oracle on tokens {toks}")
     ref = oracle_run(WL, L, batch, tokens=toks)
     log("gpu")
     g, run = gpu_run(WL, W, batch, path)
