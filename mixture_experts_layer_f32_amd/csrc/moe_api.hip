@@ -47,6 +47,7 @@ struct moe_plan_s {
   int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
   int dec_tall = -1;      // MFMA decode tiles of 32/64 rows: -1 by shape, 0 never, 1 always
+  int dec_ks = 0;         // MFMA decode wavefronts per workgroup (k-split), 0 = by shape
   int gemm_kernel = 1;    // grouped expert stage: 1 = register-weight tiles (e4m3), 0 = LDS weight tiles
   std::string info;
   std::string last_error;
@@ -102,6 +103,17 @@ bool dec_mfma_fits(const moe_plan_s* p, int T) {
 bool use_dec_mfma(const moe_plan_s* p, int T) {
   if (path_for(p, T) != MOE_PATH_DECODE || p->dec_kernel != 1 || !dec_mfma_fits(p, T)) return false;
   return T >= p->dec_mfma_min_t;
+}
+
+// Wavefronts splitting a decode tile's nkb k-units: all of them up to 4,
+// else 4, 3 or 2, whichever divides nkb (a wavefront with fewer units than
+// its neighbours waits for them at every tile's reduction), else 4.
+int dec_ks(const moe_plan_s* p, int nkb) {
+  if (p->dec_ks > 0) return std::min(p->dec_ks, nkb);
+  if (nkb <= 4) return nkb;
+  for (int ks = 4; ks >= 2; --ks)
+    if (nkb % ks == 0) return ks;
+  return 4;
 }
 
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
@@ -319,8 +331,10 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
     auto run = [&](bool gateup) {
       const int K = gateup ? d : f;
       const int ku = FMT == FMT_E4M3 ? 128 : 256;
-      const int ks = std::min(4, (K + ku - 1) / ku);
+      const int ks = dec_ks(p, (K + ku - 1) / ku);
       const dim3 blk(WAVE * ks);
+      // about 12 (tall: 8) wavefronts per CU whatever the split
+      const int g3 = p->cus * 12 / ks, g2 = p->cus * 8 / ks;
       // e2m1: an input byte holds two weights, so the activation operand
       // outweighs the weights once the tiles' token columns fill; taller tiles
       // then share it over more rows (measured: faster at 16 slots per expert,
@@ -330,14 +344,14 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
       if (p->dec_tall >= 0) tall = p->dec_tall == 1;
       if (gateup) {
         if (tall)
-          dec_mfma<FMT, true, 2, FMT == FMT_E4M3 ? 3 : 2><<<p->cus * 2, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
+          dec_mfma<FMT, true, 2, FMT == FMT_E4M3 ? 3 : 2><<<g2, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
         else
-          dec_mfma<FMT, true, 1, 2><<<p->cus * 3, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
+          dec_mfma<FMT, true, 1, 2><<<g3, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
       } else {
         if (tall)
-          dec_mfma<FMT, false, 4, 2><<<p->cus * 2, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+          dec_mfma<FMT, false, 4, 2><<<g2, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
         else
-          dec_mfma<FMT, false, 2, 2><<<p->cus * 3, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+          dec_mfma<FMT, false, 2, 2><<<g3, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
       }
     };
     mark(p, MOE_STAGE_GATEUP, false, st);
@@ -503,6 +517,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
   if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
+  if (const char* v = std::getenv("MOE_DEC_KS")) p->dec_ks = std::max(0, std::min(4, std::atoi(v)));
   // register-weight tiles measured faster for e4m3; for fp4 at its grouped
   // sizes (tens of slots per expert) the 64-token tile is mostly empty
   p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 1 : 0;

@@ -106,6 +106,18 @@ __device__ __forceinline__ float wave_max(float v) {
                fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
+// Unsigned maximum over the 64 lanes, returned to every lane (uniform).
+__device__ __forceinline__ uint32_t dpp_u32max(uint32_t v, uint32_t o) { return v > o ? v : o; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_u32max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = dpp_u32max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = dpp_u32max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = dpp_u32max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return dpp_u32max(dpp_u32max(a, b), dpp_u32max(c, d));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
 

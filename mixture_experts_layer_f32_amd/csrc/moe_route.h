@@ -12,9 +12,11 @@ namespace moe {
 // kernel adds the slices in order 0, 1, ... and then the bias, so every logit
 // has one fixed summation order.
 
-// Few tokens: one wavefront per (expert, K-slice) streams its slice of the f32
-// router row with 16-byte loads and dots it with up to TG tokens at a time; a
-// wave-wide sum finishes each partial logit.
+// Few tokens: one wavefront per (expert, K-slice).  The slice is taken in
+// chunks of up to 1024 inputs: a chunk's router weights (four 16-byte loads
+// per lane) and then the activations of TG tokens are all loaded before any
+// arithmetic, so a chunk costs about one memory latency; each lane sums its
+// inputs in ascending order and a wave-wide sum finishes each partial logit.
 template <int TG>
 __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ wr,
@@ -30,16 +32,30 @@ __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ 
     float acc[TG];
 #pragma unroll
     for (int i = 0; i < TG; ++i) acc[i] = 0.0f;
-    for (int c = k0 + lane * 4; c < k1; c += WAVE * 4) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(wrow + c);
+    for (int kc = k0; kc < k1; kc += 1024) {
+      f32x4 wv[4];
+      bool in[4];
 #pragma unroll
-      for (int i = 0; i < TG; ++i) {
-        if (t0 + i < T) {
-          const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + i) * d + c);
-          acc[i] += w.x * bf16_lo(xv.x) + w.y * bf16_hi(xv.x) + w.z * bf16_lo(xv.y) +
-                    w.w * bf16_hi(xv.y);
-        }
+      for (int c = 0; c < 4; ++c) {
+        const int k = kc + 256 * c + 4 * lane;
+        in[c] = k < k1;
+        wv[c] = in[c] ? *reinterpret_cast<const f32x4*>(wrow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      u32x2 xv[TG][4];
+#pragma unroll
+      for (int i = 0; i < TG; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int k = kc + 256 * c + 4 * lane;
+          xv[i][c] = t0 + i < T && in[c] ? *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + i) * d + k)
+                                         : u32x2{0u, 0u};
+        }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < TG; ++i)
+          acc[i] += wv[c].x * bf16_lo(xv[i][c].x) + wv[c].y * bf16_hi(xv[i][c].x) +
+                    wv[c].z * bf16_lo(xv[i][c].y) + wv[c].w * bf16_hi(xv[i][c].y);
     }
 #pragma unroll
     for (int i = 0; i < TG; ++i) {
@@ -135,7 +151,7 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
 
 constexpr int MAX_E = 1024;
 constexpr int MAX_K = 16;
-constexpr int MAX_SPLIT = 8;  // router K-slices summed by route_topk
+constexpr int MAX_SPLIT = 8;  // most router K-slices (partials summed in order by the top-k)
 
 // Order-preserving map of f32 to uint32: a > b  <=>  key(a) > key(b).
 // NaN (outside the contract) maps to 0, below every other value.
@@ -146,14 +162,13 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 }
 
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-// (the K-slice partials summed in slice order, then the bias added).
-// Selection is a radix select on the order keys: 32 rounds of wave ballots
-// build the k-th largest key K bit by bit (the largest value with at least k
-// keys >= it).  Every expert above K is selected, and of those equal to K the
-// lowest indices fill the remaining places, so equal logits go to the lower
-// index.  Each selected expert's place in ascending id order comes from the
-// ballot masks; its weight is its softmax probability over all E experts
-// (max-subtracted), divided by the sum over the k when `renorm`.
+// (the K-slice partials summed in slice order, then the bias added).  The
+// k experts are taken one at a time: each round takes the largest remaining
+// logit (by its order key), and of equal logits the lowest expert index, so
+// the k taken are the k largest with ties going to the lower index.  Each
+// selected expert's place in ascending id order comes from the ballot masks;
+// its weight is its softmax probability over all E experts (max-subtracted),
+// divided by the sum over the k when `renorm`.
 template <int NG>
 __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part, int nsplit,
                                            const float* __restrict__ bias,
@@ -161,48 +176,73 @@ __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part
                                            int T, int E, int k, int renorm) {
   const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1ull;
-  float l[NG];
-  uint32_t key[NG];
+  const size_t TE = (size_t)T * E;
+  size_t col[NG];
   bool valid[NG];
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int e = lane + WAVE * i;
     valid[i] = e < E;
-    const size_t col = (size_t)t * E + min(e, E - 1);
-    float ps[MAX_SPLIT];  // every slice loaded (clamped index) before the in-order sum
-#pragma unroll
-    for (int sp = 0; sp < MAX_SPLIT; ++sp) ps[sp] = part[(size_t)min(sp, nsplit - 1) * T * E + col];
-    float v = ps[0];
-#pragma unroll
-    for (int sp = 1; sp < MAX_SPLIT; ++sp) v += sp < nsplit ? ps[sp] : 0.0f;
-    if (bias) v += bias[col];
-    v = v == 0.0f ? 0.0f : v;  // one key for both signed zeros
-    l[i] = valid[i] && v == v ? v : -INFINITY;
-    key[i] = valid[i] ? order_key(v) : 0u;
+    col[i] = (size_t)t * E + min(e, E - 1);
   }
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < NG; ++i) n += __popcll(__ballot(valid[i] && key[i] >= cand));
-    if (n >= k) thr = cand;
-  }
-  int above = 0;
-#pragma unroll
-  for (int i = 0; i < NG; ++i) above += __popcll(__ballot(valid[i] && key[i] > thr));
-  const int need = k - above;  // places left for keys equal to the threshold
-  int ties_before = 0, sel_before = 0;
-  bool take[NG];
-  int pos[NG];
+  // every load of a group of four slices (clamped index) is issued before
+  // the in-order sum; the bias (or a dummy read) goes with the first group
+  const float* bp = bias ? bias : part;
+  float bv[NG], v[NG];
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
-    const uint64_t tie = __ballot(valid[i] && key[i] == thr);
-    take[i] = valid[i] && (key[i] > thr ||
-                           (key[i] == thr && ties_before + __popcll(tie & below) < need));
+    bv[i] = bp[col[i]];
+    v[i] = 0.0f;
+  }
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float ps[4][NG];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < NG; ++i) ps[j][i] = part[(size_t)min(s0 + j, nsplit - 1) * TE + col[i]];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        v[i] = s0 + j >= nsplit ? v[i] : (s0 + j == 0 ? ps[j][i] : v[i] + ps[j][i]);
+  }
+  float l[NG];
+  uint32_t kv[NG];  // order key + 1 of each logit (NaN: 1), 0 once taken or past E
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    float x = v[i];
+    if (bias) x += bv[i];
+    x = x == 0.0f ? 0.0f : x;  // one key for both signed zeros
+    l[i] = valid[i] && x == x ? x : -INFINITY;
+    kv[i] = valid[i] ? order_key(x) + 1u : 0u;
+  }
+  bool take[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) take[i] = false;
+  for (int j = 0; j < k; ++j) {  // k <= E, so every round finds a key >= 1
+    uint32_t lm = kv[0];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) lm = kv[i] > lm ? kv[i] : lm;
+    const uint32_t mx = wave_max_u32(lm);
+    int sel = 0;
+#pragma unroll
+    for (int i = NG - 1; i >= 0; --i) {  // the lowest index holding mx wins
+      const uint64_t b = __ballot(kv[i] == mx);
+      if (b) sel = WAVE * i + (int)__builtin_ctzll(b);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      if (lane + WAVE * i == sel) {
+        kv[i] = 0u;
+        take[i] = true;
+      }
+  }
+  int pos[NG];
+  int sel_before = 0;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
     const uint64_t sm = __ballot(take[i]);
     pos[i] = sel_before + __popcll(sm & below);
-    ties_before += __popcll(tie);
     sel_before += __popcll(sm);
   }
   float m = -INFINITY;
