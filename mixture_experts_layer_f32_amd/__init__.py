@@ -42,6 +42,15 @@ class MoeError(RuntimeError):
 
 
 def _load():
+    # One HIP runtime per process: torch ships its own libamdhip64, and a
+    # libmoe.so loaded before torch would bind the system copy, leaving two
+    # runtimes that each claim the device.  Loading torch first makes
+    # libmoe.so share torch's (same soname); without torch the system copy
+    # serves alone.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
                           "python -m mixture_experts_layer_f32_amd.build")

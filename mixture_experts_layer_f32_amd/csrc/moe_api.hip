@@ -48,7 +48,8 @@ struct moe_plan_s {
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
   int dec_tall = -1;      // MFMA decode tiles of 32/64 rows: -1 by shape, 0 never, 1 always
   int dec_ks = 0;         // MFMA decode wavefronts per workgroup (k-split), 0 = by shape
-  int gemm_kernel = 1;    // grouped expert stage: 1 = register-weight tiles (e4m3), 0 = LDS weight tiles
+  int gemm_kernel = 3;    // grouped expert stage: 3 = gemm_big (e4m3), 1 = register-weight tiles,
+                          // 2 = gemm_dma, 0 = LDS weight tiles (fp4 default)
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -116,10 +117,21 @@ int dec_ks(const moe_plan_s* p, int nkb) {
   return 4;
 }
 
+// Token chunks per wavefront of gemm_big (tile height 64 * TM): the smallest
+// tile holding 1.25 x the mean slots per expert, so most experts take one
+// tile and stream their weights once.
+int big_tm(const moe_plan_s* p, int T) {
+  const long long S = (long long)T * p->d.top_k;
+  const long long mean = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
+  return mean * 5 / 4 <= 128 ? 2 : (mean * 5 / 4 <= 192 ? 3 : 4);
+}
+
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
 // MFMA decode, else the grouped-GEMM tile height.
 int tile_rows(const moe_plan_s* p, int T) {
   if (use_dec_mfma(p, T)) return 16;
+  if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel == 3)
+    return p->d.wfmt == MOE_W_E4M3_B128 ? 64 * big_tm(p, T) : 128;
   if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel >= 1) return 64;
   return gemm_bm(p, T);
 }
@@ -253,11 +265,11 @@ struct GemmOrder {
   int nb, gc, gt, ntb;
   long long grid;
 };
-GemmOrder gemm_order(const moe_plan_s* p, int max_tiles, int N, int bnm) {
+GemmOrder gemm_order(const moe_plan_s* p, int max_tiles, int N, int bnm, int per_cu = 2) {
   GemmOrder o;
   o.nb = (N + bnm - 1) / bnm;
   o.gc = std::max(1, std::min(4, (o.nb + 7) / 8));
-  o.gt = std::max(1, (p->cus / 8) * 2 / o.gc);
+  o.gt = std::max(1, (p->cus / 8) * per_cu / o.gc);
   o.ntb = (max_tiles + o.gt - 1) / o.gt;
   const int ncb = (o.nb + 8 * o.gc - 1) / (8 * o.gc);
   o.grid = 8LL * o.gc * o.gt * o.ntb * ncb;
@@ -273,13 +285,26 @@ void launch_dma(const moe_plan_s* p, int max_tiles, int N, int K, int T, const u
       act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
 }
 
-template <int FMT, bool GATEUP, int TNW, int PD>
+template <int FMT, bool GATEUP, int TNW, int PD, int BM = 64>
 void launch_rw(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
                DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
                void* out, hipStream_t st) {
-  const GemmOrder o = gemm_order(p, max_tiles, N, RWCfg<FMT, GATEUP, TNW>::BNM);
-  gemm_rw<FMT, GATEUP, TNW, PD><<<dim3((unsigned)o.grid), 256, 0, st>>>(
+  const GemmOrder o = gemm_order(p, max_tiles, N, RWCfg<FMT, GATEUP, TNW, BM>::BNM, BM == 64 ? 2 : 1);
+  gemm_rw<FMT, GATEUP, TNW, PD, BM><<<dim3((unsigned)o.grid), 256, 0, st>>>(
       act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
+}
+
+template <bool GATEUP, int TNW>
+void launch_big(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
+                DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
+                void* out, hipStream_t st) {
+  const int nb = (N + BigCfg<GATEUP, TNW, 2>::BNM - 1) / BigCfg<GATEUP, TNW, 2>::BNM;
+  const dim3 g((unsigned)(8LL * ((max_tiles + 7) / 8) * nb));
+  switch (big_tm(p, T)) {
+    case 2: gemm_big<GATEUP, TNW, 2><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb); break;
+    case 3: gemm_big<GATEUP, TNW, 3><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb); break;
+    default: gemm_big<GATEUP, TNW, 4><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb); break;
+  }
 }
 
 template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK, int PF>
@@ -396,6 +421,21 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
       mark(p, MOE_STAGE_GATEUP, true, st);
       mark(p, MOE_STAGE_DOWN, false, st);
       launch_dma<FMT, false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
+      mark(p, MOE_STAGE_DOWN, true, st);
+      return MOE_OK;
+    }
+    if (p->gemm_kernel == 3) {
+      mark(p, MOE_STAGE_GATEUP, false, st);
+      if constexpr (FMT == FMT_E4M3)
+        launch_big<true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
+      else
+        launch_rw<FMT, true, 1, 2, 128>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
+      mark(p, MOE_STAGE_GATEUP, true, st);
+      mark(p, MOE_STAGE_DOWN, false, st);
+      if constexpr (FMT == FMT_E4M3)
+        launch_big<false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
+      else
+        launch_rw<FMT, false, 2, 2, 128>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
       mark(p, MOE_STAGE_DOWN, true, st);
       return MOE_OK;
     }
@@ -518,21 +558,24 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
   if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KS")) p->dec_ks = std::max(0, std::min(4, std::atoi(v)));
-  // register-weight tiles measured faster for e4m3; for fp4 at its grouped
-  // sizes (tens of slots per expert) the 64-token tile is mostly empty
-  p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 1 : 0;
-  if (const char* v = std::getenv("MOE_GEMM")) p->gemm_kernel = std::max(0, std::min(2, std::atoi(v)));
+  // e4m3: the 128..256-token direct-to-LDS tiles (gemm_big) measured fastest
+  // on every grouped shape (OLMoE shape at 128, 512 and 2048 tokens, the
+  // d = 7168 layer at 512 and 4096); fp4 at its grouped sizes (tens of slots
+  // per expert): LDS-decoded weight tiles
+  p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 3 : 0;
+  if (const char* v = std::getenv("MOE_GEMM")) p->gemm_kernel = std::max(0, std::min(3, std::atoi(v)));
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "
                 "(decode for T<=%d); router: wavefront gemv up to %d tokens, else 64x64 bf16x3 MFMA tiles, split-K; "
-                "decode matvec (row groups per wave %d, 0=auto); grouped MFMA 32x32x16 bf16, "
-                "BM 32/64/128 by slots per expert, BK 64 double-buffered",
+                "decode: MFMA 16-row tiles from %d tokens, matvec below; grouped kernel %d "
+                "(3: 128/192/256-token tiles by slots per expert, direct-to-LDS; 0: LDS-decoded weight tiles), "
+                "MFMA 32x32x16 bf16, BK 64",
                 dev, p->arch.c_str(), p->cus, d.d_model, d.d_ff, d.n_experts, d.top_k,
                 d.wfmt == MOE_W_E4M3_B128 ? "e4m3/128x128"
                 : d.wfmt == MOE_W_E2M1_UE8M0_G32 ? "e2m1/ue8m0x32" : "e2m1/e4m3x16", d.renorm,
                 d.path == MOE_PATH_AUTO ? "auto" : (d.path == MOE_PATH_DECODE ? "decode" : "grouped"),
-                p->t_decode, GEMV_MAX_T, p->dec_nrg);
+                p->t_decode, GEMV_MAX_T, p->dec_mfma_min_t, p->gemm_kernel);
   p->info = buf;
   *out = p;
   return MOE_OK;

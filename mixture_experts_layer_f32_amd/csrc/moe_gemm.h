@@ -23,6 +23,8 @@
 // MFMAs, and one barrier per stage orders the buffers.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_decode.h"
 
@@ -324,10 +326,11 @@ namespace moe {
 // of that 32-input group; NVFP4: 16 bytes and the two e4m3 bytes of its
 // 16-input groups); MFMA step s = 0..3 takes inputs k0 + 32h + 8s ..
 // + 7 from both operands.
-template <int FMT, bool GATEUP, int TNW>
+template <int FMT, bool GATEUP, int TNW, int BM_ = 64>
 struct RWCfg {
   static constexpr int NMAT = GATEUP ? 2 : 1;
-  static constexpr int BM = 64, BK = 64, LDK = BK + 8;  // tokens, stage depth, padded LDS row
+  static constexpr int BM = BM_, BK = 64, LDK = BK + 8;  // tokens, stage depth, padded LDS row
+  static constexpr int AC = BM * 8 / 256;               // 16-byte activation chunks per thread and stage
   static constexpr int TM = BM / 32;
   static constexpr int NW = NMAT * TNW;                 // 32-row weight tiles per wavefront
   static constexpr int BNM = 4 * 32 * TNW;              // weight rows per matrix per workgroup
@@ -341,13 +344,16 @@ template <> struct RWRaw<FMT_NVFP4> { u32x4 w; float sc[2]; };
 
 // GATEUP: act = x [T][K], out = h bf16 [S][N] (N = f, K = d); else act = h
 // [S][K], out = y f32 [S][N] (N = d, K = f).  Block order as gemm_expert.
-template <int FMT, bool GATEUP, int TNW, int PD>
-__global__ __launch_bounds__(256, 2) void gemm_rw(
+// BM_ = 64: two workgroups per CU; BM_ = 128: one, with the 32-row token
+// chunks past the tile's rows skipped.
+template <int FMT, bool GATEUP, int TNW, int PD, int BM_ = 64>
+__global__ __launch_bounds__(256, BM_ == 64 ? 2 : 1) void gemm_rw(
     const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
     void* __restrict__ out, int N, int K, int T, int nb, int gc, int gt, int ntb) {
-  using C = RWCfg<FMT, GATEUP, TNW>;
+  using C = RWCfg<FMT, GATEUP, TNW, BM_>;
   constexpr int NMAT = C::NMAT, BM = C::BM, BK = C::BK, LDK = C::LDK, NW = C::NW, TM = C::TM;
+  constexpr int AC = C::AC;
   __shared__ __attribute__((aligned(16))) uint16_t As[PD + 1][BM * LDK];
   const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
   const int sbsz = gc * gt, sb = sq / sbsz, wi = sq - sb * sbsz;
@@ -361,11 +367,12 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
   const int r32 = lane & 31, h = lane >> 5;
   const int nw0 = n0 + 32 * TNW * w;  // this wavefront's first weight row
 
-  // activation tile: 64 rows x 64 inputs = 512 16-byte chunks, 2 per thread
+  const int mt = (rows + 31) >> 5;  // 32-row token chunks holding rows
+  // activation tile: BM rows x 64 inputs = 8 * BM 16-byte chunks, AC per thread
   const int acol = (tid & 7) * 8;
-  const uint16_t* arow[2];
+  const uint16_t* arow[AC];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < AC; ++i) {
     const int r = (tid + 256 * i) >> 3;
     arow[i] = nullptr;
     if (r < rows) {
@@ -395,9 +402,9 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
     sblk[m] = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * (K >> 7);
   }
 
-  auto load_a = [&](u32x4 (&ra)[2], int k0) {
+  auto load_a = [&](u32x4 (&ra)[AC], int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < AC; ++i)
       ra[i] = arow[i] != nullptr && k0 + acol < K
                   ? *reinterpret_cast<const u32x4*>(arow[i] + k0 + acol) : u32x4{0u, 0u, 0u, 0u};
   };
@@ -420,9 +427,9 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
       }
     }
   };
-  auto store_a = [&](const u32x4 (&ra)[2], uint16_t* buf) {
+  auto store_a = [&](const u32x4 (&ra)[AC], uint16_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < AC; ++i)
       *reinterpret_cast<u32x4*>(buf + ((tid + 256 * i) >> 3) * LDK + acol) = ra[i];
   };
 
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
   // `even`: ks is even (compile-time after unrolling when NB is even): an
   // e4m3 scale block (two stages) starts there and ends on the odd stage
   auto stage = [&](int ks, bool even, const RWRaw<FMT> (&cur)[NW], RWRaw<FMT> (&pf)[NW],
-                   u32x4 (&ra_pf)[2], const u32x4 (&ra_next)[2]) {
+                   u32x4 (&ra_pf)[AC], const u32x4 (&ra_next)[AC]) {
     const int kp = min(ks + PD, nk - 1) * BK;
     load_a(ra_pf, kp);
     load_w(pf, kp);
@@ -474,6 +481,7 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+          if (TM > 2 && i >= mt) continue;  // chunk past the tile's rows (uniform)
           if constexpr (FMT == FMT_E4M3)
             part[i][t] = (even && s == 0)
                              ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, zero, 0, 0, 0)
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void gemm_rw(
 
   // prologue: stages 0 .. PD-1 loaded, stage 0's activations in LDS
   RWRaw<FMT> wr[NB][NW];
-  u32x4 ra[NB][2];
+  u32x4 ra[NB][AC];
 #pragma unroll
   for (int p = 0; p < PD; ++p) {
     load_a(ra[p], min(p, nk - 1) * BK);
@@ -784,6 +792,253 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
             reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = acc[i][j][v];
         }
       }
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM for e4m3 weights with BM = 64 TM tokens per tile (TM = 2, 3
+// or 4).  8 wavefronts (2 per SIMD) in a 2 x 4 grid: wavefront (wm, wn) owns
+// tokens 32 TM wm .. of the tile (TM 32-row chunks) and two 32-row weight
+// tiles of column wn (gate and up rows 32 wn .. for gate/up; rows 64 wn ..
+// for down), so a workgroup covers BM tokens x 128 rows of each matrix (down:
+// 256 rows) and every weight byte it loads feeds up to BM tokens: an expert
+// with up to BM slots streams its weights once.  All tile bytes move by
+// direct-to-LDS loads into NS = 3 slots (two stages in flight; at BM = 256,
+// 144 KB of LDS), one workgroup per CU.
+// LDS layouts (64 banks of 4 bytes; a 16-byte read serves 16 lanes per
+// pass): activation row r (128 bytes per 64-input stage) holds its 16-byte
+// chunk c at slot c ^ ((r >> 1) & 7), and weight row r (64 bytes) its chunk c
+// at slot c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows
+// touch 16 different bank groups; each weight load instruction covers 16
+// rows x 64 contiguous bytes.
+//
+// Block scales without a second accumulator: a block scale s = 2^e * m
+// (1 <= m < 2) is split; 2^e goes into the fp8 -> bf16 conversion (exact:
+// an e4m3 value times a power of two is a bf16 value), and the running sum is
+// kept in units of the current block's m: at each block boundary
+// R <- R * (m_prev / m) in f32, then the block's MFMAs add into R, and the
+// output is R * m_last.  This is the f32 sum of the scaled block products up
+// to one f32 rounding per block of the running sum (relative 2^-24 each).
+template <bool GATEUP, int TNW, int TM_>
+struct BigCfg {
+  static constexpr int NMAT = GATEUP ? 2 : 1;
+  static constexpr int TM = TM_, BM = 64 * TM, BK = 64;
+  static constexpr int NS = TM == 2 ? 5 : (TM == 3 ? 4 : 3);  // slots: as many as 160 KB of LDS holds
+  static constexpr int NW = NMAT * TNW;                // weight tiles per wavefront (2)
+  static constexpr int BNM = 4 * 32 * TNW;             // weight rows per matrix per workgroup
+  static constexpr int A_V4 = BM * 8;                  // u32x4 per activation stage (BM x 128 B)
+  static constexpr int W_V4 = 4 * NW * 2 * 64;         // u32x4 per weight stage (16 KB)
+  static constexpr int AL = TM;                        // activation loads per lane and stage
+  static constexpr int LOADS = AL + 2;                 // direct-to-LDS loads per lane and stage
+  static_assert(NW == 2, "each wavefront of a column loads one of its two weight tiles");
+};
+
+// The power-of-two part (exponent bits) and the signed mantissa part (+-[1, 2))
+// of a normal f32, whose product is the value.
+__device__ __forceinline__ float pow2_part(float s) { return __uint_as_float(__float_as_uint(s) & 0x7F800000u); }
+__device__ __forceinline__ float mant_part(float s) {
+  return __uint_as_float((__float_as_uint(s) & 0x807FFFFFu) | 0x3F800000u);
+}
+// e4m3 pairs times a power of two -> bf16 (exact; the conversion applies the
+// exponent of its scale operand)
+__device__ __forceinline__ bf16x8 e4m3x8_scaled_to_bf16(uint32_t lo, uint32_t hi, float p2) {
+  return pack_bf16x8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, p2, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, p2, true),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, p2, false),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, p2, true));
+}
+
+template <bool GATEUP, int TNW, int TM_>
+__global__ __launch_bounds__(512, 1) void gemm_big(
+    const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
+    void* __restrict__ out, int N, int K, int T, int nb) {
+  using C = BigCfg<GATEUP, TNW, TM_>;
+  constexpr int NMAT = C::NMAT, NW = C::NW, TM = C::TM, BK = C::BK, NS = C::NS, AL = C::AL;
+  __shared__ u32x4 sA[NS][C::A_V4];
+  __shared__ u32x4 sW[NS][C::W_V4];
+  // Block order: workgroup L runs on XCD L % 8; XCD x takes the tile-list
+  // entries x, x + 8, ... and each entry's nb column blocks in turn, so an
+  // entry's activation rows are fetched into one XCD's L2 and serve all of
+  // its column blocks, and each weight byte is read by one workgroup.
+  const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
+  const int lt = sq / nb, cblk = sq - lt * nb;
+  const int ti = 8 * lt + xcd;
+  if (ti >= *n_tiles) return;
+  const int4 tile = tiles[ti];
+  const int e = tile.x, p_start = tile.y, rows = tile.z;
+  const int n0 = cblk * C::BNM;
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int wm = w >> 2, wn = w & 3;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nw0 = n0 + 32 * TNW * wn;  // this column's first weight row
+  // 32-row token chunks of this wavefront that hold rows (uniform, 0..4)
+  const int nact = min(max(((rows + 31) >> 5) - TM * wm, 0), TM);
+
+  // activation loads of this lane: AL per stage, rows (AL w + i) * 8 + lane / 8
+  // (rows past the tile repeat its last row; their outputs are not stored),
+  // LDS slot lane % 8 of the row holding chunk slot ^ ((row >> 1) & 7)
+  const uint16_t* asrc[AL];
+  int achunk[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int r = (AL * w + i) * 8 + (lane >> 3);
+    const int rr = min(r, rows - 1);
+    const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
+                              : (size_t)(p_start + rr);
+    asrc[i] = act + src * K;
+    achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+  }
+  // the weight tile this wavefront loads: tile wm of its column (matrix wm
+  // for gate/up; rows 32 wm .. of the column for down).  Load j covers tile
+  // rows 16 j + lane / 4 (clamped to N), slot lane % 4 holding chunk
+  // slot ^ ((row >> 2) & 3) of the row's 64 bytes.
+  const int tl = wm;
+  const int ml = GATEUP ? tl : 0, jl = GATEUP ? 0 : tl;
+  const DMat& WL = ml == 0 ? W0 : W1;
+  const uint8_t* wsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int tr = 16 * j + (lane >> 2);
+    wsrc[j] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * K +
+              16 * ((lane & 3) ^ ((tr >> 2) & 3));
+  }
+  // e4m3 scales of this column's 128-row block, k-block kb in lane kb % 64 of register kb / 64
+  float scv[NMAT][2];
+  {
+    const int kbs = K >> 7;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const DMat& W = m == 0 ? W0 : W1;
+      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
+      scv[m][0] = lane < kbs ? sf[lane] : 1.0f;
+      scv[m][1] = lane + 64 < kbs ? sf[lane + 64] : 1.0f;
+    }
+  }
+  auto block_scale = [&](int m, int kb) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? scv[m][0] : scv[m][1]), kb & 63));
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  auto issue = [&](int kk, int slot) {
+    const int k0 = kk * BK;
+#pragma unroll
+    for (int i = 0; i < AL; ++i)
+      lds_dma16(asrc[i] + k0 + 8 * achunk[i], &sA[slot][(AL * w + i) * 64]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) lds_dma16(wsrc[j] + k0, &sW[slot][((wn * NW + tl) * 2 + j) * 64]);
+  };
+
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 R[TM][NW];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < NW; ++t) R[i][t] = zero;
+  float p2[NMAT], mcur[NMAT];  // power-of-two and mantissa parts of the current block's scale
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    p2[m] = pow2_part(block_scale(m, 0));
+    mcur[m] = mant_part(block_scale(m, 0));
+  }
+
+  auto compute = [&](int ks, int slot) {
+    // a new 128-deep scale block: R <- R * (m_prev / m), chunk by chunk just
+    // before the chunk's first MFMA of the block (the multiplies of one chunk
+    // then overlap the MFMAs of the one before)
+    const bool newblk = (ks & 1) == 0 && ks > 0;
+    float ratio[NMAT];
+    if (newblk) {
+      const int kb = ks >> 1;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const float sc = block_scale(m, kb);
+        const float mn = mant_part(sc);
+        ratio[m] = mcur[m] / mn;
+        p2[m] = pow2_part(sc);
+        mcur[m] = mn;
+      }
+    }
+    const u32x4* a_s = sA[slot];
+    const u32x4* w_s = sW[slot];
+    // this stage's weight fragments, decoded once for all token chunks
+    bf16x8 b[NW][4];
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {  // chunk 2h + q of row r32
+        const u32x4 v = w_s[(wn * NW + t) * 128 + r32 * 4 + ((2 * h + q) ^ ((r32 >> 2) & 3))];
+        const float ps = p2[GATEUP ? t : 0];
+        b[t][2 * q] = e4m3x8_scaled_to_bf16(v.x, v.y, ps);
+        b[t][2 * q + 1] = e4m3x8_scaled_to_bf16(v.z, v.w, ps);
+      }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= nact) break;  // uniform
+      if (newblk) {
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+          const float r = ratio[GATEUP ? t : 0];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) R[i][t][v] *= r;
+        }
+      }
+      const int mrow = 32 * TM * wm + 32 * i + r32;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, a_s[mrow * 8 + ((4 * h + s) ^ ((mrow >> 1) & 7))]);
+#pragma unroll
+        for (int t = 0; t < NW; ++t) R[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[t][s], R[i][t], 0, 0, 0);
+      }
+    }
+  };
+
+  // NS slots, NS - 1 stages in flight: at stage ks wait for its loads (the
+  // next stage may stay outstanding), one barrier (its bytes visible to every
+  // wavefront; the slot of stage ks - 1 free), issue stage ks + NS - 1 into
+  // that slot, compute stage ks.  Past the last issue the waits drain all.
+  constexpr int LD = C::LOADS;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) issue(p, p);
+  for (int ks0 = 0; ks0 < nk; ks0 += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int ks = ks0 + j;
+      if (ks >= nk) break;
+      if (ks + NS - 2 < nk)
+        wait_vm<(NS - 2) * LD>();
+      else
+        wait_vm<0>();
+      stage_barrier();
+      if (ks + NS - 1 < nk) issue(ks + NS - 1, (j + NS - 1) % NS);
+      compute(ks, j);
+    }
+  }
+  wait_vm<0>();
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= nact) break;
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 32 * TM * wm + 32 * i + acc_row(v, lane);
+        const int n = nw0 + 32 * j + r32;
+        if (m < rows && n < N) {
+          if (GATEUP) {
+            const float g = R[i][j][v] * mcur[0], u = R[i][TNW + j][v] * mcur[NMAT - 1];
+            reinterpret_cast<uint16_t*>(out)[(size_t)(p_start + m) * N + n] = (uint16_t)f32_to_bf16_rne(silu(g) * u);
+          } else {
+            reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = R[i][j][v] * mcur[0];
+          }
+        }
+      }
+  }
 }
 
 }  // namespace moe

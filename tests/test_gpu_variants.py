@@ -57,7 +57,7 @@ def check_all(g, ref):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("gemm", ["0", "1", "2"])
+@pytest.mark.parametrize("gemm", ["0", "1", "2", "3"])
 def test_grouped_kernels(fmt, gemm):
     wl, layer, W = get(fmt)
     T = wl.batches[0]
@@ -67,7 +67,7 @@ def test_grouped_kernels(fmt, gemm):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("gemm", ["0", "1", "2"])
+@pytest.mark.parametrize("gemm", ["0", "1", "2", "3"])
 def test_grouped_kernels_one_expert_many_tiles(fmt, gemm):
     """A large bias on expert 1 sends all 150 tokens there: that expert spans
     three 64-token tiles (the last one partial), the others share the rest."""
