@@ -48,8 +48,9 @@ struct moe_plan_s {
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
   int dec_tall = -1;      // MFMA decode tiles of 32/64 rows: -1 by shape, 0 never, 1 always
   int dec_ks = 0;         // MFMA decode wavefronts per workgroup (k-split), 0 = by shape
-  int gemm_kernel = 3;    // grouped expert stage: 3 = gemm_big (e4m3), 1 = register-weight tiles,
-                          // 2 = gemm_dma, 0 = LDS weight tiles (fp4 default)
+  int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (11, 12, 22, 23, 24), 0 = by shape
+  int gemm_kernel = 3;    // grouped expert stage: 3 = gemm_big (default), 1 = register-weight tiles,
+                          // 2 = gemm_dma, 0 = LDS weight tiles
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -117,21 +118,26 @@ int dec_ks(const moe_plan_s* p, int nkb) {
   return 4;
 }
 
-// Token chunks per wavefront of gemm_big (tile height 64 * TM): the smallest
-// tile holding 1.25 x the mean slots per expert, so most experts take one
-// tile and stream their weights once.
-int big_tm(const moe_plan_s* p, int T) {
+// Shape of gemm_big's tiles, as 10 * WGM + TM (tile height 32 * WGM * TM),
+// from the mean slots per expert: measured on every grouped workload over all
+// five shapes, 128-token tiles won up to 16 slots per expert (the fp4 layer at
+// 16 and 1024 tokens; even with one slot, ahead of the wide short tiles),
+// 192-token tiles at 64 to 128 (the skewed OLMoE shape at 512 tokens, whose
+// hot experts hold about 150, and the d = 7168 layer at 4096) and 256-token
+// tiles at 256 (the skewed OLMoE shape at 2048).
+int big_cfg(const moe_plan_s* p, int T) {
+  if (p->big_cfg > 0) return p->big_cfg;
   const long long S = (long long)T * p->d.top_k;
   const long long mean = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
-  return mean * 5 / 4 <= 128 ? 2 : (mean * 5 / 4 <= 192 ? 3 : 4);
+  return mean <= 32 ? 22 : (mean <= 160 ? 23 : 24);
 }
+int big_rows(int cfg) { return 32 * (cfg / 10) * (cfg % 10); }
 
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
 // MFMA decode, else the grouped-GEMM tile height.
 int tile_rows(const moe_plan_s* p, int T) {
   if (use_dec_mfma(p, T)) return 16;
-  if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel == 3)
-    return p->d.wfmt == MOE_W_E4M3_B128 ? 64 * big_tm(p, T) : 128;
+  if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel == 3) return big_rows(big_cfg(p, T));
   if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel >= 1) return 64;
   return gemm_bm(p, T);
 }
@@ -294,17 +300,30 @@ void launch_rw(const moe_plan_s* p, int max_tiles, int N, int K, int T, const ui
       act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
 }
 
-template <bool GATEUP, int TNW>
+template <int FMT, bool GATEUP, int TNW, int TM, int WGM>
+void launch_big_cfg(int max_tiles, int N, int K, int T, const uint16_t* act, DMat W0, DMat W1,
+                    const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of, void* out,
+                    hipStream_t st) {
+  constexpr int BNM = BigCfg<FMT, GATEUP, TNW, TM, WGM>::BNM;
+  const int nb = (N + BNM - 1) / BNM;
+  const dim3 g((unsigned)(8LL * ((max_tiles + 7) / 8) * nb));
+  gemm_big<FMT, GATEUP, TNW, TM, WGM><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb);
+}
+
+template <int FMT, bool GATEUP, int TNW>
 void launch_big(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
                 DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
                 void* out, hipStream_t st) {
-  const int nb = (N + BigCfg<GATEUP, TNW, 2>::BNM - 1) / BigCfg<GATEUP, TNW, 2>::BNM;
-  const dim3 g((unsigned)(8LL * ((max_tiles + 7) / 8) * nb));
-  switch (big_tm(p, T)) {
-    case 2: gemm_big<GATEUP, TNW, 2><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb); break;
-    case 3: gemm_big<GATEUP, TNW, 3><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb); break;
-    default: gemm_big<GATEUP, TNW, 4><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb); break;
+#define MOE_BIG(TM, WGM) \
+  launch_big_cfg<FMT, GATEUP, TNW, TM, WGM>(max_tiles, N, K, T, act, W0, W1, tiles, n_tiles, tok_of, out, st)
+  switch (big_cfg(p, T)) {
+    case 11: MOE_BIG(1, 1); break;
+    case 12: MOE_BIG(2, 1); break;
+    case 22: MOE_BIG(2, 2); break;
+    case 23: MOE_BIG(3, 2); break;
+    default: MOE_BIG(4, 2); break;
   }
+#undef MOE_BIG
 }
 
 template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK, int PF>
@@ -426,16 +445,10 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
     }
     if (p->gemm_kernel == 3) {
       mark(p, MOE_STAGE_GATEUP, false, st);
-      if constexpr (FMT == FMT_E4M3)
-        launch_big<true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
-      else
-        launch_rw<FMT, true, 1, 2, 128>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
+      launch_big<FMT, true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
       mark(p, MOE_STAGE_GATEUP, true, st);
       mark(p, MOE_STAGE_DOWN, false, st);
-      if constexpr (FMT == FMT_E4M3)
-        launch_big<false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
-      else
-        launch_rw<FMT, false, 2, 2, 128>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
+      launch_big<FMT, false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
       mark(p, MOE_STAGE_DOWN, true, st);
       return MOE_OK;
     }
@@ -544,11 +557,11 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   p->arch = prop.gcnArchName;
   // Decode (every selected expert's weights streamed once per 16 of its slots)
   // while the slots per expert stay small; measured crossovers against the
-  // grouped GEMM: T*k about 12*E for e4m3 (OLMoE shape between T = 64 and 128,
-  // the d = 7168 layer between 256 and 512); e2m1 decode was faster at every
-  // size measured, up to T*k = 16*E (NVFP4: the same fp4 codes, so the same
-  // crossover).
-  p->t_decode = std::max(1, (d.wfmt == MOE_W_E4M3_B128 ? 12 : 16) * d.n_experts / d.top_k);
+  // grouped GEMM (gemm_big): T*k about 10*E (OLMoE shape: decode ahead at
+  // T = 64, grouped at 96; the d = 7168 layer: decode at 256, grouped at 384;
+  // the e2m1 fp4 layer: decode at 512, grouped at 768), 12*E for NVFP4 (even
+  // at T = 768).
+  p->t_decode = std::max(1, (d.wfmt == MOE_W_E2M1_E4M3_G16 ? 12 : 10) * d.n_experts / d.top_k);
   // tuning knobs of the decode matvec
   if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
@@ -558,11 +571,14 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
   if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KS")) p->dec_ks = std::max(0, std::min(4, std::atoi(v)));
-  // e4m3: the 128..256-token direct-to-LDS tiles (gemm_big) measured fastest
-  // on every grouped shape (OLMoE shape at 128, 512 and 2048 tokens, the
-  // d = 7168 layer at 512 and 4096); fp4 at its grouped sizes (tens of slots
-  // per expert): LDS-decoded weight tiles
-  p->gemm_kernel = d.wfmt == MOE_W_E4M3_B128 ? 3 : 0;
+  if (const char* v = std::getenv("MOE_BIG_CFG")) {
+    const int c = std::atoi(v);
+    p->big_cfg = (c == 11 || c == 12 || c == 22 || c == 23 || c == 24) ? c : 0;
+  }
+  // the 128..256-token direct-to-LDS tiles (gemm_big) measured fastest on
+  // every grouped shape of every format (OLMoE shape at 128, 512 and 2048
+  // tokens, the d = 7168 layer at 512 and 4096, the fp4 layer at 1024)
+  p->gemm_kernel = 3;
   if (const char* v = std::getenv("MOE_GEMM")) p->gemm_kernel = std::max(0, std::min(3, std::atoi(v)));
   char buf[512];
   std::snprintf(buf, sizeof buf,

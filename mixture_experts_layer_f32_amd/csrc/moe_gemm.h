@@ -799,41 +799,52 @@ __global__ __launch_bounds__(256, 2) void gemm_dma(
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM for e4m3 weights with BM = 64 TM tokens per tile (TM = 2, 3
-// or 4).  8 wavefronts (2 per SIMD) in a 2 x 4 grid: wavefront (wm, wn) owns
-// tokens 32 TM wm .. of the tile (TM 32-row chunks) and two 32-row weight
-// tiles of column wn (gate and up rows 32 wn .. for gate/up; rows 64 wn ..
-// for down), so a workgroup covers BM tokens x 128 rows of each matrix (down:
-// 256 rows) and every weight byte it loads feeds up to BM tokens: an expert
-// with up to BM slots streams its weights once.  All tile bytes move by
-// direct-to-LDS loads into NS = 3 slots (two stages in flight; at BM = 256,
-// 144 KB of LDS), one workgroup per CU.
+// Grouped GEMM, every weight format: 8 wavefronts (2 per SIMD) in a WGM x
+// (8 / WGM) grid; wavefront (wm, wn) owns TM 32-row token chunks of the tile
+// (tokens 32 TM wm ..) and two 32-row weight tiles of column wn (gate and up
+// rows 32 wn .. for gate/up; rows 64 wn .. for down).  A workgroup covers
+// BM = 32 WGM TM tokens x 32 (8 / WGM) rows of each matrix (down: twice the
+// rows), and every weight byte it loads feeds up to BM tokens: an expert with
+// up to BM slots streams its weights once.  WGM = 2 with TM = 2..4 for tens
+// to hundreds of slots per expert; WGM = 1 with TM = 1..2 (wide, short
+// tiles) for a few.  All tile bytes move by direct-to-LDS loads into NS
+// slots (as many as the 160 KB of LDS holds, at most 6; NS - 1 stages in
+// flight), one workgroup per CU.
 // LDS layouts (64 banks of 4 bytes; a 16-byte read serves 16 lanes per
 // pass): activation row r (128 bytes per 64-input stage) holds its 16-byte
-// chunk c at slot c ^ ((r >> 1) & 7), and weight row r (64 bytes) its chunk c
-// at slot c ^ ((r >> 2) & 3), so the fragment reads of 16 consecutive rows
-// touch 16 different bank groups; each weight load instruction covers 16
-// rows x 64 contiguous bytes.
+// chunk c at slot c ^ ((r >> 1) & 7); an e4m3 weight row (64 bytes) its chunk
+// c at slot c ^ ((r >> 2) & 3), an fp4 row (32 bytes) at c ^ ((r >> 3) & 1),
+// so the fragment reads of 16 consecutive rows touch 16 different bank
+// groups; each weight load instruction covers whole 64- or 32-byte row
+// segments.
 //
-// Block scales without a second accumulator: a block scale s = 2^e * m
-// (1 <= m < 2) is split; 2^e goes into the fp8 -> bf16 conversion (exact:
+// e4m3 block scales without a second accumulator: a block scale s = 2^e * m
+// (1 <= |m| < 2) is split; 2^e goes into the fp8 -> bf16 conversion (exact:
 // an e4m3 value times a power of two is a bf16 value), and the running sum is
 // kept in units of the current block's m: at each block boundary
 // R <- R * (m_prev / m) in f32, then the block's MFMAs add into R, and the
 // output is R * m_last.  This is the f32 sum of the scaled block products up
 // to one f32 rounding per block of the running sum (relative 2^-24 each).
-template <bool GATEUP, int TNW, int TM_>
+// fp4 scales are applied exactly in the conversion, so there is no rescale.
+template <int FMT, bool GATEUP, int TNW, int TM_, int WGM_>
 struct BigCfg {
+  static constexpr bool FP4 = FMT != FMT_E4M3;
   static constexpr int NMAT = GATEUP ? 2 : 1;
-  static constexpr int TM = TM_, BM = 64 * TM, BK = 64;
-  static constexpr int NS = TM == 2 ? 5 : (TM == 3 ? 4 : 3);  // slots: as many as 160 KB of LDS holds
+  static constexpr int WGM = WGM_, WGN = 8 / WGM;      // wavefront grid
+  static constexpr int TM = TM_, BM = 32 * WGM * TM, BK = 64;
   static constexpr int NW = NMAT * TNW;                // weight tiles per wavefront (2)
-  static constexpr int BNM = 4 * 32 * TNW;             // weight rows per matrix per workgroup
+  static constexpr int BNM = WGN * 32 * TNW;           // weight rows per matrix per workgroup
   static constexpr int A_V4 = BM * 8;                  // u32x4 per activation stage (BM x 128 B)
-  static constexpr int W_V4 = 4 * NW * 2 * 64;         // u32x4 per weight stage (16 KB)
-  static constexpr int AL = TM;                        // activation loads per lane and stage
-  static constexpr int LOADS = AL + 2;                 // direct-to-LDS loads per lane and stage
-  static_assert(NW == 2, "each wavefront of a column loads one of its two weight tiles");
+  static constexpr int AL = (A_V4 + 511) / 512;        // activation loads per lane and stage
+  static constexpr int WL = FP4 ? 1 : 2;               // weight loads per lane, tile and stage
+  static constexpr int TPW = NW / WGM;                 // weight tiles each wavefront loads
+  static constexpr int W_V4 = WGN * NW * WL * 64;      // u32x4 per weight stage
+  static constexpr int S_V4 = FP4 ? WGN * NW * 16 : 0; // fp4: one scale dword per lane and tile, after the weights
+  static constexpr int LOADS = AL + TPW * (WL + (FP4 ? 1 : 0));  // direct-to-LDS loads per lane and stage
+  static constexpr int SLOT = 16 * (A_V4 + W_V4 + S_V4);
+  static constexpr int NS = 160 * 1024 / SLOT > 6 ? 6 : 160 * 1024 / SLOT;  // slots the 160 KB of LDS holds
+  static_assert(NS >= 3, "two stages in flight");
+  static_assert(NW == 2 && (WGM == 1 || WGM == 2), "the wavefronts of a column share its two weight tiles");
 };
 
 // The power-of-two part (exponent bits) and the signed mantissa part (+-[1, 2))
@@ -850,16 +861,32 @@ __device__ __forceinline__ bf16x8 e4m3x8_scaled_to_bf16(uint32_t lo, uint32_t hi
                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, p2, false),
                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, p2, true));
 }
+// Direct-to-LDS loads of one byte / one 16-bit word per lane: lane l's value,
+// zero-extended, lands in the dword at LDS base + 4 l.
+__device__ __forceinline__ void lds_dma_u8(const void* g, const uint32_t* l) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t*)l);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ubyte %0, off" ::"v"(g), "s"(a) : "m0");
+}
+__device__ __forceinline__ void lds_dma_u16(const void* g, const uint32_t* l) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t*)l);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(a) : "m0");
+}
 
-template <bool GATEUP, int TNW, int TM_>
+template <int FMT, bool GATEUP, int TNW, int TM_, int WGM_>
 __global__ __launch_bounds__(512, 1) void gemm_big(
     const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
     void* __restrict__ out, int N, int K, int T, int nb) {
-  using C = BigCfg<GATEUP, TNW, TM_>;
+  using C = BigCfg<FMT, GATEUP, TNW, TM_, WGM_>;
+  constexpr bool FP4 = C::FP4;
   constexpr int NMAT = C::NMAT, NW = C::NW, TM = C::TM, BK = C::BK, NS = C::NS, AL = C::AL;
+  constexpr int WGM = C::WGM, BM = C::BM, TPW = C::TPW;
   __shared__ u32x4 sA[NS][C::A_V4];
-  __shared__ u32x4 sW[NS][C::W_V4];
+  __shared__ u32x4 sW[NS][C::W_V4 + C::S_V4];
+  // fp4 scale dwords of slot s: after the slot's weight bytes
+  auto sS = [&](int slot) { return reinterpret_cast<uint32_t*>(&sW[slot][C::W_V4]); };
   // Block order: workgroup L runs on XCD L % 8; XCD x takes the tile-list
   // entries x, x + 8, ... and each entry's nb column blocks in turn, so an
   // entry's activation rows are fetched into one XCD's L2 and serve all of
@@ -872,43 +899,64 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   const int e = tile.x, p_start = tile.y, rows = tile.z;
   const int n0 = cblk * C::BNM;
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
-  const int wm = w >> 2, wn = w & 3;
+  const int wm = WGM == 2 ? w >> 2 : 0, wn = WGM == 2 ? w & 3 : w;
   const int r32 = lane & 31, h = lane >> 5;
   const int nw0 = n0 + 32 * TNW * wn;  // this column's first weight row
   // 32-row token chunks of this wavefront that hold rows (uniform, 0..4)
   const int nact = min(max(((rows + 31) >> 5) - TM * wm, 0), TM);
 
   // activation loads of this lane: AL per stage, rows (AL w + i) * 8 + lane / 8
-  // (rows past the tile repeat its last row; their outputs are not stored),
-  // LDS slot lane % 8 of the row holding chunk slot ^ ((row >> 1) & 7)
+  // mod BM (a short tile's rows are loaded twice, to the same place; rows
+  // past the tile repeat its last row, their outputs are not stored), LDS
+  // slot lane % 8 of the row holding chunk slot ^ ((row >> 1) & 7)
   const uint16_t* asrc[AL];
   int achunk[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = (AL * w + i) * 8 + (lane >> 3);
+    const int r = ((AL * w + i) * 8 + (lane >> 3)) % BM;
     const int rr = min(r, rows - 1);
     const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
                               : (size_t)(p_start + rr);
     asrc[i] = act + src * K;
     achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
   }
-  // the weight tile this wavefront loads: tile wm of its column (matrix wm
-  // for gate/up; rows 32 wm .. of the column for down).  Load j covers tile
-  // rows 16 j + lane / 4 (clamped to N), slot lane % 4 holding chunk
-  // slot ^ ((row >> 2) & 3) of the row's 64 bytes.
-  const int tl = wm;
-  const int ml = GATEUP ? tl : 0, jl = GATEUP ? 0 : tl;
-  const DMat& WL = ml == 0 ? W0 : W1;
-  const uint8_t* wsrc[2];
+  // the weight tiles this wavefront loads: WGM = 2: tile wm of its column
+  // (the other wavefront of the column loads the other); WGM = 1: both.  Tile
+  // t is matrix t for gate/up, rows 32 t .. of the column for down; rows are
+  // clamped to N.  e4m3 (64 bytes of a row per stage): load j covers tile rows
+  // 16 j + lane / 4, slot lane % 4 holding chunk slot ^ ((row >> 2) & 3).  fp4
+  // (32 bytes): one load covers the 32 rows, slot lane % 2 of row lane / 2
+  // holding chunk slot ^ ((row >> 3) & 1).  The fp4 scales of lane (r, h):
+  // the group of inputs 32 h .. of row r (e2m1: one UE8M0 byte; NVFP4: the
+  // two e4m3 bytes of its 16-input halves).
+  const int64_t rbytes = FP4 ? (int64_t)K / 2 : (int64_t)K;
+  const int sgroups = FMT == FMT_NVFP4 ? K >> 4 : K >> 5;
+  int tls[TPW];
+  const uint8_t* wsrc[TPW][2];
+  int wchunk = 0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tr = 16 * j + (lane >> 2);
-    wsrc[j] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * K +
-              16 * ((lane & 3) ^ ((tr >> 2) & 3));
+  for (int u = 0; u < TPW; ++u) {
+    const int tl = WGM == 2 ? wm : u;
+    tls[u] = tl;
+    const int ml = GATEUP ? tl : 0, jl = GATEUP ? 0 : tl;
+    const DMat& WL = ml == 0 ? W0 : W1;
+    if constexpr (!FP4) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tr = 16 * j + (lane >> 2);
+        wsrc[u][j] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes +
+                     16 * ((lane & 3) ^ ((tr >> 2) & 3));
+      }
+    } else {
+      const int tr = lane >> 1;
+      wchunk = (lane & 1) ^ ((tr >> 3) & 1);
+      wsrc[u][0] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+      wsrc[u][1] = WL.s + e * WL.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
+    }
   }
   // e4m3 scales of this column's 128-row block, k-block kb in lane kb % 64 of register kb / 64
   float scv[NMAT][2];
-  {
+  if constexpr (!FP4) {
     const int kbs = K >> 7;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
@@ -923,13 +971,28 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   };
 
   const int nk = (K + BK - 1) / BK;
+  // stage kk's loads into slot `slot` (addresses clamped into the rows at a
+  // k-tail; those inputs are zeroed at decode)
   auto issue = [&](int kk, int slot) {
     const int k0 = kk * BK;
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      lds_dma16(asrc[i] + k0 + 8 * achunk[i], &sA[slot][(AL * w + i) * 64]);
+      lds_dma16(asrc[i] + min(k0 + 8 * achunk[i], K - 8), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) lds_dma16(wsrc[j] + k0, &sW[slot][((wn * NW + tl) * 2 + j) * 64]);
+    for (int u = 0; u < TPW; ++u) {
+      const int tl = tls[u];
+      if constexpr (!FP4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) lds_dma16(wsrc[u][j] + k0, &sW[slot][((wn * NW + tl) * 2 + j) * 64]);
+      } else {
+        lds_dma16(wsrc[u][0] + min(k0 + 32 * wchunk, K - 32) / 2, &sW[slot][(wn * NW + tl) * 64]);
+        const int kl = min(k0 + 32 * h, K - 32);
+        if constexpr (FMT == FMT_NVFP4)
+          lds_dma_u16(wsrc[u][1] + (kl >> 4), sS(slot) + (wn * NW + tl) * 64);
+        else
+          lds_dma_u8(wsrc[u][1] + (kl >> 5), sS(slot) + (wn * NW + tl) * 64);
+      }
+    }
   };
 
   const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -938,18 +1001,18 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int t = 0; t < NW; ++t) R[i][t] = zero;
-  float p2[NMAT], mcur[NMAT];  // power-of-two and mantissa parts of the current block's scale
+  float p2[NMAT], mcur[NMAT];  // e4m3: power-of-two and mantissa parts of the current block's scale
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
-    p2[m] = pow2_part(block_scale(m, 0));
-    mcur[m] = mant_part(block_scale(m, 0));
+    p2[m] = FP4 ? 1.0f : pow2_part(block_scale(m, 0));
+    mcur[m] = FP4 ? 1.0f : mant_part(block_scale(m, 0));
   }
 
   auto compute = [&](int ks, int slot) {
-    // a new 128-deep scale block: R <- R * (m_prev / m), chunk by chunk just
-    // before the chunk's first MFMA of the block (the multiplies of one chunk
-    // then overlap the MFMAs of the one before)
-    const bool newblk = (ks & 1) == 0 && ks > 0;
+    // e4m3, a new 128-deep scale block: R <- R * (m_prev / m), chunk by
+    // chunk just before the chunk's first MFMA of the block (the multiplies
+    // of one chunk then overlap the MFMAs of the one before)
+    const bool newblk = !FP4 && (ks & 1) == 0 && ks > 0;
     float ratio[NMAT];
     if (newblk) {
       const int kb = ks >> 1;
@@ -966,15 +1029,33 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     const u32x4* w_s = sW[slot];
     // this stage's weight fragments, decoded once for all token chunks
     bf16x8 b[NW][4];
+    if constexpr (!FP4) {
 #pragma unroll
-    for (int t = 0; t < NW; ++t)
+      for (int t = 0; t < NW; ++t)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {  // chunk 2h + q of row r32
-        const u32x4 v = w_s[(wn * NW + t) * 128 + r32 * 4 + ((2 * h + q) ^ ((r32 >> 2) & 3))];
-        const float ps = p2[GATEUP ? t : 0];
-        b[t][2 * q] = e4m3x8_scaled_to_bf16(v.x, v.y, ps);
-        b[t][2 * q + 1] = e4m3x8_scaled_to_bf16(v.z, v.w, ps);
+        for (int q = 0; q < 2; ++q) {  // chunk 2h + q of row r32
+          const u32x4 v = w_s[(wn * NW + t) * 128 + r32 * 4 + ((2 * h + q) ^ ((r32 >> 2) & 3))];
+          const float ps = p2[GATEUP ? t : 0];
+          b[t][2 * q] = e4m3x8_scaled_to_bf16(v.x, v.y, ps);
+          b[t][2 * q + 1] = e4m3x8_scaled_to_bf16(v.z, v.w, ps);
+        }
+    } else {
+      const bool ktail = ks * BK + 32 * h >= K;  // this lane's inputs lie past K
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        u32x4 v = w_s[(wn * NW + t) * 64 + r32 * 2 + (h ^ ((r32 >> 3) & 1))];
+        if (ktail) v = u32x4{0u, 0u, 0u, 0u};
+        const uint32_t sb = sS(slot)[(wn * NW + t) * 64 + lane];
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if constexpr (FMT == FMT_NVFP4)
+            b[t][q] = nvfp4x8_to_bf16(wd[q], e4m3_to_f32(q < 2 ? (sb & 0xFF) : (sb >> 8)));
+          else
+            b[t][q] = e2m1x8_to_bf16(wd[q], ue8m0_to_f32(sb));
+        }
       }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i >= nact) break;  // uniform
@@ -996,8 +1077,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     }
   };
 
-  // NS slots, NS - 1 stages in flight: at stage ks wait for its loads (the
-  // next stage may stay outstanding), one barrier (its bytes visible to every
+  // NS slots, NS - 1 stages in flight: at stage ks wait for its loads (later
+  // stages may stay outstanding), one barrier (its bytes visible to every
   // wavefront; the slot of stage ks - 1 free), issue stage ks + NS - 1 into
   // that slot, compute stage ks.  Past the last issue the waits drain all.
   constexpr int LD = C::LOADS;

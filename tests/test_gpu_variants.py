@@ -1,6 +1,7 @@
 """GPU parity of the expert-stage kernels that the default dispatch does not
-pick for these shapes but that a plan can be switched to (MOE_GEMM for the
-grouped path, MOE_DEC_KERNEL / MOE_DEC_MFMA_MIN_T for the decode path): each
+pick for these shapes but that a plan can be switched to (MOE_GEMM and
+MOE_BIG_CFG for the grouped path, MOE_DEC_KERNEL / MOE_DEC_MFMA_MIN_T for the
+decode path): each
 one against the CPU oracle with the same bars as the default path.  The
 shapes carry the tails the kernels guard: K = 160 (an fp4 k-tail of 32
 inputs against 64-input stages), N = 96 and 384 (partial 128- and 256-row
@@ -99,3 +100,19 @@ def test_decode_mfma_one_token(fmt):
     batch = synth.make_batch(wl, layer, 1)
     ref = oracle_run(wl, layer, batch)
     check_all(run_with_env({"MOE_DEC_MFMA_MIN_T": "1"}, wl, W, batch, DECODE), ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
+@pytest.mark.parametrize("cfg", ["11", "12", "22", "23", "24"])
+def test_big_tile_shapes(fmt, cfg):
+    """Every tile shape of the default grouped kernel (MOE_GEMM=3): 32 x 256,
+    64 x 256, 128 x 128, 192 x 128 and 256 x 128 tokens x rows per matrix, on
+    the one-expert batch (one expert spans several tiles of the small shapes)."""
+    wl, layer, W = get(fmt)
+    T = 150
+    batch = synth.make_batch(wl, layer, T)
+    bias = np.zeros((T, wl.E), np.float32)
+    bias[:, 1] = 100.0
+    batch = synth.Batch(batch.x, bias)
+    ref = oracle_run(wl, layer, batch)
+    check_all(run_with_env({"MOE_GEMM": "3", "MOE_BIG_CFG": cfg}, wl, W, batch, GROUPED), ref)
