@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ 
 // in f32).  A bf16 activation times a bf16 value is exact in f32, so three
 // v_mfma_f32_32x32x16_bf16 per 16-deep slice give x.w with only the f32
 // accumulation rounding of an f32 dot product.  4 wavefronts in a 2x2 grid
-// own 32x32 patches; K advances 32 per LDS stage within this block's slice.
+// own 32x32 patches; K advances 64 per LDS stage within this block's slice.
 __device__ __forceinline__ void split3_bf16(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
   const uint32_t u = __float_as_uint(w);
   const float fh = __uint_as_float(u & 0xFFFF0000u);
@@ -90,42 +90,63 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
                                                    const float* __restrict__ wr,
                                                    float* __restrict__ part, int T, int d, int E,
                                                    int slice) {
-  constexpr int BK = 32, LDK = BK + 8;
+  // 64-deep LDS stages; the global loads of the next D - 1 stages are in
+  // flight in registers while a stage is split and multiplied
+  constexpr int BK = 64, LDK = BK + 8, D = 4;
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t ws[3][64 * LDK];
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
   const int k0 = blockIdx.z * slice, k1 = min(d, k0 + slice);
   const int wm0 = (wv >> 1) * 32, wn0 = (wv & 1) * 32;
-  f32x16 acc;
+  const int nit = (k1 - k0 + BK - 1) / BK;
+  u32x4 rx[D][2];  // activations: 64 rows x 64 bf16 = 512 16-byte chunks, 2 per thread
+  f32x4 rw[D][4];  // router rows: 64 x 64 f32 = 1024 16-byte chunks, 4 per thread
+  auto load = [&](int it, int set) {
+    const int k = k0 + it * BK;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int k = k0; k < k1; k += BK) {
-    {  // activations: 64 rows x 32 bf16, one 16-byte chunk per thread
-      const int r = tid >> 2, c = (tid & 3) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t0 + r < T) v = *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * d + k + c);
-      *reinterpret_cast<u32x4*>(xs + r * LDK + c) = v;
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
+      rx[set][i] = t0 + r < T && k + col < k1
+                       ? *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * d + k + col)
+                       : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // router rows: 64 x 32 f32, split into hi / mid / lo
-      const int q = tid + 256 * i;
-      const int r = q >> 3, c = (q & 7) * 4;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (e0 + r < E) v = *reinterpret_cast<const f32x4*>(wr + (size_t)(e0 + r) * d + k + c);
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c >> 4, col = (c & 15) * 4;
+      rw[set][i] = e0 + r < E && k + col < k1
+                       ? *reinterpret_cast<const f32x4*>(wr + (size_t)(e0 + r) * d + k + col)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // the stage's bytes into LDS, each router weight split into hi / mid / lo
+  auto store = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<u32x4*>(xs + r * LDK + col) = rx[set][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c >> 4, col = (c & 15) * 4;
+      const f32x4 v = rw[set][i];
       uint16_t h[4], m[4], l[4];
       split3_bf16(v.x, h[0], m[0], l[0]);
       split3_bf16(v.y, h[1], m[1], l[1]);
       split3_bf16(v.z, h[2], m[2], l[2]);
       split3_bf16(v.w, h[3], m[3], l[3]);
-      *reinterpret_cast<u32x2*>(ws[0] + r * LDK + c) =
+      *reinterpret_cast<u32x2*>(ws[0] + r * LDK + col) =
           u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
-      *reinterpret_cast<u32x2*>(ws[1] + r * LDK + c) =
+      *reinterpret_cast<u32x2*>(ws[1] + r * LDK + col) =
           u32x2{(uint32_t)m[0] | ((uint32_t)m[1] << 16), (uint32_t)m[2] | ((uint32_t)m[3] << 16)};
-      *reinterpret_cast<u32x2*>(ws[2] + r * LDK + c) =
+      *reinterpret_cast<u32x2*>(ws[2] + r * LDK + col) =
           u32x2{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
     }
-    __syncthreads();
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  auto compute = [&]() {
     const int r = lane & 31, kh = (lane >> 5) * 8;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
@@ -136,7 +157,21 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+#pragma unroll
+  for (int p = 0; p < D - 1; ++p)
+    if (p < nit) load(p, p);
+  for (int it0 = 0; it0 < nit; it0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int it = it0 + j;
+      if (it >= nit) break;
+      if (it + D - 1 < nit) load(it + D - 1, (j + D - 1) % D);
+      __syncthreads();  // the previous stage's MFMAs are done with LDS
+      store(j);
+      __syncthreads();
+      compute();
+    }
   }
   float* out = part + (size_t)blockIdx.z * T * E;
 #pragma unroll
