@@ -920,6 +920,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     asrc[i] = act + src * K;
     achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
   }
+  // activation loads of this wavefront that hold rows of the tile (its first
+  // n_a; a load of 8 rows all past `rows` is skipped: the MFMAs of rows past
+  // `rows` only reach outputs that are not stored, so their LDS bytes may be
+  // stale)
+  int n_a = 0;
+#pragma unroll
+  for (int i = 0; i < AL; ++i) n_a += (((AL * w + i) * 8) % BM) < rows ? 1 : 0;
   // the weight tiles this wavefront loads: WGM = 2: tile wm of its column
   // (the other wavefront of the column loads the other); WGM = 1: both.  Tile
   // t is matrix t for gate/up, rows 32 t .. of the column for down; rows are
@@ -977,7 +984,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     const int k0 = kk * BK;
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      lds_dma16(asrc[i] + min(k0 + 8 * achunk[i], K - 8), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
+      if (i < n_a)
+        lds_dma16(asrc[i] + min(k0 + 8 * achunk[i], K - 8), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tl = tls[u];
@@ -1081,7 +1089,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   // stages may stay outstanding), one barrier (its bytes visible to every
   // wavefront; the slot of stage ks - 1 free), issue stage ks + NS - 1 into
   // that slot, compute stage ks.  Past the last issue the waits drain all.
-  constexpr int LD = C::LOADS;
+  // loads per lane and stage of this wavefront: LD minus its skipped activation loads
+  constexpr int LDW = C::LOADS - AL;
+  auto wait_stage = [&]() {  // all but the NS - 2 most recent stages' loads done
+    switch (n_a) {
+      case 0: wait_vm<(NS - 2) * LDW>(); break;
+      case 1: wait_vm<(NS - 2) * (LDW + 1)>(); break;
+      case 2: wait_vm<(NS - 2) * (LDW + (AL >= 2 ? 2 : 1))>(); break;
+      case 3: wait_vm<(NS - 2) * (LDW + (AL >= 3 ? 3 : 1))>(); break;
+      default: wait_vm<(NS - 2) * (LDW + AL)>(); break;
+    }
+  };
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < nk) issue(p, p);
@@ -1091,7 +1109,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
       const int ks = ks0 + j;
       if (ks >= nk) break;
       if (ks + NS - 2 < nk)
-        wait_vm<(NS - 2) * LD>();
+        wait_stage();
       else
         wait_vm<0>();
       stage_barrier();
