@@ -197,10 +197,12 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 }
 
 // One wavefront per token.  Lane l holds the logits of experts l, l+64, ...
-// (the K-slice partials summed in slice order, then the bias added).  The
-// k experts are taken one at a time: each round takes the largest remaining
-// logit (by its order key), and of equal logits the lowest expert index, so
-// the k taken are the k largest with ties going to the lower index.  Each
+// (the K-slice partials summed in slice order, then the bias added).  Up to
+// 128 experts the k-th largest order key is found by a radix select; above,
+// the k experts are taken one at a time, each round taking the largest
+// remaining logit (by its order key) and of equal logits the lowest expert
+// index.  Either way the k taken are the k largest with ties going to the
+// lower index.  Each
 // selected expert's place in ascending id order comes from the ballot masks;
 // its weight is its softmax probability over all E experts (max-subtracted),
 // divided by the sum over the k when `renorm`.
@@ -220,8 +222,9 @@ __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part
     valid[i] = e < E;
     col[i] = (size_t)t * E + min(e, E - 1);
   }
-  // every load of a group of four slices (clamped index) is issued before
-  // the in-order sum; the bias (or a dummy read) goes with the first group
+  // every load of a group of SG slices (clamped index) is issued before the
+  // in-order sum; the bias (or a dummy read) goes with the first group
+  constexpr int SG = NG <= 2 ? 8 : 4;
   const float* bp = bias ? bias : part;
   float bv[NG], v[NG];
 #pragma unroll
@@ -229,14 +232,14 @@ __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part
     bv[i] = bp[col[i]];
     v[i] = 0.0f;
   }
-  for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    float ps[4][NG];
+  for (int s0 = 0; s0 < nsplit; s0 += SG) {
+    float ps[SG][NG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < SG; ++j)
 #pragma unroll
       for (int i = 0; i < NG; ++i) ps[j][i] = part[(size_t)min(s0 + j, nsplit - 1) * TE + col[i]];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < SG; ++j)
 #pragma unroll
       for (int i = 0; i < NG; ++i)
         v[i] = s0 + j >= nsplit ? v[i] : (s0 + j == 0 ? ps[j][i] : v[i] + ps[j][i]);
@@ -254,23 +257,49 @@ __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part
   bool take[NG];
 #pragma unroll
   for (int i = 0; i < NG; ++i) take[i] = false;
-  for (int j = 0; j < k; ++j) {  // k <= E, so every round finds a key >= 1
-    uint32_t lm = kv[0];
+  if constexpr (NG <= 2) {
+    // up to 128 experts: radix select (cheaper than k rounds at one or two
+    // keys per lane): 32 ballot rounds build the k-th largest key thr (the
+    // largest value with at least k keys >= it); every key above thr is
+    // taken, and of those equal to thr the lowest indices fill the rest.
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int n = 0;
 #pragma unroll
-    for (int i = 1; i < NG; ++i) lm = kv[i] > lm ? kv[i] : lm;
-    const uint32_t mx = wave_max_u32(lm);
-    int sel = 0;
-#pragma unroll
-    for (int i = NG - 1; i >= 0; --i) {  // the lowest index holding mx wins
-      const uint64_t b = __ballot(kv[i] == mx);
-      if (b) sel = WAVE * i + (int)__builtin_ctzll(b);
+      for (int i = 0; i < NG; ++i) n += __popcll(__ballot(kv[i] >= cand));
+      if (n >= k) thr = cand;
     }
+    int above = 0;
 #pragma unroll
-    for (int i = 0; i < NG; ++i)
-      if (lane + WAVE * i == sel) {
-        kv[i] = 0u;
-        take[i] = true;
+    for (int i = 0; i < NG; ++i) above += __popcll(__ballot(kv[i] > thr));
+    const int need = k - above;  // places left for keys equal to thr (>= 1: past E never ties)
+    int ties_before = 0;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const uint64_t tie = __ballot(kv[i] == thr);
+      take[i] = kv[i] > thr || (kv[i] == thr && ties_before + __popcll(tie & below) < need);
+      ties_before += __popcll(tie);
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {  // k <= E, so every round finds a key >= 1
+      uint32_t lm = kv[0];
+#pragma unroll
+      for (int i = 1; i < NG; ++i) lm = kv[i] > lm ? kv[i] : lm;
+      const uint32_t mx = wave_max_u32(lm);
+      int sel = 0;
+#pragma unroll
+      for (int i = NG - 1; i >= 0; --i) {  // the lowest index holding mx wins
+        const uint64_t b = __ballot(kv[i] == mx);
+        if (b) sel = WAVE * i + (int)__builtin_ctzll(b);
       }
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        if (lane + WAVE * i == sel) {
+          kv[i] = 0u;
+          take[i] = true;
+        }
+    }
   }
   int pos[NG];
   int sel_before = 0;
@@ -463,22 +492,26 @@ __global__ __launch_bounds__(1024) void route_small(
   const int e = tid;
   const int c_e = e < E ? __popcll(mask[e]) : 0;
   if (e < E) counts[e] = c_e;
+  // one scan of three 10-bit fields: slots (offsets), selected experts
+  // (record index), tiles (tile-list index).  Each partial sum is at most
+  // T*k <= 256 (c_e <= T <= 16 and BM >= 16, so an expert has at most one
+  // tile), so no field carries into the next.
+  const int mt = (e < E) ? (c_e + BM - 1) / BM : 0;
   int tot;
-  const int off = block_exclusive_scan(e < E ? c_e : 0, &tot);
+  const int packed = block_exclusive_scan(c_e | ((c_e > 0 ? 1 : 0) << 10) | (mt << 20), &tot);
+  const int off = packed & 1023, act = (packed >> 10) & 1023, tb = packed >> 20;
   if (e < E) {
     offsets[e] = off;
     off_s[e] = off;
   }
   const int S = T * k;
   if (e == 0) offsets[E] = S;
-  const int act = block_exclusive_scan((e < E && c_e > 0) ? 1 : 0, &tot);
   if (e < E && c_e > 0) slot_info[act] = make_int4(e, off, c_e, 0);
-  if (e == 0) *n_active = tot;
-  for (int i = tot + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
-  const int mt = (e < E) ? (c_e + BM - 1) / BM : 0;
-  const int tb = block_exclusive_scan(mt, &tot);
+  const int n_act = (tot >> 10) & 1023;
+  if (e == 0) *n_active = n_act;
+  for (int i = n_act + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
   for (int i = 0; i < mt; ++i) tiles[tb + i] = make_int4(e, off + i * BM, min(BM, c_e - i * BM), 0);
-  if (e == 0) *n_tiles = tot;
+  if (e == 0) *n_tiles = tot >> 20;
   __syncthreads();
   for (int s = tid; s < S; s += 1024) {
     const int t = s / k;
