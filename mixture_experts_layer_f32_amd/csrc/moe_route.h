@@ -421,9 +421,17 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   const int e = threadIdx.x;
   int c_e = 0;
   if (e < E) {
-    for (int c = 0; c < nchunk; ++c) {
-      base[(size_t)c * E + e] = c_e;
-      c_e += hist[(size_t)c * E + e];
+    // eight chunks' histogram loads in flight, then their running sums
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+      int hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = c0 + j < nchunk ? hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < nchunk) {
+          base[(size_t)(c0 + j) * E + e] = c_e;
+          c_e += hv[j];
+        }
     }
     counts[e] = c_e;
   }
