@@ -416,13 +416,21 @@ __global__ __launch_bounds__(256) void dec_down_persist(
 // For e4m3 and a 128-input block starting at k0 it supplies, to MFMA a = 0..3,
 // the 8 inputs k0 + 16q + 8a (a < 2) or k0 + 64 + 16q + 8(a - 2) (two 16-byte
 // loads per row and lane); for e2m1 and 256 inputs from k0, to MFMA 4h + a,
-// the inputs k0 + 128h + 32q + 8a (two 16-byte loads); token
+// the inputs k0 + 64q + 32h + 8a (two adjacent 16-byte loads); token
 // column (l & 15) takes the activations of the same inputs, so every MFMA sums
 // products of matching (row, input) and (input, token) pairs.  e4m3: the four
 // MFMAs of a block start from zero and their sum is multiplied by the block's
 // scale and added to the running f32 sum (one f32 accumulation per 128 x 128
 // scale block); e2m1: the ue8m0 scale of the lane's 32-input group is applied
-// exactly inside the conversion.
+// exactly inside the conversion (nvfp4: the e4m3 scales of its two 16-input
+// halves, in f32).
+//
+// e2m1/nvfp4 group scales: a unit needs 8 (nvfp4: 16) scale bytes per row,
+// and a per-lane byte load for each would cost as much load issue as the
+// weights themselves.  Instead, every fourth unit of a tile each lane loads
+// the whole scale run of one of the next four units (lane q: unit j + q) with
+// one wide load, the wavefront parks them in its own LDS rows, and each unit
+// reads its lane's 2 (nvfp4: 4) bytes back with one LDS read per row group.
 //
 // Persistent grid: workgroup b takes tiles b, b + G, b + 2G, ... (so the tiles
 // in flight at any time are neighbours in HBM); its KS wavefronts split each
@@ -466,14 +474,45 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 // One unit = one (tile, k-range) step of a wavefront: per matrix and 16-row
 // group, two 16-byte weight loads per lane (e4m3: 128 inputs, one scale
-// block; e2m1: 256 inputs, the lane's two 32-input groups at k0 + 32q and
-// k0 + 128 + 32q), and the activations of those inputs, shared by all of the
-// unit's row groups and matrices.
+// block; e2m1: 256 inputs, the lane's two 32-input groups at k0 + 64q and
+// k0 + 64q + 32), and the activations of those inputs, shared by all of the
+// unit's row groups and matrices.  e2m1/nvfp4: g holds, on units j = 0 mod 4
+// of a tile, the scale run of unit j + q of the lane's row.
 template <int FMT> struct DecUnitW;
 template <> struct DecUnitW<FMT_E4M3> { u32x4 w[2]; };
-template <> struct DecUnitW<FMT_E2M1> { u32x4 w[2]; uint32_t sb[2]; };
-// NVFP4: sb[h] holds the two e4m3 scale bytes of the load's two 16-input groups
-template <> struct DecUnitW<FMT_NVFP4> { u32x4 w[2]; uint32_t sb[2]; };
+template <> struct DecUnitW<FMT_E2M1> { u32x4 w[2]; u32x2 g; };
+template <> struct DecUnitW<FMT_NVFP4> { u32x4 w[2]; u32x4 g; };
+// Scale bytes per row and unit, and the LDS row stride that parks four units'
+// runs (strides 40 and 80 put the 16 rows' reads of one unit in distinct banks).
+template <int FMT> constexpr int dec_run_bytes() { return FMT == FMT_NVFP4 ? 16 : 8; }
+template <int FMT> constexpr int dec_run_stride() { return FMT == FMT_NVFP4 ? 80 : 40; }
+
+// The scale run of one unit of row n: bytes [off, off + SB) of the row's
+// scales, of which `avail` lie inside the row (fewer than SB only on the last
+// unit of a row whose K is not a multiple of 256: the rest read as zero).
+// Wide loads need no alignment on gfx950 (unaligned buffer access).
+template <int FMT>
+__device__ __forceinline__ decltype(DecUnitW<FMT>::g) load_scale_run(__amdgpu_buffer_rsrc_t sr, bool in,
+                                                                     uint32_t off, int avail) {
+  constexpr int SB = dec_run_bytes<FMT>();
+  if (avail >= SB || !in) {
+    const uint32_t o = in ? off : BUF_OOB;
+    if constexpr (FMT == FMT_NVFP4)
+      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, 0));
+    else
+      return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sr, o, 0, 0));
+  }
+  uint32_t v[SB / 4];
+#pragma unroll
+  for (int i = 0; i < SB / 4; ++i) v[i] = 0;
+#pragma unroll
+  for (int i = 0; i < SB; ++i)
+    v[i >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, i < avail ? off + i : BUF_OOB, 0, 0) << (8 * (i & 3));
+  if constexpr (FMT == FMT_NVFP4)
+    return u32x4{v[0], v[1], v[2], v[3]};
+  else
+    return u32x2{v[0], v[1]};
+}
 template <int FMT> constexpr int dec_unit_k() { return FMT == FMT_E4M3 ? 128 : 256; }
 template <int FMT> constexpr int dec_unit_x() { return FMT == FMT_E4M3 ? 4 : 8; }
 
@@ -489,7 +528,10 @@ __global__ __launch_bounds__(256) void dec_mfma(
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int KU = dec_unit_k<FMT>(), NX = dec_unit_x<FMT>();
   constexpr int TR = 16 * RT;  // rows per tile
+  constexpr int RS = dec_run_stride<FMT>(), SB = dec_run_bytes<FMT>();
   __shared__ f32x4 red[2][3][NM * RT][WAVE];
+  // per wavefront: NM * RT row groups x 16 rows x RS bytes of parked scale runs
+  __shared__ __attribute__((aligned(16))) uint8_t runs[FMT == FMT_E4M3 ? 16 : 4 * NM * RT * 16 * RS];
   const int KS = blockDim.x / WAVE;
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int r = lane & 15, q = lane >> 4;
@@ -514,7 +556,8 @@ __global__ __launch_bounds__(256) void dec_mfma(
   };
   auto issue = [&](Unit& s, int u) {
     const int jt = u / nu;
-    const int kb = w + KS * (u - jt * nu);
+    const int j = u - jt * nu;
+    const int kb = w + KS * j;
     const int tile = b + jt * G;
     const int ti = tile / tpe, n0 = (tile - ti * tpe) * TR;
     const int4 info = tiles[ti];
@@ -534,21 +577,18 @@ __global__ __launch_bounds__(256) void dec_mfma(
         s.sc[m] = reinterpret_cast<const float*>(M[m].s + e * M[m].ss)[(n0 >> 7) * (K >> 7) + kb];
       } else {
         const __amdgpu_buffer_rsrc_t sr = buf_rsrc(M[m].s + e * M[m].ss, s_bytes);
+        const int run0 = SB * (w + KS * (j + q));  // lane's scale run: unit j + q
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int n = n0 + 16 * t + r;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int k = k0 + 128 * h + 32 * q;
-            const bool in = n < N && k < K;
-            s.wv[m][t].w[h] = buf_load16(wr, in ? (uint32_t)n * rb + k / 2 : BUF_OOB, 0);
-            if constexpr (FMT == FMT_NVFP4)  // the two adjacent group scales (2-byte aligned)
-              s.wv[m][t].sb[h] = __builtin_amdgcn_raw_buffer_load_b16(
-                  sr, in ? (uint32_t)n * sgroups + (k >> 4) : BUF_OOB, 0, 0);
-            else
-              s.wv[m][t].sb[h] = __builtin_amdgcn_raw_buffer_load_b8(
-                  sr, in ? (uint32_t)n * sgroups + (k >> 5) : BUF_OOB, 0, 0);
+            const bool in = n < N && k0 + 64 * q + 32 * h < K;
+            s.wv[m][t].w[h] = buf_load16(wr, in ? (uint32_t)n * rb + k0 / 2 + 32 * q + 16 * h : BUF_OOB, 0);
           }
+          if ((j & 3) == 0)
+            s.wv[m][t].g = load_scale_run<FMT>(sr, n < N && j + q < nu, (uint32_t)n * sgroups + run0,
+                                                (int)sgroups - run0);
         }
         s.sc[m] = 0.0f;
       }
@@ -575,7 +615,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int k = k0 + 128 * h + 32 * q;
+        const int k = k0 + 64 * q + 32 * h;
         const uint32_t off = r < cnt && k < K ? (row * K + k) * 2 : BUF_OOB;
 #pragma unroll
         for (int a = 0; a < 4; ++a) s.x[4 * h + a] = buf_load16(ar, off, 16 * a);
@@ -587,7 +627,30 @@ __global__ __launch_bounds__(256) void dec_mfma(
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Unit& s) {
+  auto compute = [&](const Unit& s, int u) {
+    // e2m1/nvfp4: park the runs of units j..j+3 (on j = 0 mod 4; the wavefront's
+    // own LDS rows, so program order orders the write before the reads), then
+    // read this unit's bytes: e2m1 byte h = scale of chunk h; nvfp4 bytes
+    // 2h, 2h + 1 = scales of chunk h's two halves
+    uint32_t sv[NM][RT];
+    if constexpr (FMT != FMT_E4M3) {
+      const int j = u - (u / nu) * nu;
+      uint8_t* const base = runs + w * (NM * RT * 16 * RS);
+      if ((j & 3) == 0) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            *reinterpret_cast<decltype(DecUnitW<FMT>::g)*>(base + ((m * RT + t) * 16 + r) * RS + SB * q) = s.wv[m][t].g;
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const uint8_t* pr = base + ((m * RT + t) * 16 + r) * RS + SB * (j & 3) + (SB / 4) * q;
+          sv[m][t] = FMT == FMT_NVFP4 ? *reinterpret_cast<const uint32_t*>(pr) : *reinterpret_cast<const uint16_t*>(pr);
+        }
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -608,13 +671,13 @@ __global__ __launch_bounds__(256) void dec_mfma(
             const u32x4 v = wq.w[h];
             bf16x8 a0, a1, a2, a3;
             if constexpr (FMT == FMT_NVFP4) {  // words x, y: first 16-input group; z, w: second
-              const float s0 = e4m3_to_f32(wq.sb[h] & 0xFF), s1 = e4m3_to_f32(wq.sb[h] >> 8);
-              a0 = nvfp4x8_to_bf16(v.x, s0);
-              a1 = nvfp4x8_to_bf16(v.y, s0);
-              a2 = nvfp4x8_to_bf16(v.z, s1);
-              a3 = nvfp4x8_to_bf16(v.w, s1);
+              const f32x2 s01 = h ? __builtin_amdgcn_cvt_pk_f32_fp8(sv[m][t], true) : __builtin_amdgcn_cvt_pk_f32_fp8(sv[m][t], false);
+              a0 = nvfp4x8_to_bf16(v.x, s01.x);
+              a1 = nvfp4x8_to_bf16(v.y, s01.x);
+              a2 = nvfp4x8_to_bf16(v.z, s01.y);
+              a3 = nvfp4x8_to_bf16(v.w, s01.y);
             } else {
-              const float sc = ue8m0_to_f32(wq.sb[h]);
+              const float sc = ue8m0_to_f32((sv[m][t] >> (8 * h)) & 0xFFu);
               a0 = e2m1x8_to_bf16(v.x, sc);
               a1 = e2m1x8_to_bf16(v.y, sc);
               a2 = e2m1x8_to_bf16(v.z, sc);
@@ -687,7 +750,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
       if (u0 + s + D - 1 < units) issue(st[(s + D - 1) % D], u0 + s + D - 1);
       const int u = u0 + s;
       if (u < units) {
-        compute(st[s]);
+        compute(st[s], u);
         const int jt = u / nu;
         if (u - jt * nu == nu - 1) finish(jt);
       }

@@ -179,6 +179,44 @@ def test_nvfp4_scale_alignment():
     assert torch.all(outs["out"] == 7.0)
 
 
+WL4W = synth.Workload("edge-e2m1-wide", 512, 288, 8, 2, "e2m1", False, (9,), False, 4004)
+WLNW = synth.Workload("edge-nvfp4-wide", 512, 288, 8, 2, "nvfp4", False, (9,), False, 4005)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("wl", [WL4W, WLNW], ids=lambda w: w.name)
+def test_fp4_scales_at_unaligned_addresses(wl, path):
+    """Group scales read as whole runs of a row: scale buffers moved to the
+    smallest alignment the format allows (e2m1: 1 byte, nvfp4: 2 bytes, both
+    for the pointer and the expert stride) give the same bits.  d = 512 takes
+    full 256-input steps, f = 288 a ragged last one."""
+    import torch
+    import mixture_experts_layer_f32_amd as m
+    from mixture_experts_layer_f32_amd.device import to_dev
+    L, W = get(wl)
+    T = 9
+    batch = synth.make_batch(wl, L, T)
+    a, _ = gpu_run(wl, W, batch, path)
+    step = 1 if wl.fmt == "e2m1" else 2
+    moved = []
+    for q, sc in ((L.gate.q, L.gate.s), (L.up.q, L.up.s), (L.down.q, L.down.s)):
+        per = sc[0].nbytes
+        stride = per + step
+        buf = np.zeros(step + wl.E * stride, np.uint8)
+        for e in range(wl.E):
+            buf[step + e * stride:step + e * stride + per] = sc[e].reshape(-1).view(np.uint8)
+        dq, ds = to_dev(q), to_dev(buf)
+        moved.append((dq, ds, m.moe_mat(dq.data_ptr(), ds.data_ptr() + step, q[0].nbytes, stride)))
+    run = runner(wl, T, path)
+    outs = run.outputs(T)
+    m.moe_forward(run.plan, T, to_dev(batch.x), W.w_router, None, moved[0][2], moved[1][2],
+                  moved[2][2], outs["out"], workspace=run.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(outs["out"].cpu().numpy().view(np.uint32), a["out"].view(np.uint32))
+    ref = oracle_run(wl, L, batch)
+    check_out(a["out"], ref.out)
+
+
 def test_nonfinite_input_row_does_not_fault():
     """A NaN activation row is outside the contract: the call must still
     complete, and the other tokens' outputs are unaffected."""
