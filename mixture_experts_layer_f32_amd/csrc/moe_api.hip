@@ -381,10 +381,10 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
       const int g3 = p->cus * 12 / ks, g2 = p->cus * 8 / ks;
       // e2m1: an input byte holds two weights, so the activation operand
       // outweighs the weights once the tiles' token columns fill; taller tiles
-      // then share it over more rows (measured: faster at 16 slots per expert,
+      // then share it over more rows (measured: faster at 8 slots per expert,
       // slower at 4)
       bool tall = big(gateup ? f : d, gateup ? 32 : 64) &&
-                  (FMT == FMT_E4M3 || S >= 16LL * p->d.n_experts);
+                  (FMT == FMT_E4M3 || S >= 8LL * p->d.n_experts);
       if (p->dec_tall >= 0) tall = p->dec_tall == 1;
       if (gateup) {
         if (tall)

@@ -414,8 +414,9 @@ __global__ __launch_bounds__(256) void dec_down_persist(
 //
 // Lane l of a wavefront owns weight row n0 + (l & 15) and k-slot q = l >> 4.
 // For e4m3 and a 128-input block starting at k0 it supplies, to MFMA a = 0..3,
-// the 8 inputs k0 + 16q + 8a (a < 2) or k0 + 64 + 16q + 8(a - 2) (two 16-byte
-// loads per row and lane); for e2m1 and 256 inputs from k0, to MFMA 4h + a,
+// the 8 inputs k0 + 32q + 8a (two adjacent 16-byte loads per row and lane:
+// each load then spans the row's whole 128-byte run, which streams faster
+// than two half runs); for e2m1 and 256 inputs from k0, to MFMA 4h + a,
 // the inputs k0 + 64q + 32h + 8a (two adjacent 16-byte loads); token
 // column (l & 15) takes the activations of the same inputs, so every MFMA sums
 // products of matching (row, input) and (input, token) pairs.  e4m3: the four
@@ -570,9 +571,9 @@ __global__ __launch_bounds__(256) void dec_mfma(
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int n = n0 + 16 * t + r;
-          const uint32_t off = n < N ? (uint32_t)n * rb + k0 + 16 * q : BUF_OOB;
+          const uint32_t off = n < N ? (uint32_t)n * rb + k0 + 32 * q : BUF_OOB;
           s.wv[m][t].w[0] = buf_load16(wr, off, 0);
-          s.wv[m][t].w[1] = buf_load16(wr, off, 64);
+          s.wv[m][t].w[1] = buf_load16(wr, off, 16);
         }
         s.sc[m] = reinterpret_cast<const float*>(M[m].s + e * M[m].ss)[(n0 >> 7) * (K >> 7) + kb];
       } else {
@@ -607,11 +608,11 @@ __global__ __launch_bounds__(256) void dec_mfma(
       row = min((uint32_t)t, (uint32_t)(T - 1));
     }
     if constexpr (FMT == FMT_E4M3) {
-      const uint32_t off = r < cnt ? (row * K + k0 + 16 * q) * 2 : BUF_OOB;
+      const uint32_t off = r < cnt ? (row * K + k0 + 32 * q) * 2 : BUF_OOB;
       s.x[0] = buf_load16(ar, off, 0);
       s.x[1] = buf_load16(ar, off, 16);
-      s.x[2] = buf_load16(ar, off, 128);
-      s.x[3] = buf_load16(ar, off, 144);
+      s.x[2] = buf_load16(ar, off, 32);
+      s.x[3] = buf_load16(ar, off, 48);
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
