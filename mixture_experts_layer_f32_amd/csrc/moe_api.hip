@@ -810,8 +810,18 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
 
   // a6: fixed-order combine
   mark(p, MOE_STAGE_COMBINE, false, s);
-  combine_fixed_order<<<dim3(T, (d / 4 + 255) / 256), 256, 0, s>>>(
-      reinterpret_cast<const float*>(ws + L.y), w, inv, out, d, k);
+  {
+    const dim3 g(T, (d / 4 + 255) / 256);
+    const float* y = reinterpret_cast<const float*>(ws + L.y);
+    switch (k) {
+#define MOE_COMBINE(KM) \
+  case KM: combine_fixed_order<KM><<<g, 256, 0, s>>>(y, w, inv, out, d); break;
+      MOE_COMBINE(1) MOE_COMBINE(2) MOE_COMBINE(3) MOE_COMBINE(4) MOE_COMBINE(5) MOE_COMBINE(6)
+      MOE_COMBINE(7) MOE_COMBINE(8) MOE_COMBINE(9) MOE_COMBINE(10) MOE_COMBINE(11) MOE_COMBINE(12)
+      MOE_COMBINE(13) MOE_COMBINE(14) MOE_COMBINE(15) default: MOE_COMBINE(16)
+#undef MOE_COMBINE
+    }
+  }
   mark(p, MOE_STAGE_COMBINE, true, s);
   if (p->timing_mask && p->timing_n < p->timing_max) ++p->timing_n;
   err = hipGetLastError();

@@ -770,22 +770,35 @@ __global__ __launch_bounds__(256) void dec_mfma(
 // out[t][m] = sum over j ascending of w[t][j] * y[inv_perm[t*k+j]][m]: a
 // gather in router order, so every output has one fixed summation order
 // (WARP BACKENDS.md, "Coherent memory": partials reduced in router order).
+// KM = k (the plan's top-k, 1..16) as a compile-time count: all k row
+// indices and weights are loaded first (uniform: scalar loads), then all k
+// rows, then summed in j order, so a thread waits two memory round trips,
+// not 2k.
+template <int KM>
 __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restrict__ y,
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ inv_perm,
-                                                           float* __restrict__ out, int d,
-                                                           int k) {
+                                                           float* __restrict__ out, int d) {
   const int t = blockIdx.x;
   const int m = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (m >= d) return;
+  int idx[KM];
+  float wv[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    idx[j] = inv_perm[(size_t)t * KM + j];
+    wv[j] = w[(size_t)t * KM + j];
+  }
+  f32x4 v[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) v[j] = *reinterpret_cast<const f32x4*>(y + (size_t)idx[j] * d + m);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(y + (size_t)inv_perm[(size_t)t * k + j] * d + m);
-    acc.x += wj * v.x;
-    acc.y += wj * v.y;
-    acc.z += wj * v.z;
-    acc.w += wj * v.w;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    acc.x += wv[j] * v[j].x;
+    acc.y += wv[j] * v[j].y;
+    acc.z += wv[j] * v[j].z;
+    acc.w += wv[j] * v[j].w;
   }
   *reinterpret_cast<f32x4*>(out + (size_t)t * d + m) = acc;
 }

@@ -210,7 +210,8 @@ template <int NG>
 __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part, int nsplit,
                                            const float* __restrict__ bias,
                                            int32_t* __restrict__ ids, float* __restrict__ w,
-                                           int T, int E, int k, int renorm) {
+                                           int T, int E, int k, int renorm,
+                                           int32_t* ids_lds = nullptr) {
   const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1ull;
   const size_t TE = (size_t)T * E;
@@ -327,6 +328,7 @@ __device__ __forceinline__ void topk_token(int t, const float* __restrict__ part
     if (take[i]) {
       const float p = ex[i] / z;
       ids[(size_t)t * k + pos[i]] = lane + WAVE * i;
+      if (ids_lds) ids_lds[t * k + pos[i]] = lane + WAVE * i;
       w[(size_t)t * k + pos[i]] = renorm ? p / ps : p;
     }
 }
@@ -490,12 +492,14 @@ __global__ __launch_bounds__(1024) void route_small(
     int renorm, int BM) {
   __shared__ unsigned long long mask[MAX_E];
   __shared__ int off_s[MAX_E];
+  __shared__ int ids_s[16 * MAX_K];  // the ids again, read back without a memory round trip
   const int tid = threadIdx.x;
-  for (int t = wave_id(); t < T; t += 16) topk_token<NG>(t, part, nsplit, bias, ids, w, T, E, k, renorm);
+  for (int t = wave_id(); t < T; t += 16)
+    topk_token<NG>(t, part, nsplit, bias, ids, w, T, E, k, renorm, ids_s);
   for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
-  __syncthreads();  // ids written by this workgroup are visible to it after the barrier
+  __syncthreads();
   if (tid < T)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[min(max(ids[tid * k + j], 0), E - 1)], 1ull << tid);
+    for (int j = 0; j < k; ++j) atomicOr(&mask[min(max(ids_s[tid * k + j], 0), E - 1)], 1ull << tid);
   __syncthreads();
   const int e = tid;
   const int c_e = e < E ? __popcll(mask[e]) : 0;
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(1024) void route_small(
   __syncthreads();
   for (int s = tid; s < S; s += 1024) {
     const int t = s / k;
-    const int ex = min(max(ids[s], 0), E - 1);
+    const int ex = min(max(ids_s[s], 0), E - 1);
     const unsigned long long below = t == 0 ? 0ull : (~0ull >> (WAVE - t));
     const int p = off_s[ex] + __popcll(mask[ex] & below);
     perm[p] = s;
