@@ -166,12 +166,37 @@ moe_status moe_timing_enable(moe_plan_t plan, uint32_t stage_mask, int32_t max_f
 /* Waits for the last recorded event, then writes for each stage the summed
  * GPU time in milliseconds over the recorded forwards (stage_ms[MOE_N_STAGES];
  * 0 for stages not in the mask, and for stages a forward runs fused with the
- * previous one: for T <= 64 the permute is part of MOE_STAGE_TOPK) and their
+ * previous one: for T <= 16 the permute is part of MOE_STAGE_TOPK) and their
  * number, and starts a new count. */
 moe_status moe_timing_collect(moe_plan_t plan, float* stage_ms, int32_t* n_forwards);
 
 /* Stops recording and destroys the events. */
 moe_status moe_timing_disable(moe_plan_t plan);
+
+/* The steps either side of the layer in a transformer block (dragon.c page,
+ * summary and "Precision": the MoE reads the normed hidden state of sub-block
+ * 0, norms run in bf16, and the MoE output is added to the residual stream,
+ * at the end of sub-block 1 in the shortcut-connected layout).  Neither call
+ * needs a plan; both are asynchronous on `stream` (NULL: the default stream)
+ * and check every argument before launching.  n_tokens = 0 returns MOE_OK.
+ *
+ * RMS normalisation of bf16 rows:
+ *   xn[t][i] = bf16_rne(x[t][i] * r_t * gamma[i]),  r_t = 1 / sqrt(mean_i x[t][i]^2 + eps),
+ * in f32 with one fixed summation order per row.
+ *   x, xn  bf16 bits [T][d], gamma bf16 bits [d], all 16-byte aligned; xn may
+ *          not overlap x.  Requires d % 8 == 0 and a finite eps >= 0. */
+moe_status moe_rmsnorm(int32_t n_tokens, int32_t d, const uint16_t* x, const uint16_t* gamma,
+                       float eps, uint16_t* xn, void* stream);
+
+/* Add of the layer output into the residual stream:
+ *   out[t][i] = bf16_rne(residual[t][i] + (a[t][i] + b[t][i]))   (b NULL: + a only)
+ * in f32, in that order.  a is the routed layer's out, b the dense (shared)
+ * branch's out: a plan with one expert and top-1 (renorm) computes that
+ * branch exactly, since its routing weight is 1.
+ *   residual, out  bf16 bits [T][d], 8-byte aligned (out may be residual);
+ *   a, b           f32 [T][d], 16-byte aligned.  Requires d % 4 == 0. */
+moe_status moe_residual_add(int32_t n_tokens, int32_t d, const uint16_t* residual, const float* a,
+                            const float* b, uint16_t* out, void* stream);
 
 void moe_plan_free(moe_plan_t plan);
 

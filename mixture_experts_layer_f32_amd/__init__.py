@@ -74,6 +74,10 @@ def _load():
     L.moe_timing_collect.restype = ctypes.c_int
     L.moe_timing_disable.argtypes = [vp]
     L.moe_timing_disable.restype = ctypes.c_int
+    L.moe_rmsnorm.argtypes = [i32, i32, vp, vp, ctypes.c_float, vp, vp]
+    L.moe_rmsnorm.restype = ctypes.c_int
+    L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+    L.moe_residual_add.restype = ctypes.c_int
     L.moe_plan_free.argtypes = [vp]
     L.moe_plan_free.restype = None
     L.moe_status_str.argtypes = [ctypes.c_int]
@@ -180,6 +184,31 @@ def moe_forward(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_ma
                          _ptr(workspace), int(workspace_bytes), stream or None)
     if st != MOE_OK:
         raise MoeError(st, "moe_forward", moe_plan_info(plan))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def moe_rmsnorm(x, gamma, eps: float, xn, stream=None) -> None:
+    """RMS normalisation of bf16 rows x [T, d] (bf16 bits) with gain gamma [d]
+    into xn [T, d]; raises MoeError on a non-OK status."""
+    T, d = x.shape
+    st = lib.moe_rmsnorm(int(T), int(d), _ptr(x), _ptr(gamma), float(eps), _ptr(xn), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_rmsnorm")
+
+
+def moe_residual_add(residual, a, b, out, stream=None) -> None:
+    """out = bf16(residual + (a + b)) over [T, d] (b may be None); raises MoeError."""
+    T, d = residual.shape
+    st = lib.moe_residual_add(int(T), int(d), _ptr(residual), _ptr(a), _ptr(b), _ptr(out),
+                              _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_residual_add")
 
 
 def moe_timing_enable(plan: Plan, stages=STAGES, max_forwards: int = 1024) -> None:

@@ -13,6 +13,7 @@
 
 #include "moe.h"
 #include "moe_common.h"
+#include "moe_block.h"
 #include "moe_decode.h"
 #include "moe_gemm.h"
 #include "moe_route.h"
@@ -595,6 +596,31 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   p->info = buf;
   *out = p;
   return MOE_OK;
+}
+
+moe_status moe_rmsnorm(int32_t n_tokens, int32_t d, const uint16_t* x, const uint16_t* gamma,
+                       float eps, uint16_t* xn, void* stream) {
+  if (n_tokens < 0 || d <= 0) return MOE_ERR_BAD_SHAPE;
+  if (d % 8 || !(eps >= 0.0f) || !(eps < INFINITY)) return MOE_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !gamma || !xn) return MOE_ERR_NULL_ARG;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(xn, 16)) return MOE_ERR_ALIGNMENT;
+  rmsnorm_bf16<<<n_tokens, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(x, gamma, eps, xn, d);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_residual_add(int32_t n_tokens, int32_t d, const uint16_t* residual, const float* a,
+                            const float* b, uint16_t* out, void* stream) {
+  if (n_tokens < 0 || d <= 0) return MOE_ERR_BAD_SHAPE;
+  if (d % 4) return MOE_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return MOE_OK;
+  if (!residual || !a || !out) return MOE_ERR_NULL_ARG;
+  if (!aligned(residual, 8) || !aligned(a, 16) || (b && !aligned(b, 16)) || !aligned(out, 8))
+    return MOE_ERR_ALIGNMENT;
+  const size_t n4 = (size_t)n_tokens * d / 4;
+  residual_add_bf16<<<(unsigned)((n4 + 255) / 256), 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      residual, a, b, out, n4);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_timing_disable(moe_plan_t p) {

@@ -49,6 +49,20 @@ layer's code, so each step states the plainest reading):
 float64 stands in for exact arithmetic everywhere except the two roundings
 the definition itself makes (f32 router logits, bf16 h) and the final f32
 output.
+
+The steps either side of the layer in a transformer block (dragon.c page,
+summary: the MoE reads sub-block 0's normed hidden state, its output is added
+to the stream at the end of sub-block 1; "Precision": norms in bf16, the dense
+per-sub-block branches quantised like the routed experts):
+
+  B1  RMS normalisation (rmsnorm): xn = bf16_rne(x / sqrt(mean(x^2) + eps) * gamma)
+      per row, x and gamma bf16, float64 inside, one rounding (reading N1: the
+      page names the norm and its bf16 precision, not its formula; this is the
+      RMSNorm form with a gain and an epsilon).
+  B2  The dense (shared) branch: one SwiGLU expert on every token with weight 1,
+      which is what moe_forward computes with E = 1 and k = 1 (reading N2).
+  B3  The add into the residual stream (residual_add):
+      out = bf16_rne(residual + (routed + dense)), float64 inside, one rounding.
 """
 from __future__ import annotations
 
@@ -277,3 +291,47 @@ def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm
         out = out + w[tok, j:j + 1] * y[sub_pos[:, j]]
     return Result(logits, ids, w, counts, offsets, perm, inv_perm, None, None,
                   out.astype(np.float32))
+
+
+# ---------------------------------------------------------------- block steps (B1-B3)
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """B1: bf16 rows x [T, d] and bf16 gain gamma [d] (bit patterns) -> bf16 bits
+    of x / sqrt(mean(x^2) + eps) * gamma, computed in float64, rounded once."""
+    xf = bf16_to_f64(x)
+    g = bf16_to_f64(gamma)
+    ms = np.mean(xf * xf, axis=1, keepdims=True)
+    return bf16_rne(xf / np.sqrt(ms + eps) * g)
+
+
+def residual_add(residual: np.ndarray, routed: np.ndarray,
+                 dense: Optional[np.ndarray] = None) -> np.ndarray:
+    """B3: bf16 bits of residual + (routed + dense) (dense may be absent),
+    float64 inside, rounded once."""
+    s = np.asarray(routed, np.float64)
+    if dense is not None:
+        s = s + np.asarray(dense, np.float64)
+    return bf16_rne(bf16_to_f64(residual) + s)
+
+
+def block_forward(x_hidden, gamma, eps, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int,
+                  renorm: bool, fmt: str, dense: Optional[Sequence[Mat]] = None,
+                  residual=None):
+    """B1 -> the layer (O1-O10) -> B2 -> B3: returns (xn bf16 bits, routed out f32,
+    dense out f32 or None, block out bf16 bits).  `dense` is (gate, up, down) of
+    the shared expert, each with a leading expert axis of 1; `residual`
+    defaults to x_hidden (the plain pre-norm block; the shortcut layout passes
+    a later point of the stream)."""
+    xn = rmsnorm(x_hidden, gamma, eps)
+    routed = moe_forward(xn, w_router, bias, gate, up, down, k, renorm, fmt).out
+    dense_out = None
+    if dense is not None:
+        dg, du, dd = dense
+        xf = bf16_to_f64(xn)
+        Wg = dequant(dg.q[0], dg.s[0], fmt, dg.K)
+        Wu = dequant(du.q[0], du.s[0], fmt, du.K)
+        Wd = dequant(dd.q[0], dd.s[0], fmt, dd.K)
+        dense_out = expert_ffn(xf, Wg, Wu, Wd)[1].astype(np.float32)
+    res = x_hidden if residual is None else residual
+    return xn, routed, dense_out, residual_add(res, routed, dense_out)

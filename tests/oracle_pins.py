@@ -284,6 +284,65 @@ def pin_token_subset(om):
     assert np.array_equal(sub.out, full.out[[3, 0]])
 
 
+# ---------------------------------------------------------------- block steps
+
+
+def _bf16(vals):
+    """bf16 bit patterns of float64 values by torch's RNE cast (a library routine)."""
+    t = torch.tensor(np.asarray(vals, np.float64)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_rmsnorm(om):
+    """RMS normalisation: a hand-worked row, the closed forms of a constant row
+    and of power-of-two rescaling, the unit mean square of the output, and the
+    gain applied per column."""
+    # x = [3, 4]: mean square 12.5, so x / sqrt(12.5) = [0.84853, 1.13137],
+    # whose bf16 roundings (7 fraction bits) are 217/256 and 145/128
+    x = _bf16([[3.0, 4.0]])
+    got = om.rmsnorm(x, _bf16([1.0, 1.0]), 0.0)
+    assert list(got[0]) == [0x3F59, 0x3F91], [hex(v) for v in got[0]]
+    assert np.array_equal(got, _bf16([[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]]))
+    # a constant row c with eps = 0 normalises to sign(c) * gamma exactly
+    rng = np.random.default_rng(11)
+    gam = _bf16(rng.uniform(0.5, 2.0, 64))
+    for c in (0.375, -3.0, 1000.0):
+        got = om.rmsnorm(_bf16(np.full((1, 64), c)), gam, 0.0)
+        want = _bf16(np.sign(c) * torch.tensor(gam.view(np.int16)).view(torch.bfloat16).double().numpy())
+        assert np.array_equal(got[0], want), c
+    # rescaling a row by 2^j leaves it unchanged (eps = 0), and the gain is
+    # applied per column: gamma = 2 on one column doubles that column exactly
+    xr = _bf16(rng.standard_normal((3, 96)))
+    one = _bf16(np.ones(96))
+    base = om.rmsnorm(xr, one, 0.0)
+    scaled = _bf16(torch.tensor(xr.view(np.int16)).view(torch.bfloat16).double().numpy() * 8.0)
+    assert np.array_equal(om.rmsnorm(scaled, one, 0.0), base)
+    g2 = np.ones(96)
+    g2[5] = 2.0
+    two = om.rmsnorm(xr, _bf16(g2), 0.0)
+    dbl = torch.tensor(base.view(np.int16)).view(torch.bfloat16).double().numpy() * 2.0
+    assert np.array_equal(two[:, 5], _bf16(dbl[:, 5]))
+    assert np.array_equal(np.delete(two, 5, axis=1), np.delete(base, 5, axis=1))
+    # unit mean square (gain 1, eps 0) up to the bf16 rounding of each entry
+    yv = torch.tensor(base.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.all(np.abs(np.mean(yv * yv, axis=1) - 1.0) < 2.0 ** -7)
+    # eps keeps a zero row at zero; with eps = mean square the scale is 1/sqrt(2)
+    assert np.all(om.rmsnorm(_bf16(np.zeros((1, 8))), _bf16(np.ones(8)), 1e-6) == 0)
+    got = om.rmsnorm(_bf16(np.full((1, 8), 2.0)), _bf16(np.ones(8)), 4.0)
+    assert np.array_equal(got[0], _bf16(np.full(8, 2.0 / math.sqrt(8.0))))
+
+
+def pin_residual_add(om):
+    """The add into the residual stream, exact on small dyadic values, one
+    rounding at the end (257.5 has no bf16 form and rounds to 258; 257 is a
+    tie and goes to the even 256), and the dense term optional."""
+    res = _bf16([[1.0, 2.0, -3.0, 256.0]])
+    a = np.array([[0.5, 0.25, 1.0, 1.0]], np.float32)
+    b = np.array([[0.25, 0.0, -1.0, 0.5]], np.float32)
+    assert np.array_equal(om.residual_add(res, a, b), _bf16([[1.75, 2.25, -3.0, 258.0]]))
+    assert np.array_equal(om.residual_add(res, a), _bf16([[1.5, 2.25, -2.0, 256.0]]))
+
+
 FAST_PINS = [
     lambda om: pin_bruteforce(om, "tiny"),
     lambda om: pin_bruteforce(om, "e4m3-nonsquare", biased=True),
@@ -291,5 +350,5 @@ FAST_PINS = [
     lambda om: pin_bruteforce(om, "nvfp4-small"),
     pin_onehot, pin_routing_closed_form, pin_router_exact, pin_topk_ties, pin_permute, pin_silu,
     pin_scale_doubling, pin_identical_experts, pin_relabel, pin_zero_input, pin_single_expert,
-    pin_lossless_grid, pin_token_subset,
+    pin_lossless_grid, pin_token_subset, pin_rmsnorm, pin_residual_add,
 ]

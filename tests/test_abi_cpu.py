@@ -64,3 +64,23 @@ def test_null_plan_queries():
     assert m.lib.moe_plan_path(None, 4) == -1
     assert m.lib.moe_plan_info(None) == b""
     m.lib.moe_plan_free(None)
+
+
+def test_block_step_argument_errors_before_launch():
+    """moe_rmsnorm / moe_residual_add check every argument before launching
+    (these calls never reach a launch, so they need no device)."""
+    import mixture_experts_layer_f32_amd as m
+    L = m.lib
+    A = 1 << 20  # a 16-byte-aligned address that is never dereferenced
+    assert L.moe_rmsnorm(0, 2048, None, None, 1e-6, None, None) == m.MOE_OK
+    assert L.moe_rmsnorm(-1, 2048, A, A, 1e-6, A, None) == m.MOE_ERR_BAD_SHAPE
+    assert L.moe_rmsnorm(4, 0, A, A, 1e-6, A, None) == m.MOE_ERR_BAD_SHAPE
+    assert L.moe_rmsnorm(4, 12, A, A, 1e-6, A, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_rmsnorm(4, 16, A, A, -1.0, A, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_rmsnorm(4, 16, None, A, 1e-6, A, None) == m.MOE_ERR_NULL_ARG
+    assert L.moe_rmsnorm(4, 16, A + 2, A, 1e-6, A, None) == m.MOE_ERR_ALIGNMENT
+    assert L.moe_residual_add(0, 64, None, None, None, None, None) == m.MOE_OK
+    assert L.moe_residual_add(4, 6, A, A, None, A, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_residual_add(4, 64, A, None, None, A, None) == m.MOE_ERR_NULL_ARG
+    assert L.moe_residual_add(4, 64, A, A + 8, None, A, None) == m.MOE_ERR_ALIGNMENT
+    assert L.moe_residual_add(4, 64, A, A, A + 4, A, None) == m.MOE_ERR_ALIGNMENT

@@ -10,7 +10,7 @@ import oracle_pins as P
 
 _orig = {name: getattr(om, name) for name in (
     "unpack_e2m1", "dequant", "routing_weights", "router_logits", "select_topk", "silu",
-    "expert_ffn", "combine", "permute", "bf16_rne")}
+    "expert_ffn", "combine", "permute", "bf16_rne", "rmsnorm", "residual_add")}
 
 
 def m_nibble_swap(q, K):
@@ -131,7 +131,30 @@ def m_bf16_truncate(v):
     return (v.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def m_rmsnorm_no_gain(x, gamma, eps):
+    return _orig["rmsnorm"](x, np.full_like(gamma, 0x3F80), eps)
+
+
+def m_rmsnorm_sum_not_mean(x, gamma, eps):
+    xf = om.bf16_to_f64(x)
+    return om.bf16_rne(xf / np.sqrt(np.sum(xf * xf, axis=1, keepdims=True) + eps) * om.bf16_to_f64(gamma))
+
+
+def m_rmsnorm_eps_outside(x, gamma, eps):
+    xf = om.bf16_to_f64(x)
+    ms = np.mean(xf * xf, axis=1, keepdims=True)
+    return om.bf16_rne(xf / (np.sqrt(ms) + eps) * om.bf16_to_f64(gamma))
+
+
+def m_residual_drops_dense(residual, routed, dense=None):
+    return _orig["residual_add"](residual, routed)
+
+
 MUTATIONS = {
+    "rmsnorm_gain_dropped": ("rmsnorm", m_rmsnorm_no_gain),
+    "rmsnorm_sum_not_mean": ("rmsnorm", m_rmsnorm_sum_not_mean),
+    "rmsnorm_eps_outside_sqrt": ("rmsnorm", m_rmsnorm_eps_outside),
+    "residual_add_drops_dense": ("residual_add", m_residual_drops_dense),
     "nibble_swap": ("unpack_e2m1", m_nibble_swap),
     "scale_block_transposed": ("dequant", m_scale_transposed),
     "scale_divided": ("dequant", m_scale_divided),
