@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; achieved HBM GB/s (decode), MFMA TFLOPS (prefill)"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["moe_common.h", "moe_route.h", "moe_decode.h", "moe_gemm.h", "moe_api.hip"]
+KERNEL_SOURCES = ["moe_common.h", "moe_route.h", "moe_decode.h", "moe_gemm.h", "moe_block.h",
+                  "moe_api.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -115,6 +116,87 @@ def write_traffic(args):
     print(json.dumps(out["entries"][key]))
 
 
+def bench_block(args, wl, T, layer, xs, Ws, copies, run, outs, stream, moe, np, torch, synth,
+                DeviceWeights, Runner, to_dev):
+    """One step = RMSNorm of the bf16 hidden rows -> the routed layer on them ->
+    the dense branch (a one-expert top-1 plan, weight exactly 1) -> the add of
+    both into the residual stream.  Each piece timed with events on `stream`."""
+    d = wl.d
+    dwl = synth.Workload(wl.name + "-dense", d, wl.f, 1, 1, wl.fmt, True, (), False, wl.seed + 100)
+    dl = synth.make_layer(dwl)
+    WD = DeviceWeights.upload(dl.w_router, dl.gate.q, dl.gate.s, dl.up.q, dl.up.s, dl.down.q,
+                              dl.down.s)
+    WDs = [WD] + [DeviceWeights(*(t.clone() for t in (WD.w_router, WD.gate_q, WD.gate_s, WD.up_q,
+                                                      WD.up_s, WD.down_q, WD.down_s)))
+                  for _ in range(copies - 1)]
+    dense = Runner(d, wl.f, 1, 1, wl.fmt, True, T)
+    douts = dense.outputs(T)
+    rng = np.random.default_rng(wl.seed)
+    gamma = to_dev((np.frombuffer(rng.uniform(0.5, 1.5, d).astype(np.float32).tobytes(), np.uint32)
+                    >> 16).astype(np.uint16))
+    xn = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    hid = [x.clone() for x in xs]
+    outb = torch.empty((T, d), dtype=torch.int16, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    acc = np.zeros(4)
+
+    def bstep(i, timed=False):
+        j = i % len(xs)
+        if timed:
+            ev[0].record(stream)
+        moe.moe_rmsnorm(hid[j], gamma, 1e-6, xn, stream)
+        if timed:
+            ev[1].record(stream)
+        run.forward(Ws[i % copies], xn, None, outs, stream)
+        if timed:
+            ev[2].record(stream)
+        dense.forward(WDs[i % copies], xn, None, douts, stream)
+        if timed:
+            ev[3].record(stream)
+        moe.moe_residual_add(hid[j], outs["out"], douts["out"], outb, stream)
+        if timed:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        bstep(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        bstep(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_t = min(args.steps, 200)
+    for i in range(n_t):
+        bstep(i, True)
+        ev[4].synchronize()
+        acc += [ev[k].elapsed_time(ev[k + 1]) for k in range(4)]
+    us = acc * 1e3 / n_t
+    norm_bytes = 4 * T * d + 2 * d          # x in, xn out, gain
+    add_bytes = 2 * T * d + 8 * T * d + 2 * T * d  # residual, two f32 terms, bf16 out
+    return {
+        "metric": "transformer-block MoE step tokens/s (RMSNorm + routed layer + dense branch + "
+                  "residual add)",
+        "value": round(T * args.steps / (t1 - t0), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 norm/add, layer as the main line",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{wl.name} block: d={d} routed E={wl.E} k={wl.k} f={wl.f}, dense "
+                               f"branch f={wl.f}, {wl.fmt}, T={T}", "tokens_per_step": T},
+        "pieces_us": {"rmsnorm": round(us[0], 3), "routed_layer": round(us[1], 3),
+                      "dense_branch": round(us[2], 3), "residual_add": round(us[3], 3)},
+        "rmsnorm_roofline": {"bound": "hbm", "achieved": round(norm_bytes / (us[0] * 1e-6) / 1e9, 2),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(norm_bytes / (us[0] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                             "algorithmic_bytes": norm_bytes},
+        "residual_add_roofline": {"bound": "hbm",
+                                  "achieved": round(add_bytes / (us[3] * 1e-6) / 1e9, 2),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(add_bytes / (us[3] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                  "algorithmic_bytes": add_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +218,10 @@ def main():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                          "COPY_WRITE_CSV"),
                     help="write --traffic from rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--block", action="store_true",
+                    help="time the transformer-block steps around the layer too: RMSNorm of the "
+                         "hidden state, a dense (shared) SwiGLU branch of width f in the same "
+                         "format, and the add into the bf16 residual stream")
     ap.add_argument("--traffic-key", default="olmoe-decode/T=8/decode/gateup")
     ap.add_argument("--traffic-kernel", default="dec_mfma<0, true")
     args = ap.parse_args()
@@ -194,6 +280,12 @@ def main():
 
     def step(i):
         run.forward(Ws[i % copies], xs[i % len(xs)], biases[i % len(xs)], outs, stream)
+
+    if args.block:
+        block_line = bench_block(args, wl, T, layer, xs, Ws, copies, run, outs, stream, moe, np,
+                                 torch, synth, DeviceWeights, Runner, to_dev)
+        print(json.dumps(block_line), flush=True)
+        return
 
     # distinct experts per batch (U) from the GPU's own counts
     Us = []

@@ -344,14 +344,15 @@ void launch_gemm(const moe_plan_s* p, int max_tiles, int N, int K, int T, const 
                                                      T, o.nb, o.gc, o.gt, o.ntb);
 }
 
+// y_dst: where the down projection writes y (NULL: the workspace).
 template <int FMT>
 moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, DMat U, DMat D,
-                               const Layout& L, char* ws, hipStream_t st) {
+                               const Layout& L, char* ws, float* y_dst, hipStream_t st) {
   const int d = p->d.d_model, f = p->d.d_ff;
   const int4* info = reinterpret_cast<const int4*>(ws + L.slot_info);
   const int32_t* tok_of = reinterpret_cast<const int32_t*>(ws + L.tok_of);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
-  float* y = reinterpret_cast<float*>(ws + L.y);
+  float* y = y_dst ? y_dst : reinterpret_cast<float*>(ws + L.y);
   // Persistent decode grid (CUs x persist workgroups walking (expert, row pair)
   // items) when each wavefront gets a few items: measured faster there, and
   // slower with one item or with tens of items per wavefront.
@@ -605,7 +606,9 @@ moe_status moe_rmsnorm(int32_t n_tokens, int32_t d, const uint16_t* x, const uin
   if (n_tokens == 0) return MOE_OK;
   if (!x || !gamma || !xn) return MOE_ERR_NULL_ARG;
   if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(xn, 16)) return MOE_ERR_ALIGNMENT;
-  rmsnorm_bf16<<<n_tokens, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(x, gamma, eps, xn, d);
+  // rows of up to 8 chunks per lane (d <= 4096) are held in registers
+  rmsnorm_bf16<8><<<(n_tokens + 3) / 4, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      x, gamma, eps, xn, n_tokens, d);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -753,6 +756,19 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
   int32_t* base = reinterpret_cast<int32_t*>(ws + L.base);
 
+  // one expert, top-1 (the dense branch): the routing is the identity with
+  // weight 1, so the router, the combine and the y buffer are skipped and
+  // the down projection writes out directly (out = 1 * y exactly)
+  const bool dense = E == 1 && k == 1;
+  if (dense) {
+    mark(p, MOE_STAGE_TOPK, false, s);
+    route_dense<<<(std::max(T, L.max_tiles) + 255) / 256, 256, 0, s>>>(
+        ids, w, cnt, off, prm, inv, reinterpret_cast<int32_t*>(ws + L.tok_of),
+        reinterpret_cast<int4*>(ws + L.slot_info), reinterpret_cast<int32_t*>(ws + L.n_active),
+        reinterpret_cast<int4*>(ws + L.tiles), reinterpret_cast<int32_t*>(ws + L.n_tiles), T,
+        tile_rows(p, T));
+    mark(p, MOE_STAGE_TOPK, true, s);
+  } else {
   // a1: router logits (K-slice partials)
   int slice = 0;
   const int nsplit = router_split(p, T, &slice);
@@ -819,6 +835,7 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                                                   k);
   mark(p, MOE_STAGE_PERMUTE, true, s);
   }
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return hip_fail(p, err, "routing launch");
 
@@ -829,14 +846,16 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                up->q_expert_stride, up->s_expert_stride};
   const DMat D{static_cast<const uint8_t*>(down->q), static_cast<const uint8_t*>(down->scale),
                down->q_expert_stride, down->s_expert_stride};
-  st = p->d.wfmt == MOE_W_E4M3_B128       ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, s)
-       : p->d.wfmt == MOE_W_E2M1_UE8M0_G32 ? launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, s)
-                                           : launch_expert_stage<FMT_NVFP4>(p, T, x, G, U, D, L, ws, s);
+  float* y_dst = dense ? out : nullptr;
+  st = p->d.wfmt == MOE_W_E4M3_B128 ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, y_dst, s)
+       : p->d.wfmt == MOE_W_E2M1_UE8M0_G32
+           ? launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, y_dst, s)
+           : launch_expert_stage<FMT_NVFP4>(p, T, x, G, U, D, L, ws, y_dst, s);
   if (st != MOE_OK) return st;
 
   // a6: fixed-order combine
   mark(p, MOE_STAGE_COMBINE, false, s);
-  {
+  if (!dense) {
     const dim3 g(T, (d / 4 + 255) / 256);
     const float* y = reinterpret_cast<const float*>(ws + L.y);
     switch (k) {

@@ -13,48 +13,57 @@
 namespace moe {
 
 // xn[t][i] = bf16(x[t][i] * r_t * gamma[i]), r_t = 1 / sqrt(mean_i x[t][i]^2 + eps),
-// all in f32.  One workgroup of 256 per row; each thread sums the squares of
-// its 8-input chunks (chunks tid, tid + 256, ...) in order, the wavefront
-// sums in a fixed DPP order and the four wavefront sums are added in wave
-// order, so every row has one summation order.  The second pass re-reads the
-// row (cache-resident) to scale it.
+// all in f32.  One wavefront per row, four rows per workgroup: lane l sums the
+// squares of its 8-input chunks (chunks l, l + 64, ...) in order and the
+// wavefront sums the lanes in a fixed DPP order, so every row has one
+// summation order; the row's first RC chunks per lane stay in registers for
+// the scaling pass (longer rows re-read the rest, cache-resident).
+template <int RC>
 __global__ __launch_bounds__(256) void rmsnorm_bf16(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ gamma, float eps,
-                                                    uint16_t* __restrict__ xn, int d) {
-  __shared__ float part[4];
-  const int t = blockIdx.x, tid = threadIdx.x;
+                                                    uint16_t* __restrict__ xn, int T, int d) {
+  const int t = blockIdx.x * 4 + wave_id(), lane = lane_id();
+  if (t >= T) return;
   const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * d);
   const u32x4* g = reinterpret_cast<const u32x4*>(gamma);
   u32x4* dst = reinterpret_cast<u32x4*>(xn + (size_t)t * d);
   const int nc = d >> 3;
+  u32x4 keep[RC];
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = lane + 64 * i;
+    keep[i] = c < nc ? row[c] : u32x4{0u, 0u, 0u, 0u};
+  }
   float ss = 0.0f;
-  for (int c = tid; c < nc; c += 256) {
-    const u32x4 v = row[c];
+  auto sq = [&](const u32x4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_lo(w[j]), b = bf16_hi(w[j]);
       ss = fmaf(a, a, ss);
       ss = fmaf(b, b, ss);
     }
-  }
-  ss = wave_sum(ss);
-  if (lane_id() == 0) part[wave_id()] = ss;
-  __syncthreads();
-  const float ms = ((part[0] + part[1]) + part[2] + part[3]) / (float)d;
-  const float r = 1.0f / sqrtf(ms + eps);
-  for (int c = tid; c < nc; c += 256) {
-    const u32x4 v = row[c], gv = g[c];
+  };
+#pragma unroll
+  for (int i = 0; i < RC; ++i) sq(keep[i]);
+  for (int c = lane + 64 * RC; c < nc; c += 64) sq(row[c]);
+  const float r = 1.0f / sqrtf(wave_sum(ss) / (float)d + eps);
+  auto scale = [&](const u32x4& v, int c) {
+    const u32x4 gv = g[c];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
     uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = f32_to_bf16_rne(bf16_lo(w[i]) * r * bf16_lo(gw[i]));
-      const uint32_t hi = f32_to_bf16_rne(bf16_hi(w[i]) * r * bf16_hi(gw[i]));
-      o[i] = lo | (hi << 16);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = f32_to_bf16_rne(bf16_lo(w[j]) * r * bf16_lo(gw[j]));
+      const uint32_t hi = f32_to_bf16_rne(bf16_hi(w[j]) * r * bf16_hi(gw[j]));
+      o[j] = lo | (hi << 16);
     }
     dst[c] = u32x4{o[0], o[1], o[2], o[3]};
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < RC; ++i)
+    if (lane + 64 * i < nc) scale(keep[i], lane + 64 * i);
+  for (int c = lane + 64 * RC; c < nc; c += 64) scale(row[c], c);
 }
 
 // out[i] = bf16(residual[i] + (a[i] + b[i])) (b may be absent: + a[i] only),

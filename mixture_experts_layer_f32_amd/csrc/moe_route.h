@@ -536,4 +536,38 @@ __global__ __launch_bounds__(1024) void route_small(
   }
 }
 
+// Routing of a one-expert top-1 layer (the dense branch): every token goes
+// to expert 0 with weight exactly 1 (the softmax of one logit), so the
+// permutation is the identity and no logits are needed.  Writes the same
+// outputs and lists as the general routing kernels.
+__global__ __launch_bounds__(256) void route_dense(int32_t* __restrict__ ids, float* __restrict__ w,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ perm,
+                                                   int32_t* __restrict__ inv_perm,
+                                                   int32_t* __restrict__ tok_of,
+                                                   int4* __restrict__ slot_info,
+                                                   int32_t* __restrict__ n_active,
+                                                   int4* __restrict__ tiles,
+                                                   int32_t* __restrict__ n_tiles, int T, int BM) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < T) {
+    ids[i] = 0;
+    w[i] = 1.0f;
+    perm[i] = i;
+    inv_perm[i] = i;
+    tok_of[i] = i;
+  }
+  const int mt = (T + BM - 1) / BM;
+  if (i < mt) tiles[i] = make_int4(0, i * BM, min(BM, T - i * BM), 0);
+  if (i == 0) {
+    counts[0] = T;
+    offsets[0] = 0;
+    offsets[1] = T;
+    slot_info[0] = make_int4(0, 0, T, 0);
+    *n_active = 1;
+    *n_tiles = mt;
+  }
+}
+
 }  // namespace moe

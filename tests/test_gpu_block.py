@@ -103,11 +103,12 @@ def layers():
     return _cache[ROUTED.name], _cache[DENSE.name]
 
 
-@pytest.mark.parametrize("T", [1, 8, 100])
+@pytest.mark.parametrize("T", [1, 8, 100, 300])
 def test_block_forward(T):
     """x -> RMSNorm -> routed layer + dense branch (a one-expert top-1 plan) ->
     add into the residual stream, every step against the oracle.  1 and 8
-    tokens take the decode path, 100 the grouped one."""
+    tokens take the decode path, 100 and 300 the grouped one (the dense
+    branch's 300 rows span several tiles)."""
     import torch
     import mixture_experts_layer_f32_amd as m
     from mixture_experts_layer_f32_amd.device import Runner
@@ -138,7 +139,12 @@ def test_block_forward(T):
     check_out(r_out["out"].cpu().numpy(), ref_r.out)
     ref_d = oracle.moe_forward(xn_g, LD.w_router, None, M(LD.gate), M(LD.up), M(LD.down), 1, True,
                                DENSE.fmt)
+    # one expert, top-1: identity routing with weight exactly 1, no router or combine
     assert np.all(d_out["topk_w"].cpu().numpy() == 1.0)
+    assert np.all(d_out["topk_ids"].cpu().numpy() == 0)
+    assert np.array_equal(d_out["perm"].cpu().numpy(), np.arange(T))
+    assert np.array_equal(d_out["counts"].cpu().numpy(), [T])
+    assert np.array_equal(d_out["offsets"].cpu().numpy(), [0, T])
     check_out(d_out["out"].cpu().numpy(), ref_d.out)
     # the add: the oracle's sum of its own layer outputs, so the bound is the
     # layers' tolerance plus one bf16 step
