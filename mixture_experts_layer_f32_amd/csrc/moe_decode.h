@@ -148,6 +148,64 @@ __device__ __forceinline__ void dec_matvec(const uint8_t* const (&q)[NM],
       for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int t = 0; t < TG; ++t) acc[m][r][t] = 0.0f;
+    if constexpr (FMT != FMT_E4M3) {
+      // fp4: a lane takes two adjacent chunks (32 inputs, 16 bytes of codes:
+      // one e2m1 scale group, two NVFP4 groups) per step, so a step is one
+      // 16-byte code load and one scale load per row instead of two of each
+      const int npair = nch >> 1;
+      for (int p0 = lane; p0 < npair; p0 += WAVE * U) {
+        u32x4 w[U][NM][RPW];
+        uint32_t sb[U][NM][RPW];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pp = p0 + WAVE * u;
+          if (pp < npair) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int r = 0; r < RPW; ++r) {
+                w[u][m][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q[m] + r * rb) + pp);
+                if constexpr (FMT == FMT_NVFP4)
+                  sb[u][m][r] = reinterpret_cast<const uint16_t*>(s[m] + (size_t)(n0 + r) * (K >> 4))[pp];
+                else
+                  sb[u][m][r] = s[m][(size_t)(n0 + r) * (K >> 5) + pp];
+              }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pp = p0 + WAVE * u;
+          if (pp < npair) {
+            uint32_t xv[TG][2][8];
+#pragma unroll
+            for (int t = 0; t < TG; ++t)
+              if (t < ntok) {
+                load_act16(ar[t], 2 * pp, xv[t][0]);
+                load_act16(ar[t], 2 * pp + 1, xv[t][1]);
+              }
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int r = 0; r < RPW; ++r) {
+                float sc0, sc1;
+                if constexpr (FMT == FMT_NVFP4) {
+                  const f32x2 sv = __builtin_amdgcn_cvt_pk_f32_fp8(sb[u][m][r], false);
+                  sc0 = sv.x;
+                  sc1 = sv.y;
+                } else {
+                  sc0 = sc1 = ue8m0_to_f32(sb[u][m][r]);
+                }
+                bf16x2 wa[8], wb[8];
+                Chunk<FMT>::decode(u32x2{w[u][m][r].x, w[u][m][r].y}, sc0, wa);
+                Chunk<FMT>::decode(u32x2{w[u][m][r].z, w[u][m][r].w}, sc1, wb);
+#pragma unroll
+                for (int t = 0; t < TG; ++t)
+                  if (t < ntok) acc[m][r][t] = (acc[m][r][t] + dot16(wa, xv[t][0])) + dot16(wb, xv[t][1]);
+              }
+          }
+        }
+      }
+    } else
     for (int c0 = lane; c0 < nch; c0 += WAVE * U) {
       typename Chunk<FMT>::raw w[U][NM][RPW];
 #pragma unroll
