@@ -166,7 +166,8 @@ moe_status moe_timing_enable(moe_plan_t plan, uint32_t stage_mask, int32_t max_f
 /* Waits for the last recorded event, then writes for each stage the summed
  * GPU time in milliseconds over the recorded forwards (stage_ms[MOE_N_STAGES];
  * 0 for stages not in the mask, and for stages a forward runs fused with the
- * previous one: for T <= 16 the permute is part of MOE_STAGE_TOPK) and their
+ * previous one: for T <= 16 (T <= 64 with at most 64 experts) the permute is
+ * part of MOE_STAGE_TOPK) and their
  * number, and starts a new count. */
 moe_status moe_timing_collect(moe_plan_t plan, float* stage_ms, int32_t* n_forwards);
 

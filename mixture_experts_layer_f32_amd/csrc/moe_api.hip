@@ -48,6 +48,7 @@ struct moe_plan_s {
   int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
   int dec_tall = -1;      // MFMA decode tiles of 32/64 rows: -1 by shape, 0 never, 1 always
+  int small_route_t = 0;  // top-k + permute in one workgroup up to this many tokens (<= 64), 0 = by shape
   int dec_ks = 0;         // MFMA decode wavefronts per workgroup (k-split), 0 = by shape
   int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (11, 12, 22, 23, 24), 0 = by shape
   int gemm_kernel = 3;    // grouped expert stage: 3 = gemm_big (default), 1 = register-weight tiles,
@@ -572,6 +573,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
   if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
   if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
+  if (const char* v = std::getenv("MOE_SMALL_ROUTE_T")) p->small_route_t = std::max(1, std::min(64, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KS")) p->dec_ks = std::max(0, std::min(4, std::atoi(v)));
   if (const char* v = std::getenv("MOE_BIG_CFG")) {
     const int c = std::atoi(v);
@@ -788,7 +790,11 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   mark(p, MOE_STAGE_ROUTER, true, s);
   const int ng = (E + WAVE - 1) / WAVE;
   const int ngp = ng <= 1 ? 1 : ng <= 2 ? 2 : ng <= 4 ? 4 : ng <= 8 ? 8 : 16;
-  if (T <= 16) {
+  // up to 64 tokens with at most 64 experts (measured on the OLMoE shape:
+  // 2-5 % faster per step at 24-48 tokens than the four routing launches;
+  // no gain with 256 or 384 experts), else up to 16 tokens
+  const int small_t = p->small_route_t > 0 ? p->small_route_t : (E <= 64 ? 64 : 16);
+  if (T <= small_t && S <= 1023) {
     // a2 + a3 in one workgroup
     mark(p, MOE_STAGE_TOPK, false, s);
 #define MOE_SMALL(NG)                                                                            \

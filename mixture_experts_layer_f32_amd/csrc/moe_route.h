@@ -492,7 +492,7 @@ __global__ __launch_bounds__(1024) void route_small(
     int renorm, int BM) {
   __shared__ unsigned long long mask[MAX_E];
   __shared__ int off_s[MAX_E];
-  __shared__ int ids_s[16 * MAX_K];  // the ids again, read back without a memory round trip
+  __shared__ int ids_s[WAVE * MAX_K];  // the ids again, read back without a memory round trip
   const int tid = threadIdx.x;
   for (int t = wave_id(); t < T; t += 16)
     topk_token<NG>(t, part, nsplit, bias, ids, w, T, E, k, renorm, ids_s);
@@ -504,10 +504,10 @@ __global__ __launch_bounds__(1024) void route_small(
   const int e = tid;
   const int c_e = e < E ? __popcll(mask[e]) : 0;
   if (e < E) counts[e] = c_e;
-  // one scan of three 10-bit fields: slots (offsets), selected experts
-  // (record index), tiles (tile-list index).  Each partial sum is at most
-  // T*k <= 256 (c_e <= T <= 16 and BM >= 16, so an expert has at most one
-  // tile), so no field carries into the next.
+  // one scan of three fields: slots (offsets, 10 bits), selected experts
+  // (record index, 10 bits), tiles (tile-list index, bits 20..30).  The
+  // caller keeps T <= 64 and T*k <= 1023, so no partial sum of the first two
+  // exceeds 1023, and the tiles (at most T*k/16 + E with BM >= 16) fit 11 bits.
   const int mt = (e < E) ? (c_e + BM - 1) / BM : 0;
   int tot;
   const int packed = block_exclusive_scan(c_e | ((c_e > 0 ? 1 : 0) << 10) | (mt << 20), &tot);

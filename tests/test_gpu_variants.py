@@ -116,3 +116,24 @@ def test_big_tile_shapes(fmt, cfg):
     batch = synth.Batch(batch.x, bias)
     ref = oracle_run(wl, layer, batch)
     check_all(run_with_env({"MOE_GEMM": "3", "MOE_BIG_CFG": cfg}, wl, W, batch, GROUPED), ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("T,path", [(17, DECODE), (37, DECODE), (64, GROUPED)])
+def test_one_workgroup_routing_up_to_64_tokens(fmt, T, path):
+    """Top-k and permute in one workgroup (MOE_SMALL_ROUTE_T) for 17..64 tokens:
+    several row-group tiles per expert in the tile list, against the oracle."""
+    wl, layer, W = get(fmt)
+    batch = synth.make_batch(wl, layer, T)
+    ref = oracle_run(wl, layer, batch)
+    check_all(run_with_env({"MOE_SMALL_ROUTE_T": "64"}, wl, W, batch, path), ref)
+
+
+def test_one_workgroup_routing_olmoe_shape():
+    """64 experts, top-8, 64 tokens (512 slots) routed in one workgroup."""
+    wl = synth.WORKLOADS["olmoe-decode"]
+    layer = synth.make_layer(wl)
+    W = device_weights(layer)
+    batch = synth.make_batch(wl, layer, 64)
+    ref = oracle_run(wl, layer, batch)
+    check_all(run_with_env({"MOE_SMALL_ROUTE_T": "64"}, wl, W, batch, DECODE), ref)
