@@ -229,3 +229,22 @@ def test_nonfinite_input_row_does_not_fault():
     g, _ = gpu_run(WL, W, synth.Batch(x, None), 0)
     ok = [t for t in range(T) if t != 2]
     check_out(g["out"][ok], ref.out[ok])
+
+
+WL_MAX = synth.Workload("edge-max-experts", 128, 128, 1024, 16, "e4m3", True, (9,), False, 4006)
+WL_MAX4 = synth.Workload("edge-max-experts-fp4", 64, 96, 1024, 16, "e2m1", False, (9,), False, 4007)
+
+
+@pytest.mark.parametrize("wl", [WL_MAX, WL_MAX4], ids=lambda w: w.name)
+@pytest.mark.parametrize("T,path", [(1, 0), (16, 0), (40, 1), (100, 2)])
+def test_largest_expert_count_and_top_k(wl, T, path):
+    """The plan's limits: 1024 experts (16 groups of 64 in the top-k) and
+    top-16, through the one-workgroup routing (T <= 16), the multi-launch
+    permute (40, 100) and both expert paths."""
+    L, W = get(wl)
+    batch = synth.make_batch(wl, L, T)
+    ref = oracle_run(wl, L, batch)
+    g, _ = gpu_run(wl, W, batch, path)
+    check_routing(g, ref)
+    check_h(g["h"], ref.h)
+    check_out(g["out"], ref.out)
