@@ -63,9 +63,31 @@ per-sub-block branches quantised like the routed experts):
       which is what moe_forward computes with E = 1 and k = 1 (reading N2).
   B3  The add into the residual stream (residual_add):
       out = bf16_rne(residual + (routed + dense)), float64 inside, one rounding.
+
+The activation-quantised variant (opt-in; it changes results by design: the
+dev.to DeepSeek-V4.1-Flash post, "Three bugs on RTX 50xx that never raise an
+error", item 2: the model's activation quantiser writes fp8 with UE8M0
+(power-of-two) scales, always on in that model; WARP BACKENDS.md, the SDOT
+mode table and "i8mm/SMMLA for the batched matmul": quantised activations
+move results by about 1e-2 relative, a real change rather than rounding
+noise):
+
+  Q1  act_quant_e4m3: each bf16 row is cut into groups of 128 consecutive
+      inputs (the last group of a row whose length is not a multiple of 128
+      is shorter; reading Q-a); a group's scale is the smallest power of two
+      2^E with max|x| <= 448 * 2^E, stored as the byte E + 127 (UE8M0; 127 for
+      an all-zero group; reading Q-b), and each input becomes the e4m3 code
+      nearest x / 2^E (ties to the even mantissa; the sign bit is x's, so -0
+      and negatives that round to zero keep it).  x / 2^E is exact, and
+      |x / 2^E| <= 448 so nothing saturates.
+  Q2  The forward with both expert inputs quantised by Q1 (reading Q-c): the
+      token rows x before gate/up, and h (already bf16 by O8) before down;
+      the GEMMs then see the dequantised values code * 2^E exactly.  The
+      router still reads the unquantised x (O2).
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -211,12 +233,14 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
-def expert_ffn(xf: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray):
-    """Rows xf [M, d] (float64) through one SwiGLU expert: (h bf16 bits [M, f], y [M, d])."""
+def expert_ffn(xf: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, act_q: bool = False):
+    """Rows xf [M, d] (float64) through one SwiGLU expert: (h bf16 bits [M, f], y [M, d]).
+    With act_q, h is quantised by Q1 before the down projection (Q2)."""
     g = xf @ Wg.T
     u = xf @ Wu.T
     h = bf16_rne(silu(g) * u)
-    y = bf16_to_f64(h) @ Wd.T
+    hin = act_dequant(*act_quant_e4m3(h)) if act_q else bf16_to_f64(h)
+    y = hin @ Wd.T
     return h, y
 
 
@@ -228,6 +252,66 @@ def combine(y_sorted: np.ndarray, w: np.ndarray, inv_perm: np.ndarray) -> np.nda
     for j in range(k):
         out = out + w[:, j:j + 1] * y_sorted[pos[:, j]]
     return out.astype(np.float32)
+
+
+# ---------------------------------------------------------------- activation quantiser (Q1)
+
+ACT_GROUP = 128
+E4M3_MAX = 448.0
+
+
+def e4m3_rne(v: np.ndarray) -> np.ndarray:
+    """float64 values with |v| <= 448 -> e4m3 codes, round to nearest with ties
+    to the even mantissa; the sign bit is v's sign bit."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    assert np.all(a <= E4M3_MAX), "e4m3_rne: value beyond 448"
+    with np.errstate(divide="ignore"):
+        _, ex = np.frexp(a)                   # a = fr * 2^ex, fr in [0.5, 1)
+    e = np.maximum(ex - 1, -6)                # exponent of the leading bit, floored (subnormals)
+    q = np.ldexp(1.0, e - 3)                  # quantum: 3 fraction bits
+    r = np.where(a == 0, 0.0, np.rint(a / q) * q)   # np.rint: half to even
+    # codes 0x00 .. 0x7E hold the non-negative values in increasing order
+    idx = np.searchsorted(E4M3[:0x7F], r)
+    assert np.all(E4M3[idx] == r)
+    return (idx | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def ue8m0_for(amax: float) -> int:
+    """The byte E + 127 of the smallest power of two 2^E with amax <= 448 * 2^E
+    (at least 0); 127 for amax = 0 (Q1)."""
+    if amax == 0:
+        return 127
+    E = max(math.frexp(amax)[1] - 9, -127)    # within one or two of the answer
+    while amax > E4M3_MAX * 2.0 ** E:
+        E += 1
+    while E > -127 and amax <= E4M3_MAX * 2.0 ** (E - 1):
+        E -= 1
+    return E + 127
+
+
+def act_quant_e4m3(bits: np.ndarray, group: int = ACT_GROUP):
+    """Q1: bf16 rows [R, K] -> (e4m3 codes uint8 [R, K], UE8M0 scale bytes uint8
+    [R, ceil(K / group)])."""
+    x = bf16_to_f64(bits)
+    R, K = x.shape
+    ng = -(-K // group)
+    codes = np.zeros((R, K), np.uint8)
+    scales = np.zeros((R, ng), np.uint8)
+    for g in range(ng):
+        blk = x[:, g * group:(g + 1) * group]
+        for r in range(R):
+            b = ue8m0_for(float(np.max(np.abs(blk[r]))) if blk.shape[1] else 0.0)
+            scales[r, g] = b
+            codes[r, g * group:(g + 1) * group] = e4m3_rne(blk[r] / 2.0 ** (b - 127))
+    return codes, scales
+
+
+def act_dequant(codes: np.ndarray, scales: np.ndarray, group: int = ACT_GROUP) -> np.ndarray:
+    """code * 2^(byte - 127) per group, float64 (exact)."""
+    K = codes.shape[1]
+    sc = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), group, axis=1)[:, :K]
+    return E4M3[codes] * sc
 
 
 @dataclass
@@ -253,11 +337,12 @@ class Result:
 
 
 def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm: bool,
-                fmt: str, tokens: Optional[Sequence[int]] = None) -> Result:
+                fmt: str, tokens: Optional[Sequence[int]] = None, act_quant: bool = False) -> Result:
     """The whole layer (O1-O10).  With `tokens`, routing is computed for every
     token (the permutation needs all of them) but the expert FFN and the
     combine only for the listed tokens; `out` then has one row per listed
-    token and h/y are not returned."""
+    token and h/y are not returned.  With `act_quant`, the activation-quantised
+    variant (Q1-Q2)."""
     T, d = x.shape
     E = w_router.shape[0]
     f = gate.q.shape[1]
@@ -266,7 +351,7 @@ def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm
     w = routing_weights(logits, ids, renorm)
     counts, offsets, perm, inv_perm = permute(ids, E)
     S = T * k
-    xf = bf16_to_f64(x)
+    xf = bf16_to_f64(x) if not act_quant else act_dequant(*act_quant_e4m3(x))
     want = np.ones(S, bool) if tokens is None else np.isin(np.arange(S) // k, list(tokens))
     h = np.zeros((S, f), np.uint16)
     y = np.zeros((S, d), np.float64)
@@ -280,7 +365,10 @@ def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm
         Wg = dequant(gate.q[e], gate.s[e], fmt, gate.K)
         Wu = dequant(up.q[e], up.s[e], fmt, up.K)
         Wd = dequant(down.q[e], down.s[e], fmt, down.K)
-        h[pos], y[pos] = expert_ffn(xf[rows], Wg, Wu, Wd)
+        if act_quant:
+            h[pos], y[pos] = expert_ffn(xf[rows], Wg, Wu, Wd, act_q=True)
+        else:
+            h[pos], y[pos] = expert_ffn(xf[rows], Wg, Wu, Wd)
     if tokens is None:
         out = combine(y, w, inv_perm)
         return Result(logits, ids, w, counts, offsets, perm, inv_perm, h, y, out)

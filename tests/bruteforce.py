@@ -5,6 +5,7 @@ and no gather.  Decoding uses torch's float8 cast and a bit-shift nibble
 split; bf16 rounding is a nearest-value search over all bf16 values; logits
 are exact sums (math.fsum) of exactly-representable products."""
 import math
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -107,9 +108,43 @@ def softmax_row(l):
     return np.array([v / Z for v in z])
 
 
-def forward(x_bits, w_router, bias, mats, k, renorm, fmt):
+def scale_byte(a):
+    """The biased exponent E + 127 of the smallest power of two 2^E with
+    a <= 448 * 2^E, by exact rational arithmetic (at least 0; 127 for a = 0)."""
+    if a == 0:
+        return 127
+    f = Fraction(float(a)) / 448
+    E = f.numerator.bit_length() - f.denominator.bit_length()
+    while Fraction(2) ** E < f:
+        E += 1
+    while Fraction(2) ** (E - 1) >= f:
+        E -= 1
+    return max(E, -127) + 127
+
+
+def act_quant_values(xf, group=128):
+    """Per-row groups of `group` inputs quantised to e4m3 with a power-of-two
+    scale by torch's float8 cast (round to nearest even; every value fits),
+    returned dequantised (float64) together with codes and scale bytes."""
+    R, K = xf.shape
+    codes = np.zeros((R, K), np.uint8)
+    bytes_ = np.zeros((R, -(-K // group)), np.uint8)
+    out = np.zeros((R, K))
+    for r in range(R):
+        for g0 in range(0, K, group):
+            blk = xf[r, g0:g0 + group]
+            b = scale_byte(np.max(np.abs(blk)))
+            v = torch.from_numpy(blk / 2.0 ** (b - 127)).to(torch.float32).to(torch.float8_e4m3fn)
+            codes[r, g0:g0 + group] = v.view(torch.uint8).numpy()
+            bytes_[r, g0 // group] = b
+            out[r, g0:g0 + group] = v.to(torch.float64).numpy() * 2.0 ** (b - 127)
+    return out, codes, bytes_
+
+
+def forward(x_bits, w_router, bias, mats, k, renorm, fmt, act_quant=False):
     """Dense evaluation.  mats = (gate_q, gate_s, up_q, up_s, down_q, down_s), each
-    with a leading expert axis.  Returns (ids [T,k], w [T,k], out f64 [T,d])."""
+    with a leading expert axis.  Returns (ids [T,k], w [T,k], out f64 [T,d]).
+    act_quant: the expert inputs (x, then h) quantised per 128-input group."""
     gq, gs, uq, us, dq, ds = mats
     T = x_bits.shape[0]
     E = w_router.shape[0]
@@ -117,6 +152,8 @@ def forward(x_bits, w_router, bias, mats, k, renorm, fmt):
     mask = topk_mask(logits, k)
     P = np.stack([softmax_row(logits[t]) for t in range(T)]) if T else np.zeros((0, E))
     xf = bf16_bits_to_f64(x_bits)
+    if act_quant:
+        xf = act_quant_values(xf)[0]
     d = xf.shape[1]
     out = np.zeros((T, d))
     ids = np.zeros((T, k), np.int64)
@@ -134,6 +171,8 @@ def forward(x_bits, w_router, bias, mats, k, renorm, fmt):
         g = xf @ Wg.T
         u = xf @ Wu.T
         h = bf16_round(g / (1.0 + np.exp(-g)) * u)
+        if act_quant:
+            h = act_quant_values(h)[0]
         Y[e] = h @ Wd.T
     for t in range(T):
         acc = np.zeros(d)

@@ -343,6 +343,58 @@ def pin_residual_add(om):
     assert np.array_equal(om.residual_add(res, a), _bf16([[1.5, 2.25, -2.0, 256.0]]))
 
 
+# ---------------------------------------------------------------- activation-quantised variant
+
+
+def pin_act_quant(om):
+    """Q1 on hand-worked groups (448 is code 0x7E at scale 1; 1.0625 and
+    1.1875 are ties that go to the even mantissas 1.0 and 1.25; -0 and a
+    negative that rounds to zero keep the sign bit; the next bf16 above
+    448 * 2^j needs 2^(j+1); a short last group has its own scale), then on
+    random rows of many magnitudes against an independent route: exact
+    rational scale search and torch's float8 cast (a library routine)."""
+    row = [448.0, 1.0625, 1.1875, -0.0, -1e-6] + [0.0] * 123 + [7.0] + [0.5] * 63
+    codes, sc = om.act_quant_e4m3(_bf16([row]))
+    assert [int(c) for c in codes[0, :5]] == [0x7E, 0x38, 0x3A, 0x80, 0x80], codes[0, :5]
+    assert sc.shape == (1, 2) and list(sc[0]) == [127, 121], sc      # 7 = 448 * 2^-6
+    assert codes[0, 128] == 0x7E and np.all(codes[0, 129:] == 0x60)   # 0.5 * 2^6 = 32 = 2^5
+    for j in (-3, 0, 5):
+        c, s_ = om.act_quant_e4m3(_bf16([[448.0 * 2.0 ** j] + [1.0] * 127]))
+        assert s_[0, 0] == 127 + j and c[0, 0] == 0x7E
+        c, s_ = om.act_quant_e4m3(_bf16([[450.0 * 2.0 ** j] + [1.0] * 127]))  # next bf16 up
+        assert s_[0, 0] == 128 + j and c[0, 0] == 0x76, (s_, hex(c[0, 0]))  # 225 -> 224
+    c, s_ = om.act_quant_e4m3(np.zeros((2, 256), np.uint16))
+    assert np.all(c == 0) and np.all(s_ == 127)
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((6, 320)) * np.ldexp(1.0, rng.integers(-30, 30, (6, 1)))
+    x[2, 128:256] = 0.0
+    x[3, ::7] *= 1e-4                         # values below the e4m3 normal range of their group
+    bits = _bf16(x)
+    codes, sc = om.act_quant_e4m3(bits)
+    deq, c_ref, s_ref = bf.act_quant_values(bf.bf16_bits_to_f64(bits))
+    assert np.array_equal(sc, s_ref), "scale bytes differ from the exact route"
+    assert np.array_equal(codes, c_ref), "codes differ from torch's float8 cast"
+    assert np.array_equal(om.act_dequant(codes, sc), deq)
+    # half a quantum at most: 2^-4 relative in the normal range, 2^-10 of the scale below it
+    xf = bf.bf16_bits_to_f64(bits)
+    scale = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 128, axis=1)[:, :320]
+    assert np.all(np.abs(deq - xf) <= np.maximum(np.abs(xf) * 2.0 ** -4, scale * 2.0 ** -10))
+
+
+def pin_act_quant_forward(om, name):
+    """Q2 against the dense brute force with the same quantiser route (exact
+    scales, torch's float8 cast) applied to x and to h."""
+    wl, layer, batch = case(name)
+    r = run(om, wl, layer, batch, act_quant=True)
+    ids, w, out = bf.forward(batch.x, layer.w_router, batch.bias,
+                             (layer.gate.q, layer.gate.s, layer.up.q, layer.up.s, layer.down.q,
+                              layer.down.s), wl.k, wl.renorm, wl.fmt, act_quant=True)
+    assert np.array_equal(r.ids, ids)
+    assert_out_close(r.out, out)
+    # and it is not the unquantised layer
+    assert not np.array_equal(r.out, run(om, wl, layer, batch).out)
+
+
 FAST_PINS = [
     lambda om: pin_bruteforce(om, "tiny"),
     lambda om: pin_bruteforce(om, "e4m3-nonsquare", biased=True),
@@ -350,5 +402,7 @@ FAST_PINS = [
     lambda om: pin_bruteforce(om, "nvfp4-small"),
     pin_onehot, pin_routing_closed_form, pin_router_exact, pin_topk_ties, pin_permute, pin_silu,
     pin_scale_doubling, pin_identical_experts, pin_relabel, pin_zero_input, pin_single_expert,
-    pin_lossless_grid, pin_token_subset, pin_rmsnorm, pin_residual_add,
+    pin_lossless_grid, pin_token_subset, pin_rmsnorm, pin_residual_add, pin_act_quant,
+    lambda om: pin_act_quant_forward(om, "e4m3-nonsquare"),
+    lambda om: pin_act_quant_forward(om, "e2m1-small"),
 ]

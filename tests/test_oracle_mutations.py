@@ -10,7 +10,8 @@ import oracle_pins as P
 
 _orig = {name: getattr(om, name) for name in (
     "unpack_e2m1", "dequant", "routing_weights", "router_logits", "select_topk", "silu",
-    "expert_ffn", "combine", "permute", "bf16_rne", "rmsnorm", "residual_add")}
+    "expert_ffn", "combine", "permute", "bf16_rne", "rmsnorm", "residual_add", "ue8m0_for",
+    "act_quant_e4m3", "e4m3_rne")}
 
 
 def m_nibble_swap(q, K):
@@ -150,7 +151,35 @@ def m_residual_drops_dense(residual, routed, dense=None):
     return _orig["residual_add"](residual, routed)
 
 
+def m_actq_scale_low(amax):
+    b = _orig["ue8m0_for"](amax)
+    return b - 1 if amax else b
+
+
+def m_actq_group64(bits, group=128):
+    return _orig["act_quant_e4m3"](bits, 64)
+
+
+def m_actq_ties_away(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    with np.errstate(divide="ignore"):
+        _, ex = np.frexp(a)
+    q = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+    r = np.where(a == 0, 0.0, np.floor(a / q + 0.5) * q)
+    idx = np.searchsorted(om.E4M3[:0x7F], r)
+    return (idx | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def m_actq_h_unquantised(xf, Wg, Wu, Wd, act_q=False):
+    return _orig["expert_ffn"](xf, Wg, Wu, Wd)
+
+
 MUTATIONS = {
+    "act_quant_scale_one_binade_low": ("ue8m0_for", m_actq_scale_low),
+    "act_quant_group_64": ("act_quant_e4m3", m_actq_group64),
+    "act_quant_ties_away": ("e4m3_rne", m_actq_ties_away),
+    "act_quant_h_not_quantised": ("expert_ffn", m_actq_h_unquantised),
     "rmsnorm_gain_dropped": ("rmsnorm", m_rmsnorm_no_gain),
     "rmsnorm_sum_not_mean": ("rmsnorm", m_rmsnorm_sum_not_mean),
     "rmsnorm_eps_outside_sqrt": ("rmsnorm", m_rmsnorm_eps_outside),

@@ -16,9 +16,14 @@ def test_bruteforce_small(name, biased):
                                  P.pin_topk_ties, P.pin_permute, P.pin_silu, P.pin_scale_doubling,
                                  P.pin_identical_experts, P.pin_relabel, P.pin_zero_input,
                                  P.pin_single_expert, P.pin_lossless_grid, P.pin_token_subset,
-                                 P.pin_rmsnorm, P.pin_residual_add])
+                                 P.pin_rmsnorm, P.pin_residual_add, P.pin_act_quant])
 def test_pin(pin):
     pin(om)
+
+
+@pytest.mark.parametrize("name", ["e4m3-nonsquare", "e2m1-small"])
+def test_act_quant_forward_bruteforce(name):
+    P.pin_act_quant_forward(om, name)
 
 
 def test_bruteforce_olmoe_decode_shapes():
