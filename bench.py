@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; achieved HBM GB/s (decode), MFMA TFLOPS (prefill)"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-KERNEL_SOURCES = ["moe_common.h", "moe_route.h", "moe_decode.h", "moe_gemm.h", "moe_block.h",
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the activation-quantised variant)
+KERNEL_SOURCES = ["moe_common.h", "moe_route.h", "moe_decode.h", "moe_gemm.h", "moe_block.h", "moe_q8.h",
                   "moe_api.hip"]
 
 
@@ -222,6 +223,9 @@ def main():
                     help="time the transformer-block steps around the layer too: RMSNorm of the "
                          "hidden state, a dense (shared) SwiGLU branch of width f in the same "
                          "format, and the add into the bf16 residual stream")
+    ap.add_argument("--act-quant", action="store_true",
+                    help="the activation-quantised variant: x and h as e4m3 per 128-input group "
+                         "(UE8M0 scales), block-scaled fp8 MFMA; opt-in, it changes results")
     ap.add_argument("--traffic-key", default="olmoe-decode/T=8/decode/gateup")
     ap.add_argument("--traffic-kernel", default="dec_mfma<0, true")
     args = ap.parse_args()
@@ -267,7 +271,8 @@ def main():
     biases = [to_dev(b.bias) if b.bias is not None else None for b in batches]
     path = {"auto": moe.MOE_PATH_AUTO, "decode": moe.MOE_PATH_DECODE,
             "grouped": moe.MOE_PATH_GROUPED}[args.path]
-    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path)
+    act_fmt = moe.MOE_ACT_E4M3_G128 if args.act_quant else moe.MOE_ACT_BF16
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path, act_fmt=act_fmt)
     outs = run.outputs(T)
     used_path = "decode" if moe.moe_plan_path(run.plan, T) == moe.MOE_PATH_DECODE else "grouped"
     # expert-stage arithmetic (the router is f32 throughout): bf16 products
@@ -276,6 +281,8 @@ def main():
     mfma = used_path == "grouped" or (os.environ.get("MOE_DEC_KERNEL", "1") != "0"
                                       and T >= int(os.environ.get("MOE_DEC_MFMA_MIN_T", "2")))
     dtype = "bf16-mfma/f32-acc" if mfma else "bf16-dot2/f32-acc"
+    if args.act_quant:
+        dtype = "e4m3xe4m3-mfma/f32-acc" if wl.fmt == "e4m3" else "e4m3xe2m1-mfma/f32-acc"
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -325,14 +332,15 @@ def main():
     dom = max(("gateup", "down"), key=lambda s: stage_avg_us[s])
     dur_s = stage_avg_us[dom] * 1e-6
     intensity = flops[dom] / nbytes[dom]
-    if intensity > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved, peak, unit, bound = flops[dom] / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    peak_mfma = PEAK_FP8_TFLOPS if args.act_quant else PEAK_BF16_TFLOPS
+    if intensity > peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved, peak, unit, bound = flops[dom] / dur_s / 1e12, peak_mfma, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = nbytes[dom] / dur_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
 
     traffic = None
     ksrc = kernel_source_hash()
-    key = f"{wl.name}/T={T}/{used_path}/{dom}"
+    key = f"{wl.name}/T={T}/{used_path}{'-q8' if args.act_quant else ''}/{dom}"
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
             tr = json.load(f)
@@ -359,7 +367,7 @@ def main():
         while True:
             b = batches[done % len(batches)]
             oracle.moe_forward(b.x, layer.w_router, b.bias, M(layer.gate), M(layer.up),
-                               M(layer.down), wl.k, wl.renorm, wl.fmt)
+                               M(layer.down), wl.k, wl.renorm, wl.fmt, act_quant=args.act_quant)
             done += 1
             tok += T
             if time.perf_counter() - tc0 >= args.cpu_seconds:
@@ -390,7 +398,7 @@ def main():
             "weights": {"e4m3": "e4m3 + f32 128x128 block scales",
                         "e2m1": "e2m1 + ue8m0 per 32",
                         "nvfp4": "e2m1 + e4m3 per 16 (nvfp4)"}[wl.fmt],
-            "activations": "bf16",
+            "activations": "e4m3 per 128-input group, ue8m0 scales" if args.act_quant else "bf16",
             "distinct_experts_per_step": U,
             "weight_copies_rotated": copies,
             "x_batches_rotated": len(xs),

@@ -78,6 +78,26 @@ typedef enum {
   MOE_PATH_GROUPED = 2   /* grouped MFMA GEMM over expert tiles */
 } moe_path;
 
+/* Precision of the expert inputs.  The dev.to DeepSeek-V4.1-Flash post
+ * ("Three bugs on RTX 50xx that never raise an error", item 2) runs its
+ * activations through an fp8 quantiser with UE8M0 scales; WARP BACKENDS.md
+ * measures what quantised activations cost in accuracy (about 1e-2 relative
+ * on logits), so the default keeps them in bf16. */
+typedef enum {
+  /* bf16 activations, weights decoded exactly to bf16 (the default) */
+  MOE_ACT_BF16 = 0,
+  /* the token rows x (before gate/up) and h (before down) quantised per
+   * 128-input group of a row: scale = the smallest power of two 2^E with
+   * max|x| <= 448 * 2^E (UE8M0 byte E + 127; 127 for an all-zero group),
+   * codes = e4m3 nearest x / 2^E (ties to even, the sign kept); a row whose
+   * length is not a multiple of 128 ends in a shorter group.  The GEMMs run
+   * on gfx950's block-scaled fp8/fp4 MFMA with f32 accumulation.  Weights
+   * e4m3 or e2m1 (not NVFP4, whose e4m3 group scales are not powers of two);
+   * e2m1 needs d_model % 64 == 0 and d_ff % 64 == 0 and 2-byte aligned
+   * scales.  Always the grouped path (MOE_PATH_DECODE is refused). */
+  MOE_ACT_E4M3_G128 = 1
+} moe_act_fmt;
+
 typedef struct {
   int32_t d_model;     /* hidden size d */
   int32_t d_ff;        /* expert FFN width f */
@@ -87,6 +107,7 @@ typedef struct {
   int32_t wfmt;        /* moe_wfmt */
   int32_t renorm;      /* 1: divide the k weights by their sum; 0: keep softmax probabilities */
   int32_t path;        /* moe_path */
+  int32_t act_fmt;     /* moe_act_fmt */
 } moe_desc;
 
 typedef struct moe_plan_s* moe_plan_t;
@@ -198,6 +219,23 @@ moe_status moe_rmsnorm(int32_t n_tokens, int32_t d, const uint16_t* x, const uin
  *   a, b           f32 [T][d], 16-byte aligned.  Requires d % 4 == 0. */
 moe_status moe_residual_add(int32_t n_tokens, int32_t d, const uint16_t* residual, const float* a,
                             const float* b, uint16_t* out, void* stream);
+
+/* The activation quantiser of MOE_ACT_E4M3_G128 on its own (the forward of
+ * such a plan runs it on x and on h): each bf16 row of x [rows][K] is cut
+ * into groups of 128 inputs (the last group of a row is shorter when
+ * K % 128 != 0); a group's scale byte is E + 127 for the smallest power of
+ * two 2^E (E >= -127) with max|x| <= 448 * 2^E (127 for an all-zero group),
+ * and each input becomes the e4m3 code nearest x / 2^E (ties to the even
+ * mantissa, the sign bit kept).  dev.to DeepSeek-V4.1-Flash post, "Three bugs
+ * on RTX 50xx that never raise an error", item 2 (fp8 activations with
+ * UE8M0 scales).
+ *   x       bf16 bits [rows][K], 16-byte aligned
+ *   q       e4m3 codes [rows][K], 8-byte aligned
+ *   scales  UE8M0 bytes [rows][ceil(K / 128)]
+ * Requires K % 8 == 0; rows == 0 is a no-op.  Arguments are checked before
+ * the launch. */
+moe_status moe_act_quant(int32_t rows, int32_t K, const uint16_t* x, uint8_t* q, uint8_t* scales,
+                         void* stream);
 
 void moe_plan_free(moe_plan_t plan);
 

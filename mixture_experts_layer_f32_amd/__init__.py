@@ -19,6 +19,7 @@ MOE_OK, MOE_ERR_NULL_ARG, MOE_ERR_BAD_SHAPE, MOE_ERR_UNSUPPORTED = 0, 1, 2, 3
 MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
 MOE_W_E4M3_B128, MOE_W_E2M1_UE8M0_G32, MOE_W_E2M1_E4M3_G16 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
+MOE_ACT_BF16, MOE_ACT_E4M3_G128 = 0, 1
 STAGES = ("router", "topk", "permute", "gateup", "down", "combine")
 WFMT = {"e4m3": MOE_W_E4M3_B128, "e2m1": MOE_W_E2M1_UE8M0_G32, "nvfp4": MOE_W_E2M1_E4M3_G16}
 
@@ -27,7 +28,7 @@ class moe_desc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("wfmt", ctypes.c_int32),
-                ("renorm", ctypes.c_int32), ("path", ctypes.c_int32)]
+                ("renorm", ctypes.c_int32), ("path", ctypes.c_int32), ("act_fmt", ctypes.c_int32)]
 
 
 class moe_mat(ctypes.Structure):
@@ -78,6 +79,8 @@ def _load():
     L.moe_rmsnorm.restype = ctypes.c_int
     L.moe_residual_add.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.moe_residual_add.restype = ctypes.c_int
+    L.moe_act_quant.argtypes = [i32, i32, vp, vp, vp, vp]
+    L.moe_act_quant.restype = ctypes.c_int
     L.moe_plan_free.argtypes = [vp]
     L.moe_plan_free.restype = None
     L.moe_status_str.argtypes = [ctypes.c_int]
@@ -108,11 +111,12 @@ class Plan:
 
 
 def moe_plan(d_model: int, d_ff: int, n_experts: int, top_k: int, max_tokens: int,
-             wfmt: int | str, renorm: bool, path: int = MOE_PATH_AUTO) -> Plan:
+             wfmt: int | str, renorm: bool, path: int = MOE_PATH_AUTO,
+             act_fmt: int = MOE_ACT_BF16) -> Plan:
     if isinstance(wfmt, str):
         wfmt = WFMT[wfmt]
     desc = moe_desc(d_model, d_ff, n_experts, top_k, max_tokens, int(wfmt), int(bool(renorm)),
-                    int(path))
+                    int(path), int(act_fmt))
     h = ctypes.c_void_p()
     st = lib.moe_plan(ctypes.byref(desc), ctypes.byref(h))
     if st != MOE_OK:
@@ -232,3 +236,12 @@ def moe_timing_collect(plan: Plan):
 
 def moe_timing_disable(plan: Plan) -> None:
     lib.moe_timing_disable(plan.handle)
+
+
+def moe_act_quant(x, q, scales, stream=None) -> None:
+    """bf16 rows x [R, K] (bits) -> e4m3 codes q [R, K] and UE8M0 scale bytes
+    [R, ceil(K / 128)]; raises MoeError on a non-OK status."""
+    R, K = x.shape
+    st = lib.moe_act_quant(int(R), int(K), _ptr(x), _ptr(q), _ptr(scales), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_act_quant")

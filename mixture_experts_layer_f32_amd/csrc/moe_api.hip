@@ -17,6 +17,7 @@
 #include "moe_decode.h"
 #include "moe_gemm.h"
 #include "moe_route.h"
+#include "moe_q8.h"
 
 using namespace moe;
 
@@ -29,7 +30,7 @@ constexpr int GEMV_MAX_T = 16;   // router: wavefront GEMV up to this many token
 
 struct Layout {
   size_t logits, ids, w, counts, offsets, perm, inv_perm, tok_of, rank, hist, base, slot_info, n_active,
-      tiles, n_tiles, h, y, total;
+      tiles, n_tiles, h, y, qx, sx, qh, sh, total;
   int nchunk, max_tiles, n_slots;
 };
 
@@ -52,6 +53,7 @@ struct moe_plan_s {
   int small_route_t = 0;  // top-k + permute in one workgroup up to this many tokens (<= 64), 0 = by shape
   int dec_ks = 0;         // MFMA decode wavefronts per workgroup (k-split), 0 = by shape
   int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (11, 12, 22, 23, 24), 0 = by shape
+  int q8_tm = 0;          // gemm_q8 token chunks per wavefront (tile 64 * tm tokens), 0 = by shape
   int gemm_kernel = 3;    // grouped expert stage: 3 = gemm_big (default), 1 = register-weight tiles,
                           // 2 = gemm_dma, 0 = LDS weight tiles
   std::string info;
@@ -67,6 +69,7 @@ struct moe_plan_s {
 namespace {
 
 int path_for(const moe_plan_s* p, int T) {
+  if (p->d.act_fmt == MOE_ACT_E4M3_G128) return MOE_PATH_GROUPED;
   if (p->d.path == MOE_PATH_DECODE) return MOE_PATH_DECODE;
   if (p->d.path == MOE_PATH_GROUPED) return MOE_PATH_GROUPED;
   return T <= p->t_decode ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
@@ -140,9 +143,20 @@ int big_cfg(const moe_plan_s* p, int T) {
 }
 int big_rows(int cfg) { return 32 * (cfg / 10) * (cfg % 10); }
 
+// gemm_q8 tile height 64 * tm tokens (tm 1..3; 4 would spill registers), from
+// the mean slots per expert (an expert of up to one tile streams its weights
+// once)
+int q8_tm(const moe_plan_s* p, int T) {
+  if (p->q8_tm > 0) return p->q8_tm;
+  const long long S = (long long)T * p->d.top_k;
+  const long long mean = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
+  return mean <= 96 ? 2 : 3;
+}
+
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
 // MFMA decode, else the grouped-GEMM tile height.
 int tile_rows(const moe_plan_s* p, int T) {
+  if (p->d.act_fmt == MOE_ACT_E4M3_G128) return 64 * q8_tm(p, T);
   if (use_dec_mfma(p, T)) return 16;
   if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel == 3) return big_rows(big_cfg(p, T));
   if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel >= 1) return 64;
@@ -180,6 +194,11 @@ Layout layout(const moe_plan_s* p, int T) {
   L.n_tiles = take(4);
   L.h = take(S * f * 2);
   L.y = take(S * d * 4);
+  const bool q8 = p->d.act_fmt == MOE_ACT_E4M3_G128;
+  L.qx = take(q8 ? (size_t)T * d : 0);
+  L.sx = take(q8 ? (size_t)T * ((d + 127) / 128) : 0);
+  L.qh = take(q8 ? S * f : 0);
+  L.sh = take(q8 ? S * ((f + 127) / 128) : 0);
   L.total = o;
   return L;
 }
@@ -497,6 +516,61 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
   return MOE_OK;
 }
 
+template <int FMT, bool GATEUP, int TM>
+void launch_q8_cfg(int max_tiles, int N, int K, int T, const uint8_t* aq, const uint8_t* as,
+                   DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles,
+                   const int32_t* tok_of, void* out, hipStream_t st) {
+  constexpr int BNM = Q8Cfg<FMT, GATEUP, TM>::BNM;
+  const int nb = (N + BNM - 1) / BNM;
+  const dim3 g((unsigned)(8LL * ((max_tiles + 7) / 8) * nb));
+  gemm_q8<FMT, GATEUP, TM><<<g, 512, 0, st>>>(aq, as, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb);
+}
+
+template <int FMT, bool GATEUP>
+void launch_q8(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint8_t* aq,
+               const uint8_t* as, DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles,
+               const int32_t* tok_of, void* out, hipStream_t st) {
+  switch (q8_tm(p, T)) {
+    case 1: launch_q8_cfg<FMT, GATEUP, 1>(max_tiles, N, K, T, aq, as, W0, W1, tiles, n_tiles, tok_of, out, st); break;
+    case 2: launch_q8_cfg<FMT, GATEUP, 2>(max_tiles, N, K, T, aq, as, W0, W1, tiles, n_tiles, tok_of, out, st); break;
+    default: launch_q8_cfg<FMT, GATEUP, 3>(max_tiles, N, K, T, aq, as, W0, W1, tiles, n_tiles, tok_of, out, st); break;
+  }
+}
+
+void launch_act_quant(const uint16_t* x, uint8_t* q, uint8_t* sc, long long R, int K, hipStream_t st) {
+  const int ng = (K + 127) / 128;
+  act_quant_e4m3<<<(unsigned)((R * ng + 15) / 16), 256, 0, st>>>(x, q, sc, (int)R, K, ng);
+}
+
+// The activation-quantised expert stage: x quantised, gate/up + SwiGLU on
+// the block-scaled MFMA -> h (bf16), h quantised, down -> y.
+template <int FMT>
+moe_status launch_q8_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, DMat U, DMat D,
+                           const Layout& L, char* ws, float* y_dst, hipStream_t st) {
+  const int d = p->d.d_model, f = p->d.d_ff;
+  const long long S = (long long)T * p->d.top_k;
+  const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
+  const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
+  const int32_t* tok_of = reinterpret_cast<const int32_t*>(ws + L.tok_of);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* y = y_dst ? y_dst : reinterpret_cast<float*>(ws + L.y);
+  uint8_t* qx = reinterpret_cast<uint8_t*>(ws + L.qx);
+  uint8_t* sx = reinterpret_cast<uint8_t*>(ws + L.sx);
+  uint8_t* qh = reinterpret_cast<uint8_t*>(ws + L.qh);
+  uint8_t* sh = reinterpret_cast<uint8_t*>(ws + L.sh);
+  mark(p, MOE_STAGE_GATEUP, false, st);
+  launch_act_quant(x, qx, sx, T, d, st);
+  launch_q8<FMT, true>(p, L.max_tiles, f, d, T, qx, sx, G, U, tiles, n_tiles, tok_of, h, st);
+  mark(p, MOE_STAGE_GATEUP, true, st);
+  mark(p, MOE_STAGE_DOWN, false, st);
+  launch_act_quant(h, qh, sh, S, f, st);
+  launch_q8<FMT, false>(p, L.max_tiles, d, f, T, qh, sh, D, D, tiles, n_tiles, tok_of, y, st);
+  mark(p, MOE_STAGE_DOWN, true, st);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return hip_fail(p, err, "expert stage launch");
+  return MOE_OK;
+}
+
 moe_status check_mat(const moe_plan_s* p, const moe_mat* m) {
   if (m == nullptr || m->q == nullptr || m->scale == nullptr) return MOE_ERR_NULL_ARG;
   if (m->q_expert_stride < 0 || m->s_expert_stride < 0) return MOE_ERR_BAD_SHAPE;
@@ -504,6 +578,10 @@ moe_status check_mat(const moe_plan_s* p, const moe_mat* m) {
   if (p->d.wfmt == MOE_W_E4M3_B128 && (!aligned(m->scale, 4) || m->s_expert_stride % 4))
     return MOE_ERR_ALIGNMENT;
   if (p->d.wfmt == MOE_W_E2M1_E4M3_G16 && (!aligned(m->scale, 2) || m->s_expert_stride % 2))
+    return MOE_ERR_ALIGNMENT;
+  // the activation-quantised e2m1 GEMM reads a row's group scales two at a time
+  if (p->d.act_fmt == MOE_ACT_E4M3_G128 && p->d.wfmt == MOE_W_E2M1_UE8M0_G32 &&
+      (!aligned(m->scale, 2) || m->s_expert_stride % 2))
     return MOE_ERR_ALIGNMENT;
   return MOE_OK;
 }
@@ -535,6 +613,11 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (d.top_k > d.n_experts) return MOE_ERR_BAD_SHAPE;
   if (d.renorm != 0 && d.renorm != 1) return MOE_ERR_BAD_SHAPE;
   if (d.path < MOE_PATH_AUTO || d.path > MOE_PATH_GROUPED) return MOE_ERR_BAD_SHAPE;
+  if (d.act_fmt != MOE_ACT_BF16 && d.act_fmt != MOE_ACT_E4M3_G128) return MOE_ERR_BAD_SHAPE;
+  if (d.act_fmt == MOE_ACT_E4M3_G128) {
+    if (d.wfmt == MOE_W_E2M1_E4M3_G16 || d.path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
+    if (d.wfmt == MOE_W_E2M1_UE8M0_G32 && (d.d_model % 64 || d.d_ff % 64)) return MOE_ERR_UNSUPPORTED;
+  }
   if (d.n_experts > MAX_E || d.top_k > MAX_K) return MOE_ERR_UNSUPPORTED;
   if (d.wfmt == MOE_W_E4M3_B128) {
     if (d.d_model % 128 || d.d_ff % 128) return MOE_ERR_UNSUPPORTED;
@@ -581,6 +664,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (const char* v = std::getenv("MOE_ROUTER_SPLIT")) p->router_split = std::max(0, std::min(8, std::atoi(v)));
   if (const char* v = std::getenv("MOE_SMALL_ROUTE_T")) p->small_route_t = std::max(1, std::min(64, std::atoi(v)));
   if (const char* v = std::getenv("MOE_DEC_KS")) p->dec_ks = std::max(0, std::min(4, std::atoi(v)));
+  if (const char* v = std::getenv("MOE_Q8_TM")) p->q8_tm = std::max(0, std::min(3, std::atoi(v)));
   if (const char* v = std::getenv("MOE_BIG_CFG")) {
     const int c = std::atoi(v);
     p->big_cfg = (c == 11 || c == 12 || c == 22 || c == 23 || c == 24) ? c : 0;
@@ -603,6 +687,9 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
                 d.path == MOE_PATH_AUTO ? "auto" : (d.path == MOE_PATH_DECODE ? "decode" : "grouped"),
                 p->t_decode, GEMV_MAX_T, p->dec_mfma_min_t, p->gemm_kernel);
   p->info = buf;
+  if (d.act_fmt == MOE_ACT_E4M3_G128)
+    p->info += "; activations: e4m3 per 128-input group (UE8M0 scales), grouped path only, "
+               "block-scaled MFMA 32x32x64 (fp8 x fp8 / fp8 x fp4), 128-input stages";
   *out = p;
   return MOE_OK;
 }
@@ -631,6 +718,17 @@ moe_status moe_residual_add(int32_t n_tokens, int32_t d, const uint16_t* residua
   const size_t n4 = (size_t)n_tokens * d / 4;
   residual_add_bf16<<<(unsigned)((n4 + 255) / 256), 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
       residual, a, b, out, n4);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_act_quant(int32_t rows, int32_t K, const uint16_t* x, uint8_t* q, uint8_t* scales,
+                         void* stream) {
+  if (rows < 0 || K <= 0) return MOE_ERR_BAD_SHAPE;
+  if (K % 8) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_NULL_ARG;
+  if (!aligned(x, 16) || !aligned(q, 8)) return MOE_ERR_ALIGNMENT;
+  launch_act_quant(x, q, scales, rows, K, reinterpret_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -859,6 +957,10 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   const DMat D{static_cast<const uint8_t*>(down->q), static_cast<const uint8_t*>(down->scale),
                down->q_expert_stride, down->s_expert_stride};
   float* y_dst = dense ? out : nullptr;
+  if (p->d.act_fmt == MOE_ACT_E4M3_G128)
+    st = p->d.wfmt == MOE_W_E4M3_B128 ? launch_q8_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, y_dst, s)
+                                      : launch_q8_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, y_dst, s);
+  else
   st = p->d.wfmt == MOE_W_E4M3_B128 ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, y_dst, s)
        : p->d.wfmt == MOE_W_E2M1_UE8M0_G32
            ? launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, y_dst, s)

@@ -1,0 +1,353 @@
+// The activation-quantised variant of the expert stage (opt-in per plan).
+// The expert inputs, the token rows x before gate/up and h before down, are
+// cut into groups of 128 consecutive inputs; each group gets a power-of-two
+// scale (a UE8M0 byte) and e4m3 codes (dev.to DeepSeek-V4.1-Flash post,
+// "Three bugs on RTX 50xx that never raise an error", item 2: the model's
+// activation quantiser writes fp8 with UE8M0 scales).  The GEMMs then run on
+// gfx950's block-scaled fp8/fp4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4),
+// whose per-32-input scale operands take the activation scale and the
+// weight's power-of-two scale part, so the weight codes enter the MFMA
+// undecoded.
+#pragma once
+
+#include "moe_gemm.h"
+
+namespace moe {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Quantiser: bf16 rows x [R][K] -> e4m3 codes q [R][K] and UE8M0 bytes
+// s [R][ng], ng = ceil(K / 128); K % 8 == 0.  A group's scale is the
+// smallest 2^E (E >= -127) with max |x| <= 448 * 2^E: for max |x| = fr * 2^ex
+// (fr in [0.5, 1)) that is E = ex - 9, plus one when fr > 0.875 (448 is
+// 0.875 * 2^9); an all-zero group gets byte 127.  A code is the e4m3 value
+// nearest x * 2^-E (exact product; ties to the even mantissa), the sign bit
+// taken from x.  16 lanes per group, 8 inputs per lane, 16 groups per
+// workgroup.
+__global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x,
+                                                      uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ s, int R, int K,
+                                                      int ng) {
+  const long long gid = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  const bool live = gid < (long long)R * ng;
+  const int row = live ? (int)(gid / ng) : 0;
+  const int g = live ? (int)(gid - (long long)row * ng) : 0;
+  const int k = 128 * g + 8 * j;
+  const bool in = live && k < K;
+  const u32x4 v = in ? *reinterpret_cast<const u32x4*>(x + (size_t)row * K + k) : u32x4{0u, 0u, 0u, 0u};
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+  // the 16 lanes of a group are an aligned 16-lane block of the wavefront
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
+  const uint32_t ab = __float_as_uint(am);
+  const int fe = (int)(ab >> 23);  // biased exponent (am >= 0)
+  int E;
+  if (am == 0.0f)
+    E = 0;
+  else if (fe == 0)
+    E = -127;
+  else
+    E = max((fe - 126) - 9 + ((ab & 0x7FFFFFu) > 0x600000u ? 1 : 0), -127);
+  const float mul = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E, E in [-127, 120]
+  uint32_t code[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = fabsf(f[i] * mul);  // below 2^-126 it rounds to a zero code either way
+    const int ee = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+    // a / 2^(ee - 3): an integer 0..16 after rounding; codes are contiguous
+    // across binade edges and from the subnormals into the normals
+    const float r = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - ee) << 23));
+    code[i] = ((__float_as_uint(f[i]) >> 31) << 7) | (uint32_t)(8 * (ee + 6) + (int)r);
+  }
+  if (in) {
+    *reinterpret_cast<u32x2*>(q + (size_t)row * K + k) =
+        u32x2{code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+              code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24};
+    if (j == 0) s[(size_t)row * ng + g] = (uint8_t)(E + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM on quantised activations.  8 wavefronts in a 2 x 4 grid:
+// wavefront (wm, wn) owns TM 32-token chunks of the tile (tokens
+// 32 TM wm ..) and two 32-row weight tiles of column wn (gate/up: gate and up
+// rows 32 wn ..; down: rows 64 wn and 64 wn + 32).  A workgroup covers
+// BM = 64 TM tokens x 128 rows of each matrix (down: 256 rows); 128-input
+// stages (one activation scale group, one e4m3 weight block column) move by
+// direct-to-LDS loads into NS slots, NS - 1 stages in flight.
+//
+// Operands of v_mfma_scale_f32_32x32x64_f8f6f4 (checked on the device):
+//   fp8 A/B: lane (r, h) holds row r's inputs 16 h .. 16 h + 15 in its first
+//   four registers and 32 + 16 h .. 32 + 16 h + 15 in the next four;
+//   fp4 B: lane (r, h) holds inputs 32 h .. 32 h + 31 in four registers, the
+//   lower nibble first;
+//   the scale of row r for inputs 32 b .. 32 b + 31 comes from lane r + 32 b
+//   (its byte 0).
+//   Products of fp8 x fp8 are summed inside the instruction with about 2^-14
+//   relative rounding, so for e4m3 weights each stage's two MFMAs start from
+//   zero and the partial joins the f32 running sum outside (R += m * P, m
+//   the mantissa part of the weight block scale, whose power of two went
+//   into the MFMA's B scale); fp8 x fp4 measured exact, and the e2m1 group
+//   scales are the MFMA's B scales, so those MFMAs accumulate directly.
+//
+// LDS rows: a 128-byte row (activations, e4m3 weights) holds its 16-byte
+// chunk c at slot c ^ ((row >> 1) & 7), a 64-byte fp4 row at c ^ ((row >> 2)
+// & 3), so each 16-lane pass of a fragment read touches 16 bank groups.
+template <int FMT, bool GATEUP, int TM_>
+struct Q8Cfg {
+  static constexpr bool FP4 = FMT != FMT_E4M3;
+  static constexpr int TM = TM_, BM = 64 * TM, BK = 128;
+  static constexpr int TNW = GATEUP ? 1 : 2;
+  static constexpr int BNM = 4 * 32 * TNW;          // weight rows per matrix per workgroup
+  static constexpr int A_V4 = BM * 8;               // u32x4 of activation codes per stage
+  static constexpr int AL = (A_V4 + 511) / 512;     // activation code loads per lane and stage
+  static constexpr int AS = (BM + 63) / 64;         // activation scale loads (wavefronts 0 .. AS-1)
+  static constexpr int WROW = FP4 ? 64 : 128;       // weight bytes per row and stage
+  static constexpr int W_V4 = 8 * 32 * WROW / 16;   // 8 tiles of 32 rows
+  static constexpr int WL = 32 * WROW / 1024;       // weight loads per lane, tile and stage
+  static constexpr int S_DW = FP4 ? 8 * 64 : 0;     // fp4 scale dwords per stage
+  static constexpr int SLOT = 16 * (A_V4 + W_V4) + 4 * (BM + S_DW);
+  static constexpr int NS = 160 * 1024 / SLOT > 4 ? 4 : 160 * 1024 / SLOT;
+  static_assert(NS >= 2, "one stage in flight at least");
+};
+
+template <int FMT, bool GATEUP, int TM_>
+__global__ __launch_bounds__(512, 1) void gemm_q8(
+    const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, DMat W0, DMat W1,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ n_tiles,
+    const int32_t* __restrict__ tok_of, void* __restrict__ out, int N, int K, int T, int nb) {
+  using C = Q8Cfg<FMT, GATEUP, TM_>;
+  constexpr bool FP4 = C::FP4;
+  constexpr int TM = C::TM, BM = C::BM, BK = C::BK, NS = C::NS, AL = C::AL, WL = C::WL;
+  constexpr int TNW = C::TNW;
+  __shared__ u32x4 sA[NS][C::A_V4];
+  __shared__ u32x4 sW[NS][C::W_V4];
+  __shared__ uint32_t sAs[NS][BM];
+  __shared__ uint32_t sWs[NS][C::S_DW > 0 ? C::S_DW : 1];
+  // block order as in gemm_big: XCD x takes tile-list entries x, x + 8, ...
+  const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
+  const int lt = sq / nb, cblk = sq - lt * nb;
+  const int ti = 8 * lt + xcd;
+  if (ti >= *n_tiles) return;
+  const int4 tile = tiles[ti];
+  const int e = tile.x, p_start = tile.y, rows = tile.z;
+  const int n0 = cblk * C::BNM;
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int wm = w >> 2, wn = w & 3;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nw0 = n0 + 32 * TNW * wn;
+  const int nact = min(max(((rows + 31) >> 5) - TM * wm, 0), TM);
+  const int ng = (K + 127) >> 7;  // activation scale groups per row
+
+  // activation rows of this lane's code loads: rows (AL w + i) * 8 + lane / 8
+  // (mod BM; rows past the tile repeat its last row and are not stored)
+  const uint8_t* asrc[AL];
+  int achunk[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int r = ((AL * w + i) * 8 + (lane >> 3)) % BM;
+    const int rr = min(r, rows - 1);
+    const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
+                              : (size_t)(p_start + rr);
+    asrc[i] = aq + src * K;
+    achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+  }
+  // activation scale of tile row 64 w + lane (wavefronts 0 .. AS-1)
+  const bool sload = w < C::AS;
+  const uint8_t* ssrc;
+  {
+    const int r = min(64 * w + lane, BM - 1);
+    const int rr = min(r, rows - 1);
+    const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
+                              : (size_t)(p_start + rr);
+    ssrc = as + src * ng;
+  }
+  // this wavefront loads weight tile wm of its column: tile t = wm is matrix
+  // t (gate/up) or rows 32 t .. of the column (down)
+  const int ml = GATEUP ? wm : 0, jl = GATEUP ? 0 : wm;
+  const DMat& WT = ml == 0 ? W0 : W1;
+  const int64_t rbytes = FP4 ? (int64_t)K / 2 : (int64_t)K;
+  const int sgroups = K >> 5;
+  const uint8_t* wsrc[WL];
+  int wchunk[WL];
+#pragma unroll
+  for (int j = 0; j < WL; ++j) {
+    const int tr = FP4 ? 16 * j + (lane >> 2) : 8 * j + (lane >> 3);
+    wsrc[j] = WT.q + e * WT.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+    wchunk[j] = FP4 ? (lane & 3) ^ ((tr >> 2) & 3) : (lane & 7) ^ ((tr >> 1) & 7);
+  }
+  // fp4 scales: lane (r, half) loads bytes 4 kk + 2 half .. + 1 of row r
+  const uint8_t* wssrc = FP4 ? WT.s + e * WT.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups
+                             : nullptr;
+  // e4m3 block scales of this column's 128-row block: block kb in lane kb % 64
+  // of register kb / 64
+  float scv[GATEUP ? 2 : 1][2];
+  if constexpr (!FP4) {
+    const int kbs = K >> 7;
+#pragma unroll
+    for (int m = 0; m < (GATEUP ? 2 : 1); ++m) {
+      const DMat& W = m == 0 ? W0 : W1;
+      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
+      scv[m][0] = lane < kbs ? sf[lane] : 1.0f;
+      scv[m][1] = lane + 64 < kbs ? sf[lane + 64] : 1.0f;
+    }
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  const int tslot = wn * 2 + wm;  // LDS tile this wavefront loads
+  auto issue = [&](int kk, int slot) {
+    const int k0 = kk * BK;
+#pragma unroll
+    for (int i = 0; i < AL; ++i)
+      lds_dma16(asrc[i] + min(k0 + 16 * achunk[i], K - 16), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
+    if (sload) lds_dma_u8(ssrc + kk, &sAs[slot][(64 * w) % BM]);
+#pragma unroll
+    for (int j = 0; j < WL; ++j)
+      lds_dma16(wsrc[j] + min((int64_t)(FP4 ? k0 / 2 : k0) + 16 * wchunk[j], rbytes - 16),
+                &sW[slot][(tslot * WL + j) * 64]);
+    if constexpr (FP4) lds_dma_u16(wssrc + min(4 * kk + 2 * h, sgroups - 2), &sWs[slot][tslot * 64]);
+  };
+
+  const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x16 R[TM][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) R[i][0] = R[i][1] = zero;
+
+  auto compute = [&](int ks, int slot) {
+    const int k0 = ks * BK;
+    // e4m3: this stage's block scale per weight tile, split into the power of
+    // two (the MFMA's B scale byte: the f32 exponent field) and the mantissa
+    int sb[2];
+    float mt[2];
+    if constexpr (!FP4) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int m = GATEUP ? t : 0;
+        const float sc = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(ks < 64 ? scv[m][0] : scv[m][1]), ks & 63));
+        sb[t] = (int)((__float_as_uint(sc) >> 23) & 0xFF);
+        mt[t] = mant_part(sc);
+      }
+    }
+    // weight operands of both 64-input halves u, decoded never: the codes are
+    // the MFMA's B operand as they are
+    i32x8 b[2][2];
+    int sbl[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int T2 = wn * 2 + t;  // LDS tile
+        if constexpr (!FP4) {
+          const u32x4* row = &sW[slot][T2 * 256 + r32 * 8];
+          const u32x4 lo = row[(4 * u + h) ^ ((r32 >> 1) & 7)];
+          const u32x4 hi = row[(4 * u + 2 + h) ^ ((r32 >> 1) & 7)];
+          b[u][t] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sbl[u][t] = sb[t];
+        } else {
+          const u32x4 v = sW[slot][T2 * 128 + r32 * 4 + ((2 * u + h) ^ ((r32 >> 2) & 3))];
+          b[u][t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          sbl[u][t] = (int)((sWs[slot][T2 * 64 + r32 + 32 * u] >> (8 * h)) & 0xFF);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= nact) break;  // uniform
+      const int mrow = 32 * TM * wm + 32 * i + r32;
+      const u32x4* arow = &sA[slot][mrow * 8];
+      i32x8 a[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c0 = 4 * u + h, c1 = 4 * u + 2 + h;
+        u32x4 lo = arow[c0 ^ ((mrow >> 1) & 7)];
+        u32x4 hi = arow[c1 ^ ((mrow >> 1) & 7)];
+        // inputs past K (an fp4 layer's last, shorter group) contribute zero
+        if (k0 + 16 * c0 >= K) lo = u32x4{0u, 0u, 0u, 0u};
+        if (k0 + 16 * c1 >= K) hi = u32x4{0u, 0u, 0u, 0u};
+        a[u] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      const int sa = (int)(sAs[slot][mrow] & 0xFF);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if constexpr (!FP4) {
+          f32x16 P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0], b[0][t], zero, 0, 0, 0, sa, 0, sbl[0][t]);
+          P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1], b[1][t], P, 0, 0, 0, sa, 0, sbl[1][t]);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) R[i][t][v] = fmaf(mt[t], P[v], R[i][t][v]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            R[i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u], b[u][t], R[i][t], 0, 4, 0, sa, 0,
+                                                                      sbl[u][t]);
+        }
+      }
+    }
+  };
+
+  // loads per lane and stage of this wavefront
+  constexpr int LW0 = AL + WL + (FP4 ? 1 : 0);
+  auto wait_after = [&](int n) {  // all but the loads of the n most recent stages done
+    if (sload) {
+      switch (n) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<LW0 + 1>(); break;
+        default: wait_vm<2 * (LW0 + 1)>(); break;
+      }
+    } else {
+      switch (n) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<LW0>(); break;
+        default: wait_vm<2 * LW0>(); break;
+      }
+    }
+  };
+  static_assert(NS - 2 <= 2, "wait_after covers up to two later stages");
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) issue(p, p);
+  for (int ks0 = 0; ks0 < nk; ks0 += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int ks = ks0 + j;
+      if (ks >= nk) break;
+      wait_after(min(NS - 2, nk - 1 - ks));
+      stage_barrier();
+      if (ks + NS - 1 < nk) issue(ks + NS - 1, (j + NS - 1) % NS);
+      compute(ks, j);
+    }
+  }
+  wait_vm<0>();
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= nact) break;
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 32 * TM * wm + 32 * i + acc_row(v, lane);
+        const int n = nw0 + 32 * j + r32;
+        if (m < rows && n < N) {
+          if (GATEUP) {
+            const float g = R[i][0][v], u = R[i][1][v];
+            reinterpret_cast<uint16_t*>(out)[(size_t)(p_start + m) * N + n] = (uint16_t)f32_to_bf16_rne(silu(g) * u);
+          } else {
+            reinterpret_cast<float*>(out)[(size_t)(p_start + m) * N + n] = R[i][j][v];
+          }
+        }
+      }
+  }
+}
+
+}  // namespace moe

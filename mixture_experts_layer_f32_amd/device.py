@@ -56,10 +56,10 @@ class Runner:
     """A plan for one layer shape plus a workspace sized for `max_tokens`."""
 
     def __init__(self, d: int, f: int, E: int, k: int, fmt: str, renorm: bool, max_tokens: int,
-                 path: int = MOE_PATH_AUTO, device="cuda"):
+                 path: int = MOE_PATH_AUTO, device="cuda", act_fmt: int = 0):
         self.d, self.f, self.E, self.k = d, f, E, k
         self.device = device
-        self.plan: Plan = moe_plan(d, f, E, k, max_tokens, fmt, renorm, path)
+        self.plan: Plan = moe_plan(d, f, E, k, max_tokens, fmt, renorm, path, act_fmt)
         self.max_tokens = max_tokens
         nbytes = max(moe_workspace_size(self.plan, max_tokens), 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -300,10 +300,10 @@ def act_quant_e4m3(bits: np.ndarray, group: int = ACT_GROUP):
     scales = np.zeros((R, ng), np.uint8)
     for g in range(ng):
         blk = x[:, g * group:(g + 1) * group]
-        for r in range(R):
-            b = ue8m0_for(float(np.max(np.abs(blk[r]))) if blk.shape[1] else 0.0)
-            scales[r, g] = b
-            codes[r, g * group:(g + 1) * group] = e4m3_rne(blk[r] / 2.0 ** (b - 127))
+        amax = np.max(np.abs(blk), axis=1)
+        b = np.array([ue8m0_for(float(a)) for a in amax], np.int64)
+        scales[:, g] = b
+        codes[:, g * group:(g + 1) * group] = e4m3_rne(blk / np.ldexp(1.0, b - 127)[:, None])
     return codes, scales
 
 

@@ -39,11 +39,16 @@ def test_status_strings():
     (dict(d_model=200), 3), (dict(d_ff=96), 3), (dict(wfmt=7), 3),
     (dict(wfmt=1, d_model=48), 3), (dict(wfmt=1, d_ff=80), 3),
     (dict(wfmt=2, d_model=48), 3), (dict(wfmt=2, d_ff=80), 3), (dict(wfmt=3), 3),
+    # the activation-quantised variant: unknown act_fmt; NVFP4 weights; the
+    # decode path; e2m1 dims that are multiples of 32 but not of 64
+    (dict(act_fmt=2), 2), (dict(act_fmt=-1), 2), (dict(act_fmt=1, wfmt=2), 3),
+    (dict(act_fmt=1, path=1), 3), (dict(act_fmt=1, wfmt=1, d_model=160), 3),
+    (dict(act_fmt=1, wfmt=1, d_ff=96), 3),
 ])
 def test_descriptor_validation_before_device(fields, status):
     import mixture_experts_layer_f32_amd as m
     base = dict(d_model=256, d_ff=256, n_experts=8, top_k=2, max_tokens=4, wfmt=0, renorm=1,
-                path=0)
+                path=0, act_fmt=0)
     base.update(fields)
     assert m.moe_plan_status(m.moe_desc(**base)) == status
 
@@ -84,3 +89,19 @@ def test_block_step_argument_errors_before_launch():
     assert L.moe_residual_add(4, 64, A, None, None, A, None) == m.MOE_ERR_NULL_ARG
     assert L.moe_residual_add(4, 64, A, A + 8, None, A, None) == m.MOE_ERR_ALIGNMENT
     assert L.moe_residual_add(4, 64, A, A, A + 4, A, None) == m.MOE_ERR_ALIGNMENT
+
+
+def test_act_quant_argument_errors_before_launch():
+    """moe_act_quant checks its arguments before launching (no device here:
+    only calls that must fail, or return early, are made)."""
+    import mixture_experts_layer_f32_amd as m
+    L = m.lib
+    A = 1 << 20   # a 16-byte aligned host-side stand-in; never dereferenced
+    assert L.moe_act_quant(-1, 128, A, A, A, None) == m.MOE_ERR_BAD_SHAPE
+    assert L.moe_act_quant(4, 0, A, A, A, None) == m.MOE_ERR_BAD_SHAPE
+    assert L.moe_act_quant(4, 100, A, A, A, None) == m.MOE_ERR_UNSUPPORTED
+    assert L.moe_act_quant(0, 128, None, None, None, None) == m.MOE_OK
+    assert L.moe_act_quant(4, 128, None, A, A, None) == m.MOE_ERR_NULL_ARG
+    assert L.moe_act_quant(4, 128, A, A, None, None) == m.MOE_ERR_NULL_ARG
+    assert L.moe_act_quant(4, 128, A + 8, A, A, None) == m.MOE_ERR_ALIGNMENT
+    assert L.moe_act_quant(4, 128, A, A + 4, A, None) == m.MOE_ERR_ALIGNMENT

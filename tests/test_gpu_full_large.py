@@ -44,3 +44,28 @@ def test_large_e4m3(layer, T, path):
     check_routing(g, ref)
     mx, rms, mrel = check_out(g["out"][toks], ref.out)
     log(f"max|err| {mx:.3e} rms {rms:.3e} mean rel {mrel:.3e}")
+
+
+@pytest.mark.parametrize("T", [512, 4096])
+def test_large_e4m3_act_quant(layer, T):
+    """The activation-quantised variant (x and h as e4m3 per 128-input group)
+    at full size: routing bit-exact, sampled outputs against the oracle's own
+    quantised layer."""
+    import oracle
+    from gpu_util import omat
+    from test_gpu_actquant import check_h_q8, q8_reference, run_q8
+    L, W = layer
+    batch = synth.make_batch(WL, L, T)
+    toks = sample_tokens(T)
+    log(f"{WL.name} act-quant T={T}: routing by the oracle")
+    ref = oracle.moe_forward(batch.x, L.w_router, batch.bias, omat(L.gate), omat(L.up), omat(L.down),
+                             WL.k, WL.renorm, WL.fmt, tokens=[], act_quant=True)
+    log("gpu")
+    g = run_q8(WL, W, batch)
+    check_routing(g, ref)
+    log(f"oracle steps for tokens {toks}")
+    h_ref, out_ref = q8_reference(WL, L, batch, ref, g["h"], toks)
+    pos = ref.inv_perm.reshape(T, WL.k)[toks]
+    check_h_q8(g["h"][pos.reshape(-1)], h_ref.reshape(-1, WL.f))
+    mx, rms, mrel = check_out(g["out"][toks], out_ref)
+    log(f"max|err| {mx:.3e} rms {rms:.3e} mean rel {mrel:.3e}")
