@@ -144,13 +144,16 @@ int big_cfg(const moe_plan_s* p, int T) {
 int big_rows(int cfg) { return 32 * (cfg / 10) * (cfg % 10); }
 
 // gemm_q8 tile height 64 * tm tokens (tm 1..3; 4 would spill registers), from
-// the mean slots per expert (an expert of up to one tile streams its weights
-// once)
+// the mean slots per expert, as measured on the grouped workloads: 64-token
+// tiles up to 32 (the fp4 layer at 1024 tokens, 16 per expert), 192 up to
+// 160 (the skewed OLMoE shape at 512 tokens, whose hot experts hold about
+// 150, and the d = 7168 layer at 4096, 128 per expert), 128 above (the
+// skewed OLMoE shape at 2048: 256 per expert in two full tiles)
 int q8_tm(const moe_plan_s* p, int T) {
   if (p->q8_tm > 0) return p->q8_tm;
   const long long S = (long long)T * p->d.top_k;
   const long long mean = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
-  return mean <= 96 ? 2 : 3;
+  return mean <= 32 ? 1 : (mean <= 160 ? 3 : 2);
 }
 
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
