@@ -117,9 +117,15 @@ struct Q8Cfg {
   static constexpr int W_V4 = 8 * 32 * WROW / 16;   // 8 tiles of 32 rows
   static constexpr int WL = 32 * WROW / 1024;       // weight loads per lane, tile and stage
   static constexpr int S_DW = FP4 ? 8 * 64 : 0;     // fp4 scale dwords per stage
-  static constexpr int SLOT = 16 * (A_V4 + W_V4) + 4 * (BM + S_DW);
-  static constexpr int NS = 160 * 1024 / SLOT > 4 ? 4 : 160 * 1024 / SLOT;
+  static constexpr int SA_B = 16 * A_V4 + 4 * BM;  // LDS bytes of a stage's activations
+  static constexpr int SW_B = 16 * W_V4 + 4 * S_DW; // ... and of its weights
+  static constexpr int NS = 160 * 1024 / (SA_B + SW_B) > 4 ? 4 : 160 * 1024 / (SA_B + SW_B);
   static_assert(NS >= 2, "one stage in flight at least");
+  // Where a common ring has only 2 slots but 2 activation slots and 3 weight
+  // slots fit, the weights (from HBM) get a stage more lead than the
+  // activations (mostly L2 hits: an entry's rows serve all its column blocks)
+  static constexpr bool SPLIT = NS == 2 && 2 * SA_B + 3 * SW_B <= 160 * 1024;
+  static constexpr int NSA = SPLIT ? 2 : NS, NSW = SPLIT ? 3 : NS;
 };
 
 template <int FMT, bool GATEUP, int TM_>
@@ -130,11 +136,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
   using C = Q8Cfg<FMT, GATEUP, TM_>;
   constexpr bool FP4 = C::FP4;
   constexpr int TM = C::TM, BM = C::BM, BK = C::BK, NS = C::NS, AL = C::AL, WL = C::WL;
-  constexpr int TNW = C::TNW;
-  __shared__ u32x4 sA[NS][C::A_V4];
-  __shared__ u32x4 sW[NS][C::W_V4];
-  __shared__ uint32_t sAs[NS][BM];
-  __shared__ uint32_t sWs[NS][C::S_DW > 0 ? C::S_DW : 1];
+  constexpr int TNW = C::TNW, NSA = C::NSA, NSW = C::NSW;
+  __shared__ u32x4 sA[NSA][C::A_V4];
+  __shared__ u32x4 sW[NSW][C::W_V4];
+  __shared__ uint32_t sAs[NSA][BM];
+  __shared__ uint32_t sWs[NSW][C::S_DW > 0 ? C::S_DW : 1];
   // block order as in gemm_big: XCD x takes tile-list entries x, x + 8, ...
   const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
   const int lt = sq / nb, cblk = sq - lt * nb;
@@ -206,17 +212,26 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
 
   const int nk = (K + BK - 1) / BK;
   const int tslot = wn * 2 + wm;  // LDS tile this wavefront loads
-  auto issue = [&](int kk, int slot) {
+  // a stage's activation loads (codes, then scales), then its weight loads;
+  // the pipelines below rely on this order
+  auto issue_a = [&](int kk, int slot) {
     const int k0 = kk * BK;
 #pragma unroll
     for (int i = 0; i < AL; ++i)
       lds_dma16(asrc[i] + min(k0 + 16 * achunk[i], K - 16), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
     if (sload) lds_dma_u8(ssrc + kk, &sAs[slot][(64 * w) % BM]);
+  };
+  auto issue_w = [&](int kk, int slot) {
+    const int k0 = kk * BK;
 #pragma unroll
     for (int j = 0; j < WL; ++j)
       lds_dma16(wsrc[j] + min((int64_t)(FP4 ? k0 / 2 : k0) + 16 * wchunk[j], rbytes - 16),
                 &sW[slot][(tslot * WL + j) * 64]);
     if constexpr (FP4) lds_dma_u16(wssrc + min(4 * kk + 2 * h, sgroups - 2), &sWs[slot][tslot * 64]);
+  };
+  auto issue = [&](int kk, int slot) {
+    issue_a(kk, slot);
+    issue_w(kk, slot);
   };
 
   const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
 #pragma unroll
   for (int i = 0; i < TM; ++i) R[i][0] = R[i][1] = zero;
 
-  auto compute = [&](int ks, int slot) {
+  auto compute = [&](int ks, int slot, int wslot) {
     const int k0 = ks * BK;
     // e4m3: this stage's block scale per weight tile, split into the power of
     // two (the MFMA's B scale byte: the f32 exponent field) and the mantissa
@@ -250,15 +265,15 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
       for (int t = 0; t < 2; ++t) {
         const int T2 = wn * 2 + t;  // LDS tile
         if constexpr (!FP4) {
-          const u32x4* row = &sW[slot][T2 * 256 + r32 * 8];
+          const u32x4* row = &sW[wslot][T2 * 256 + r32 * 8];
           const u32x4 lo = row[(4 * u + h) ^ ((r32 >> 1) & 7)];
           const u32x4 hi = row[(4 * u + 2 + h) ^ ((r32 >> 1) & 7)];
           b[u][t] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           sbl[u][t] = sb[t];
         } else {
-          const u32x4 v = sW[slot][T2 * 128 + r32 * 4 + ((2 * u + h) ^ ((r32 >> 2) & 3))];
+          const u32x4 v = sW[wslot][T2 * 128 + r32 * 4 + ((2 * u + h) ^ ((r32 >> 2) & 3))];
           b[u][t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sbl[u][t] = (int)((sWs[slot][T2 * 64 + r32 + 32 * u] >> (8 * h)) & 0xFF);
+          sbl[u][t] = (int)((sWs[wslot][T2 * 64 + r32 + 32 * u] >> (8 * h)) & 0xFF);
         }
       }
 #pragma unroll
@@ -313,18 +328,43 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
     }
   };
   static_assert(NS - 2 <= 2, "wait_after covers up to two later stages");
+  if constexpr (C::SPLIT) {
+    // activations of stage ks + 1 and weights of stage ks + 2 are issued at
+    // stage ks (in that order), so at stage ks only the weights issued last
+    // (stage ks + 1's) may still be in flight
+    constexpr int LWW = WL + (FP4 ? 1 : 0);
+    issue_a(0, 0);
+    issue_w(0, 0);
+    if (nk > 1) issue_w(1, 1);
+    for (int ks0 = 0; ks0 < nk; ks0 += 6) {
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nk) issue(p, p);
-  for (int ks0 = 0; ks0 < nk; ks0 += NS) {
+      for (int j = 0; j < 6; ++j) {
+        const int ks = ks0 + j;
+        if (ks >= nk) break;
+        if (ks + 1 < nk)
+          wait_vm<LWW>();
+        else
+          wait_vm<0>();
+        stage_barrier();
+        if (ks + 1 < nk) issue_a(ks + 1, (j + 1) % 2);
+        if (ks + 2 < nk) issue_w(ks + 2, (j + 2) % 3);
+        compute(ks, j % 2, j % 3);
+      }
+    }
+  } else {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int ks = ks0 + j;
-      if (ks >= nk) break;
-      wait_after(min(NS - 2, nk - 1 - ks));
-      stage_barrier();
-      if (ks + NS - 1 < nk) issue(ks + NS - 1, (j + NS - 1) % NS);
-      compute(ks, j);
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nk) issue(p, p);
+    for (int ks0 = 0; ks0 < nk; ks0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int ks = ks0 + j;
+        if (ks >= nk) break;
+        wait_after(min(NS - 2, nk - 1 - ks));
+        stage_barrier();
+        if (ks + NS - 1 < nk) issue(ks + NS - 1, (j + NS - 1) % NS);
+        compute(ks, j, j);
+      }
     }
   }
   wait_vm<0>();
