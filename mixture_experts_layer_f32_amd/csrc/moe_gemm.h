@@ -831,16 +831,23 @@ struct BigCfg {
   static constexpr bool FP4 = FMT != FMT_E4M3;
   static constexpr int NMAT = GATEUP ? 2 : 1;
   static constexpr int WGM = WGM_, WGN = 8 / WGM;      // wavefront grid
-  static constexpr int TM = TM_, BM = 32 * WGM * TM, BK = 64;
+  static constexpr int TM = TM_, BM = 32 * WGM * TM;
+  // fp4 tiles of 128 tokens x 128 rows per matrix take 128-input stages, so
+  // each weight row is read 64 contiguous bytes at a time (32 with 64-input
+  // stages); taller or wider tiles (whose LDS would then hold only 2 stages)
+  // and e4m3 (64 bytes per row already) take 64-input stages
+  static constexpr int BK = FP4 && WGM == 2 && BM <= 128 ? 128 : 64;
+  static constexpr int ACH = BK / 8;                   // 16-byte activation chunks per row and stage
   static constexpr int NW = NMAT * TNW;                // weight tiles per wavefront (2)
   static constexpr int BNM = WGN * 32 * TNW;           // weight rows per matrix per workgroup
-  static constexpr int A_V4 = BM * 8;                  // u32x4 per activation stage (BM x 128 B)
+  static constexpr int A_V4 = BM * ACH;                // u32x4 per activation stage (BM x 2 BK bytes)
   static constexpr int AL = (A_V4 + 511) / 512;        // activation loads per lane and stage
-  static constexpr int WL = FP4 ? 1 : 2;               // weight loads per lane, tile and stage
+  static constexpr int WL = FP4 ? BK / 64 : 2;         // weight loads per lane, tile and stage
+  static constexpr int SL = FP4 ? BK / 64 : 0;         // fp4 scale loads per lane, tile and stage
   static constexpr int TPW = NW / WGM;                 // weight tiles each wavefront loads
   static constexpr int W_V4 = WGN * NW * WL * 64;      // u32x4 per weight stage
-  static constexpr int S_V4 = FP4 ? WGN * NW * 16 : 0; // fp4: one scale dword per lane and tile, after the weights
-  static constexpr int LOADS = AL + TPW * (WL + (FP4 ? 1 : 0));  // direct-to-LDS loads per lane and stage
+  static constexpr int S_V4 = WGN * NW * 16 * SL;      // fp4: SL scale dwords per lane and tile, after the weights
+  static constexpr int LOADS = AL + TPW * (WL + SL);   // direct-to-LDS loads per lane and stage
   static constexpr int SLOT = 16 * (A_V4 + W_V4 + S_V4);
   static constexpr int NS = 160 * 1024 / SLOT > 6 ? 6 : 160 * 1024 / SLOT;  // slots the 160 KB of LDS holds
   static_assert(NS >= 3, "two stages in flight");
@@ -905,20 +912,24 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   // 32-row token chunks of this wavefront that hold rows (uniform, 0..4)
   const int nact = min(max(((rows + 31) >> 5) - TM * wm, 0), TM);
 
-  // activation loads of this lane: AL per stage, rows (AL w + i) * 8 + lane / 8
-  // mod BM (a short tile's rows are loaded twice, to the same place; rows
-  // past the tile repeat its last row, their outputs are not stored), LDS
-  // slot lane % 8 of the row holding chunk slot ^ ((row >> 1) & 7)
+  // activation loads of this lane: AL per stage, rows (AL w + i) * (64 / ACH)
+  // + lane / ACH mod BM (a short tile's rows are loaded twice, to the same
+  // place; rows past the tile repeat its last row, their outputs are not
+  // stored), LDS slot lane % ACH of the row holding chunk slot ^ aswz(row):
+  // 128-byte rows (8 chunks) swizzle by (row >> 1) & 7, 256-byte rows (16
+  // chunks) by row & 15, so each 16-lane pass of a fragment read touches 16
+  // bank groups
+  auto aswz = [](int r) { return C::ACH == 8 ? ((r >> 1) & 7) : (r & 15); };
   const uint16_t* asrc[AL];
   int achunk[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = ((AL * w + i) * 8 + (lane >> 3)) % BM;
+    const int r = ((AL * w + i) * (64 / C::ACH) + lane / C::ACH) % BM;
     const int rr = min(r, rows - 1);
     const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
                               : (size_t)(p_start + rr);
     asrc[i] = act + src * K;
-    achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    achunk[i] = (lane % C::ACH) ^ aswz(r);
   }
   // activation loads of this wavefront that hold rows of the tile (its first
   // n_a; a load of 8 rows all past `rows` is skipped: the MFMAs of rows past
@@ -926,21 +937,24 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   // stale)
   int n_a = 0;
 #pragma unroll
-  for (int i = 0; i < AL; ++i) n_a += (((AL * w + i) * 8) % BM) < rows ? 1 : 0;
+  for (int i = 0; i < AL; ++i) n_a += (((AL * w + i) * (64 / C::ACH)) % BM) < rows ? 1 : 0;
   // the weight tiles this wavefront loads: WGM = 2: tile wm of its column
   // (the other wavefront of the column loads the other); WGM = 1: both.  Tile
   // t is matrix t for gate/up, rows 32 t .. of the column for down; rows are
-  // clamped to N.  e4m3 (64 bytes of a row per stage): load j covers tile rows
-  // 16 j + lane / 4, slot lane % 4 holding chunk slot ^ ((row >> 2) & 3).  fp4
-  // (32 bytes): one load covers the 32 rows, slot lane % 2 of row lane / 2
-  // holding chunk slot ^ ((row >> 3) & 1).  The fp4 scales of lane (r, h):
-  // the group of inputs 32 h .. of row r (e2m1: one UE8M0 byte; NVFP4: the
-  // two e4m3 bytes of its 16-input halves).
+  // clamped to N.  64 bytes of a row per stage (e4m3, and fp4 with 128-input
+  // stages): load j covers tile rows 16 j + lane / 4, slot lane % 4 holding
+  // chunk slot ^ ((row >> 2) & 3).  fp4 with 64-input stages (32 bytes): one
+  // load covers the 32 rows, slot lane % 2 of row lane / 2 holding chunk
+  // slot ^ ((row >> 3) & 1).  The fp4 scales of lane (r, h): those of its
+  // 32-input chunks c = CPL h .. CPL h + CPL - 1 of row r, one load per chunk
+  // (e2m1: one UE8M0 byte; NVFP4: the two e4m3 bytes of its 16-input halves).
+  constexpr int CPL = BK / 64;  // fp4: 32-input chunks per lane and stage
   const int64_t rbytes = FP4 ? (int64_t)K / 2 : (int64_t)K;
   const int sgroups = FMT == FMT_NVFP4 ? K >> 4 : K >> 5;
   int tls[TPW];
   const uint8_t* wsrc[TPW][2];
-  int wchunk = 0;
+  const uint8_t* wsrc16[TPW];  // fp4 with 128-input stages: the rows of load 1 (16 further)
+  int wchunk[2] = {0, 0};
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tl = WGM == 2 ? wm : u;
@@ -954,10 +968,18 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
         wsrc[u][j] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes +
                      16 * ((lane & 3) ^ ((tr >> 2) & 3));
       }
-    } else {
+    } else if constexpr (CPL == 1) {
       const int tr = lane >> 1;
-      wchunk = (lane & 1) ^ ((tr >> 3) & 1);
+      wchunk[0] = (lane & 1) ^ ((tr >> 3) & 1);
       wsrc[u][0] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+      wsrc[u][1] = WL.s + e * WL.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
+    } else {
+      // load j covers tile rows 16 j + lane / 4
+      const int tr = lane >> 2;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wchunk[j] = (lane & 3) ^ (((16 * j + tr) >> 2) & 3);
+      wsrc[u][0] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+      wsrc16[u] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + 16 + tr, N - 1) * rbytes;
       wsrc[u][1] = WL.s + e * WL.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
     }
   }
@@ -993,12 +1015,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
 #pragma unroll
         for (int j = 0; j < 2; ++j) lds_dma16(wsrc[u][j] + k0, &sW[slot][((wn * NW + tl) * 2 + j) * 64]);
       } else {
-        lds_dma16(wsrc[u][0] + min(k0 + 32 * wchunk, K - 32) / 2, &sW[slot][(wn * NW + tl) * 64]);
-        const int kl = min(k0 + 32 * h, K - 32);
-        if constexpr (FMT == FMT_NVFP4)
-          lds_dma_u16(wsrc[u][1] + (kl >> 4), sS(slot) + (wn * NW + tl) * 64);
-        else
-          lds_dma_u8(wsrc[u][1] + (kl >> 5), sS(slot) + (wn * NW + tl) * 64);
+        const int tile = wn * NW + tl;
+        if constexpr (CPL == 1) {
+          lds_dma16(wsrc[u][0] + min(k0 + 32 * wchunk[0], K - 32) / 2, &sW[slot][tile * 64]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            lds_dma16((j == 0 ? wsrc[u][0] : wsrc16[u]) + min(k0 + 32 * wchunk[j], K - 32) / 2,
+                      &sW[slot][(tile * 2 + j) * 64]);
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int kl = min(k0 + 32 * (CPL * h + c), K - 32);
+          if constexpr (FMT == FMT_NVFP4)
+            lds_dma_u16(wsrc[u][1] + (kl >> 4), sS(slot) + (tile * CPL + c) * 64);
+          else
+            lds_dma_u8(wsrc[u][1] + (kl >> 5), sS(slot) + (tile * CPL + c) * 64);
+        }
       }
     }
   };
@@ -1036,7 +1069,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     const u32x4* a_s = sA[slot];
     const u32x4* w_s = sW[slot];
     // this stage's weight fragments, decoded once for all token chunks
-    bf16x8 b[NW][4];
+    constexpr int NSTEP = C::ACH / 2;  // 16-input MFMA steps per stage
+    bf16x8 b[NW][NSTEP];
     if constexpr (!FP4) {
 #pragma unroll
       for (int t = 0; t < NW; ++t)
@@ -1048,19 +1082,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
           b[t][2 * q + 1] = e4m3x8_scaled_to_bf16(v.z, v.w, ps);
         }
     } else {
-      const bool ktail = ks * BK + 32 * h >= K;  // this lane's inputs lie past K
 #pragma unroll
       for (int t = 0; t < NW; ++t) {
-        u32x4 v = w_s[(wn * NW + t) * 64 + r32 * 2 + (h ^ ((r32 >> 3) & 1))];
-        if (ktail) v = u32x4{0u, 0u, 0u, 0u};
-        const uint32_t sb = sS(slot)[(wn * NW + t) * 64 + lane];
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if constexpr (FMT == FMT_NVFP4)
-            b[t][q] = nvfp4x8_to_bf16(wd[q], e4m3_to_f32(q < 2 ? (sb & 0xFF) : (sb >> 8)));
-          else
-            b[t][q] = e2m1x8_to_bf16(wd[q], ue8m0_to_f32(sb));
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = CPL * h + c;  // this lane's 32-input chunk of the stage
+          u32x4 v = CPL == 1 ? w_s[(wn * NW + t) * 64 + r32 * 2 + (h ^ ((r32 >> 3) & 1))]
+                             : w_s[(wn * NW + t) * 128 + r32 * 4 + (ch ^ ((r32 >> 2) & 3))];
+          if (ks * BK + 32 * ch >= K) v = u32x4{0u, 0u, 0u, 0u};  // inputs past K
+          const uint32_t sb = sS(slot)[((wn * NW + t) * CPL + c) * 64 + lane];
+          const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (FMT == FMT_NVFP4)
+              b[t][4 * c + q] = nvfp4x8_to_bf16(wd[q], e4m3_to_f32(q < 2 ? (sb & 0xFF) : (sb >> 8)));
+            else
+              b[t][4 * c + q] = e2m1x8_to_bf16(wd[q], ue8m0_to_f32(sb));
+          }
         }
       }
     }
@@ -1077,8 +1115,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
       }
       const int mrow = 32 * TM * wm + 32 * i + r32;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, a_s[mrow * 8 + ((4 * h + s) ^ ((mrow >> 1) & 7))]);
+      for (int s = 0; s < NSTEP; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, a_s[mrow * C::ACH + ((NSTEP * h + s) ^ aswz(mrow))]);
 #pragma unroll
         for (int t = 0; t < NW; ++t) R[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[t][s], R[i][t], 0, 0, 0);
       }
