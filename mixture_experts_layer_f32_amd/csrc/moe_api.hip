@@ -651,11 +651,11 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   p->arch = prop.gcnArchName;
   // Decode (every selected expert's weights streamed once per 16 of its slots)
   // while the slots per expert stay small; measured crossovers against the
-  // grouped GEMM (gemm_big): T*k about 10*E (OLMoE shape: decode ahead at
-  // T = 64, grouped at 96; the d = 7168 layer: decode at 256, grouped at 384;
-  // the e2m1 fp4 layer: decode at 512, grouped at 768), 12*E for NVFP4 (even
-  // at T = 768).
-  p->t_decode = std::max(1, (d.wfmt == MOE_W_E2M1_E4M3_G16 ? 12 : 10) * d.n_experts / d.top_k);
+  // grouped GEMM (gemm_big): T*k about 10*E for e4m3 (OLMoE shape: decode
+  // ahead at T = 64, grouped at 96; the d = 7168 layer: decode at 256,
+  // grouped at 384), 14*E for fp4 (the e2m1 and NVFP4 layers: decode ahead at
+  // 768 by 6 and 4 %, grouped at 1024 by 12 and 14 %).
+  p->t_decode = std::max(1, (d.wfmt == MOE_W_E4M3_B128 ? 10 : 14) * d.n_experts / d.top_k);
   // tuning knobs of the decode matvec
   if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
   if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
