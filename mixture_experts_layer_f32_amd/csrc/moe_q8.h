@@ -107,17 +107,25 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
 template <int FMT, bool GATEUP, int TM_>
 struct Q8Cfg {
   static constexpr bool FP4 = FMT != FMT_E4M3;
-  static constexpr int TM = TM_, BM = 64 * TM, BK = 128;
+  static constexpr int TM = TM_, BM = 64 * TM;
+  // fp4 on 64-token tiles: 256-input stages, so each weight row is read 128
+  // contiguous bytes at a time (64 with 128-input stages); otherwise 128
+  static constexpr int BK = FP4 && TM == 1 ? 256 : 128;
+  static constexpr int NU = BK / 64;                // MFMAs per token chunk and weight tile per stage
   static constexpr int TNW = GATEUP ? 1 : 2;
   static constexpr int BNM = 4 * 32 * TNW;          // weight rows per matrix per workgroup
-  static constexpr int A_V4 = BM * 8;               // u32x4 of activation codes per stage
+  static constexpr int ACH = BK / 16;               // 16-byte activation chunks per row and stage
+  static constexpr int A_V4 = BM * ACH;             // u32x4 of activation codes per stage
   static constexpr int AL = (A_V4 + 511) / 512;     // activation code loads per lane and stage
   static constexpr int AS = (BM + 63) / 64;         // activation scale loads (wavefronts 0 .. AS-1)
-  static constexpr int WROW = FP4 ? 64 : 128;       // weight bytes per row and stage
+  static constexpr int AG = BK / 128;               // activation scale groups per stage
+  static constexpr int WROW = FP4 ? BK / 2 : 128;   // weight bytes per row and stage
+  static constexpr int WCH = WROW / 16;             // 16-byte weight chunks per row and stage
   static constexpr int W_V4 = 8 * 32 * WROW / 16;   // 8 tiles of 32 rows
   static constexpr int WL = 32 * WROW / 1024;       // weight loads per lane, tile and stage
-  static constexpr int S_DW = FP4 ? 8 * 64 : 0;     // fp4 scale dwords per stage
-  static constexpr int SA_B = 16 * A_V4 + 4 * BM;  // LDS bytes of a stage's activations
+  static constexpr int SG = FP4 ? BK / 128 : 0;     // fp4 scale loads per lane, tile and stage
+  static constexpr int S_DW = 8 * 64 * SG;          // fp4 scale dwords per stage
+  static constexpr int SA_B = 16 * A_V4 + 4 * AG * BM;  // LDS bytes of a stage's activations
   static constexpr int SW_B = 16 * W_V4 + 4 * S_DW; // ... and of its weights
   static constexpr int NS = 160 * 1024 / (SA_B + SW_B) > 4 ? 4 : 160 * 1024 / (SA_B + SW_B);
   static_assert(NS >= 2, "one stage in flight at least");
@@ -136,10 +144,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
   using C = Q8Cfg<FMT, GATEUP, TM_>;
   constexpr bool FP4 = C::FP4;
   constexpr int TM = C::TM, BM = C::BM, BK = C::BK, NS = C::NS, AL = C::AL, WL = C::WL;
-  constexpr int TNW = C::TNW, NSA = C::NSA, NSW = C::NSW;
+  constexpr int TNW = C::TNW, NSA = C::NSA, NSW = C::NSW, ACH = C::ACH, WCH = C::WCH, NU = C::NU;
+  constexpr int AG = C::AG, SG = C::SG;
   __shared__ u32x4 sA[NSA][C::A_V4];
   __shared__ u32x4 sW[NSW][C::W_V4];
-  __shared__ uint32_t sAs[NSA][BM];
+  __shared__ uint32_t sAs[NSA][AG * BM];
   __shared__ uint32_t sWs[NSW][C::S_DW > 0 ? C::S_DW : 1];
   // block order as in gemm_big: XCD x takes tile-list entries x, x + 8, ...
   const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
@@ -156,18 +165,22 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
   const int nact = min(max(((rows + 31) >> 5) - TM * wm, 0), TM);
   const int ng = (K + 127) >> 7;  // activation scale groups per row
 
-  // activation rows of this lane's code loads: rows (AL w + i) * 8 + lane / 8
-  // (mod BM; rows past the tile repeat its last row and are not stored)
+  // activation rows of this lane's code loads: rows (AL w + i) * (64 / ACH) +
+  // lane / ACH (mod BM; rows past the tile repeat its last row and are not
+  // stored); a 128-byte row holds chunk c at slot c ^ ((row >> 1) & 7), a
+  // 256-byte row at c ^ (row & 15)
+  auto aswz = [](int r) { return ACH == 8 ? ((r >> 1) & 7) : (r & 15); };
+  auto wswz = [](int r) { return WCH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3); };
   const uint8_t* asrc[AL];
   int achunk[AL];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = ((AL * w + i) * 8 + (lane >> 3)) % BM;
+    const int r = ((AL * w + i) * (64 / ACH) + lane / ACH) % BM;
     const int rr = min(r, rows - 1);
     const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
                               : (size_t)(p_start + rr);
     asrc[i] = aq + src * K;
-    achunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    achunk[i] = (lane % ACH) ^ aswz(r);
   }
   // activation scale of tile row 64 w + lane (wavefronts 0 .. AS-1)
   const bool sload = w < C::AS;
@@ -189,11 +202,12 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
   int wchunk[WL];
 #pragma unroll
   for (int j = 0; j < WL; ++j) {
-    const int tr = FP4 ? 16 * j + (lane >> 2) : 8 * j + (lane >> 3);
+    const int tr = (64 / WCH) * j + lane / WCH;
     wsrc[j] = WT.q + e * WT.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
-    wchunk[j] = FP4 ? (lane & 3) ^ ((tr >> 2) & 3) : (lane & 7) ^ ((tr >> 1) & 7);
+    wchunk[j] = (lane % WCH) ^ wswz(tr);
   }
-  // fp4 scales: lane (r, half) loads bytes 4 kk + 2 half .. + 1 of row r
+  // fp4 scales: load c of lane (r, half) brings the bytes (BK / 32) kk + 4 c +
+  // 2 half .. + 1 of row r
   const uint8_t* wssrc = FP4 ? WT.s + e * WT.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups
                              : nullptr;
   // e4m3 block scales of this column's 128-row block: block kb in lane kb % 64
@@ -219,7 +233,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
 #pragma unroll
     for (int i = 0; i < AL; ++i)
       lds_dma16(asrc[i] + min(k0 + 16 * achunk[i], K - 16), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
-    if (sload) lds_dma_u8(ssrc + kk, &sAs[slot][(64 * w) % BM]);
+    if (sload)
+#pragma unroll
+      for (int g = 0; g < AG; ++g) lds_dma_u8(ssrc + min(AG * kk + g, ng - 1), &sAs[slot][g * BM + (64 * w) % BM]);
   };
   auto issue_w = [&](int kk, int slot) {
     const int k0 = kk * BK;
@@ -227,7 +243,10 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
     for (int j = 0; j < WL; ++j)
       lds_dma16(wsrc[j] + min((int64_t)(FP4 ? k0 / 2 : k0) + 16 * wchunk[j], rbytes - 16),
                 &sW[slot][(tslot * WL + j) * 64]);
-    if constexpr (FP4) lds_dma_u16(wssrc + min(4 * kk + 2 * h, sgroups - 2), &sWs[slot][tslot * 64]);
+    if constexpr (FP4)
+#pragma unroll
+      for (int c = 0; c < SG; ++c)
+        lds_dma_u16(wssrc + min((BK / 32) * kk + 4 * c + 2 * h, sgroups - 2), &sWs[slot][(tslot * SG + c) * 64]);
   };
   auto issue = [&](int kk, int slot) {
     issue_a(kk, slot);
@@ -257,10 +276,10 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
     }
     // weight operands of both 64-input halves u, decoded never: the codes are
     // the MFMA's B operand as they are
-    i32x8 b[2][2];
-    int sbl[2][2];
+    i32x8 b[NU][2];
+    int sbl[NU][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int T2 = wn * 2 + t;  // LDS tile
@@ -271,22 +290,22 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
           b[u][t] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
           sbl[u][t] = sb[t];
         } else {
-          const u32x4 v = sW[wslot][T2 * 128 + r32 * 4 + ((2 * u + h) ^ ((r32 >> 2) & 3))];
+          const u32x4 v = sW[wslot][T2 * 32 * WCH + r32 * WCH + ((2 * u + h) ^ wswz(r32))];
           b[u][t] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sbl[u][t] = (int)((sWs[wslot][T2 * 64 + r32 + 32 * u] >> (8 * h)) & 0xFF);
+          sbl[u][t] = (int)((sWs[wslot][(T2 * SG + (u >> 1)) * 64 + r32 + 32 * (u & 1)] >> (8 * h)) & 0xFF);
         }
       }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i >= nact) break;  // uniform
       const int mrow = 32 * TM * wm + 32 * i + r32;
-      const u32x4* arow = &sA[slot][mrow * 8];
-      i32x8 a[2];
+      const u32x4* arow = &sA[slot][mrow * ACH];
+      i32x8 a[NU];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int c0 = 4 * u + h, c1 = 4 * u + 2 + h;
-        u32x4 lo = arow[c0 ^ ((mrow >> 1) & 7)];
-        u32x4 hi = arow[c1 ^ ((mrow >> 1) & 7)];
+        u32x4 lo = arow[c0 ^ aswz(mrow)];
+        u32x4 hi = arow[c1 ^ aswz(mrow)];
         // inputs past K (an fp4 layer's last, shorter group) contribute zero
         if (k0 + 16 * c0 >= K) lo = u32x4{0u, 0u, 0u, 0u};
         if (k0 + 16 * c1 >= K) hi = u32x4{0u, 0u, 0u, 0u};
@@ -302,22 +321,25 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
           for (int v = 0; v < 16; ++v) R[i][t][v] = fmaf(mt[t], P[v], R[i][t][v]);
         } else {
 #pragma unroll
-          for (int u = 0; u < 2; ++u)
-            R[i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u], b[u][t], R[i][t], 0, 4, 0, sa, 0,
+          for (int u = 0; u < NU; ++u) {
+            // the activation scale of the 128-input group holding these 64 inputs
+            const int sau = u < 2 ? sa : (int)(sAs[slot][BM + mrow] & 0xFF);
+            R[i][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[u], b[u][t], R[i][t], 0, 4, 0, sau, 0,
                                                                       sbl[u][t]);
+          }
         }
       }
     }
   };
 
   // loads per lane and stage of this wavefront
-  constexpr int LW0 = AL + WL + (FP4 ? 1 : 0);
+  constexpr int LW0 = AL + WL + SG;
   auto wait_after = [&](int n) {  // all but the loads of the n most recent stages done
     if (sload) {
       switch (n) {
         case 0: wait_vm<0>(); break;
-        case 1: wait_vm<LW0 + 1>(); break;
-        default: wait_vm<2 * (LW0 + 1)>(); break;
+        case 1: wait_vm<LW0 + AG>(); break;
+        default: wait_vm<2 * (LW0 + AG)>(); break;
       }
     } else {
       switch (n) {
@@ -332,7 +354,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
     // activations of stage ks + 1 and weights of stage ks + 2 are issued at
     // stage ks (in that order), so at stage ks only the weights issued last
     // (stage ks + 1's) may still be in flight
-    constexpr int LWW = WL + (FP4 ? 1 : 0);
+    constexpr int LWW = WL + SG;
     issue_a(0, 0);
     issue_w(0, 0);
     if (nk > 1) issue_w(1, 1);

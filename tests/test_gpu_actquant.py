@@ -170,3 +170,21 @@ def test_act_quant_differs_from_bf16_layer():
     assert 1e-3 < rel < 0.1, rel
     g, _ = gpu_run(wl, W, batch, 2)
     check_out(g["out"], ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_act_quant_dense_branch(fmt):
+    """A one-expert top-1 plan with quantised activations (the dense branch of
+    the block): identity routing with weight 1, the down projection writing
+    out directly, against the oracle's quantised layer with E = 1, k = 1."""
+    base = WLS[fmt]
+    wl = synth.Workload(f"aq-dense-{fmt}", base.d, base.f, 1, 1, fmt, True, (100,), False, 5111)
+    layer = synth.make_layer(wl)
+    W = device_weights(layer)
+    batch = synth.make_batch(wl, layer, 100)
+    ref = oracle_q8(wl, layer, batch)
+    g = run_q8(wl, W, batch)
+    assert np.all(g["topk_ids"] == 0) and np.all(g["topk_w"] == 1.0)
+    check_h_q8(g["h"], ref.h)
+    _, out_ref = q8_reference(wl, layer, batch, ref, g["h"], np.arange(100))
+    check_out(g["out"], out_ref)
