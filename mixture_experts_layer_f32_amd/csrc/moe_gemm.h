@@ -812,8 +812,9 @@ namespace moe {
 // flight), one workgroup per CU.
 // LDS layouts (64 banks of 4 bytes; a 16-byte read serves 16 lanes per
 // pass): activation row r (128 bytes per 64-input stage) holds its 16-byte
-// chunk c at slot c ^ ((r >> 1) & 7); an e4m3 weight row (64 bytes) its chunk
-// c at slot c ^ ((r >> 2) & 3), an fp4 row (32 bytes) at c ^ ((r >> 3) & 1),
+// chunk c at slot c ^ ((r >> 1) & 7), or (256 bytes per 128-input stage) at
+// c ^ (r & 15); a 64-byte weight row (e4m3, or fp4 in a 128-input stage) its
+// chunk c at slot c ^ ((r >> 2) & 3), a 32-byte fp4 row at c ^ ((r >> 3) & 1),
 // so the fragment reads of 16 consecutive rows touch 16 different bank
 // groups; each weight load instruction covers whole 64- or 32-byte row
 // segments.

@@ -84,8 +84,9 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
 // 32 TM wm ..) and two 32-row weight tiles of column wn (gate/up: gate and up
 // rows 32 wn ..; down: rows 64 wn and 64 wn + 32).  A workgroup covers
 // BM = 64 TM tokens x 128 rows of each matrix (down: 256 rows); 128-input
-// stages (one activation scale group, one e4m3 weight block column) move by
-// direct-to-LDS loads into NS slots, NS - 1 stages in flight.
+// stages (one activation scale group, one e4m3 weight block column; e2m1 on
+// 64-token tiles: 256-input stages, two groups) move by direct-to-LDS loads
+// into NS slots, NS - 1 stages in flight.
 //
 // Operands of v_mfma_scale_f32_32x32x64_f8f6f4 (checked on the device):
 //   fp8 A/B: lane (r, h) holds row r's inputs 16 h .. 16 h + 15 in its first
@@ -94,16 +95,20 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
 //   lower nibble first;
 //   the scale of row r for inputs 32 b .. 32 b + 31 comes from lane r + 32 b
 //   (its byte 0).
-//   Products of fp8 x fp8 are summed inside the instruction with about 2^-14
-//   relative rounding, so for e4m3 weights each stage's two MFMAs start from
-//   zero and the partial joins the f32 running sum outside (R += m * P, m
-//   the mantissa part of the weight block scale, whose power of two went
-//   into the MFMA's B scale); fp8 x fp4 measured exact, and the e2m1 group
-//   scales are the MFMA's B scales, so those MFMAs accumulate directly.
+//   The instruction rounds its 64-product sum at about 2^-14 of the sum's
+//   magnitude (fp8 x fp8; fp8 x fp4 came out exact) and adds C at f32
+//   precision (measured).
+// e4m3 weights: each stage's two MFMAs start from zero, with the power of two
+// of the stage's block scale as their B scale, and the partial joins the f32
+// running sum with one FMA by the scale's mantissa (R += m * P).  e2m1: the
+// group scales are the MFMA's B scales as they are, so the MFMAs accumulate
+// into R directly.
 //
-// LDS rows: a 128-byte row (activations, e4m3 weights) holds its 16-byte
-// chunk c at slot c ^ ((row >> 1) & 7), a 64-byte fp4 row at c ^ ((row >> 2)
-// & 3), so each 16-lane pass of a fragment read touches 16 bank groups.
+// LDS rows: a 128-byte row (activations, e4m3 weights, fp4 weights of a
+// 256-input stage) holds its 16-byte chunk c at slot c ^ ((row >> 1) & 7), a
+// 256-byte activation row at c ^ (row & 15), a 64-byte fp4 row at
+// c ^ ((row >> 2) & 3), so each 16-lane pass of a fragment read touches 16
+// bank groups.
 template <int FMT, bool GATEUP, int TM_>
 struct Q8Cfg {
   static constexpr bool FP4 = FMT != FMT_E4M3;
