@@ -248,3 +248,19 @@ def test_largest_expert_count_and_top_k(wl, T, path):
     check_routing(g, ref)
     check_h(g["h"], ref.h)
     check_out(g["out"], ref.out)
+
+
+@pytest.mark.parametrize("T", [1, 16, 100])
+def test_largest_expert_count_and_top_k_act_quant(T):
+    """The same limits (1024 experts, top-16) on the activation-quantised plan:
+    routing bit-exact, h and out against the oracle's quantised layer (down
+    fed the GPU's own h)."""
+    from test_gpu_actquant import check_h_q8, oracle_q8, q8_reference, run_q8
+    L, W = get(WL_MAX)
+    batch = synth.make_batch(WL_MAX, L, T)
+    ref = oracle_q8(WL_MAX, L, batch)
+    g = run_q8(WL_MAX, W, batch)
+    check_routing(g, ref)
+    check_h_q8(g["h"], ref.h)
+    _, out_ref = q8_reference(WL_MAX, L, batch, ref, g["h"], np.arange(T))
+    check_out(g["out"], out_ref)

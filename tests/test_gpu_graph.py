@@ -12,15 +12,19 @@ from gpu_util import device_weights
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("wl_name,T", [("olmoe-decode", 8), ("tiny", 4), ("olmoe-prefill-skewed", 128)])
-def test_graph_replay_matches_eager(wl_name, T):
+@pytest.mark.parametrize("wl_name,T,act_fmt", [("olmoe-decode", 8, 0), ("tiny", 4, 0),
+                                               ("olmoe-prefill-skewed", 128, 0),
+                                               ("olmoe-prefill-skewed", 128, 1)])
+def test_graph_replay_matches_eager(wl_name, T, act_fmt):
+    """act_fmt 1: the activation-quantised plan (its two quantiser launches
+    and the block-scaled GEMMs) captured the same way."""
     import torch
     from mixture_experts_layer_f32_amd.device import Runner, to_dev
     wl = synth.WORKLOADS[wl_name]
     layer = synth.make_layer(wl)
     W = device_weights(layer)
     batches = [synth.make_batch(wl, layer, T, batch_index=i) for i in range(3)]
-    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T)
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, act_fmt=act_fmt)
     x_static = to_dev(batches[0].x)
     has_bias = batches[0].bias is not None
     b_static = to_dev(batches[0].bias) if has_bias else None
