@@ -281,8 +281,10 @@ def main():
     mfma = used_path == "grouped" or (os.environ.get("MOE_DEC_KERNEL", "1") != "0"
                                       and T >= int(os.environ.get("MOE_DEC_MFMA_MIN_T", "2")))
     dtype = "bf16-mfma/f32-acc" if mfma else "bf16-dot2/f32-acc"
-    if args.act_quant:
+    if args.act_quant and used_path == "grouped":
         dtype = "e4m3xe4m3-mfma/f32-acc" if wl.fmt == "e4m3" else "e4m3xe2m1-mfma/f32-acc"
+    elif args.act_quant:  # the decode kernels on the quantised activations as bf16
+        dtype = "e4m3-act-dequantised/" + dtype
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -332,7 +334,7 @@ def main():
     dom = max(("gateup", "down"), key=lambda s: stage_avg_us[s])
     dur_s = stage_avg_us[dom] * 1e-6
     intensity = flops[dom] / nbytes[dom]
-    peak_mfma = PEAK_FP8_TFLOPS if args.act_quant else PEAK_BF16_TFLOPS
+    peak_mfma = PEAK_FP8_TFLOPS if args.act_quant and used_path == "grouped" else PEAK_BF16_TFLOPS
     if intensity > peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved, peak, unit, bound = flops[dom] / dur_s / 1e12, peak_mfma, "TFLOP/s", "mfma"
     else:

@@ -91,10 +91,11 @@ typedef enum {
    * max|x| <= 448 * 2^E (UE8M0 byte E + 127; 127 for an all-zero group),
    * codes = e4m3 nearest x / 2^E (ties to even, the sign kept); a row whose
    * length is not a multiple of 128 ends in a shorter group.  The GEMMs run
-   * on gfx950's block-scaled fp8/fp4 MFMA with f32 accumulation.  Weights
-   * e4m3 or e2m1 (not NVFP4, whose e4m3 group scales are not powers of two);
-   * e2m1 needs d_model % 64 == 0 and d_ff % 64 == 0 and 2-byte aligned
-   * scales.  Always the grouped path (MOE_PATH_DECODE is refused). */
+   * on gfx950's block-scaled fp8/fp4 MFMA with f32 accumulation on the
+   * grouped path; on the decode path the quantised values (code * 2^E, exact
+   * in bf16) go through the decode kernels.  Weights e4m3 or e2m1 (not
+   * NVFP4, whose e4m3 group scales are not powers of two); e2m1 needs
+   * d_model % 64 == 0 and d_ff % 64 == 0 and 2-byte aligned scales. */
   MOE_ACT_E4M3_G128 = 1
 } moe_act_fmt;
 

@@ -30,7 +30,7 @@ constexpr int GEMV_MAX_T = 16;   // router: wavefront GEMV up to this many token
 
 struct Layout {
   size_t logits, ids, w, counts, offsets, perm, inv_perm, tok_of, rank, hist, base, slot_info, n_active,
-      tiles, n_tiles, h, y, qx, sx, qh, sh, total;
+      tiles, n_tiles, h, y, xq, hq, qx, sx, qh, sh, total;
   int nchunk, max_tiles, n_slots;
 };
 
@@ -69,7 +69,6 @@ struct moe_plan_s {
 namespace {
 
 int path_for(const moe_plan_s* p, int T) {
-  if (p->d.act_fmt == MOE_ACT_E4M3_G128) return MOE_PATH_GROUPED;
   if (p->d.path == MOE_PATH_DECODE) return MOE_PATH_DECODE;
   if (p->d.path == MOE_PATH_GROUPED) return MOE_PATH_GROUPED;
   return T <= p->t_decode ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
@@ -159,7 +158,7 @@ int q8_tm(const moe_plan_s* p, int T) {
 // Rows per entry of the routing stage's tile list: 16-slot entries for the
 // MFMA decode, else the grouped-GEMM tile height.
 int tile_rows(const moe_plan_s* p, int T) {
-  if (p->d.act_fmt == MOE_ACT_E4M3_G128) return 64 * q8_tm(p, T);
+  if (p->d.act_fmt == MOE_ACT_E4M3_G128 && path_for(p, T) == MOE_PATH_GROUPED) return 64 * q8_tm(p, T);
   if (use_dec_mfma(p, T)) return 16;
   if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel == 3) return big_rows(big_cfg(p, T));
   if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel >= 1) return 64;
@@ -198,6 +197,8 @@ Layout layout(const moe_plan_s* p, int T) {
   L.h = take(S * f * 2);
   L.y = take(S * d * 4);
   const bool q8 = p->d.act_fmt == MOE_ACT_E4M3_G128;
+  L.xq = take(q8 ? (size_t)T * d * 2 : 0);  // decode path: the quantised x as bf16
+  L.hq = take(q8 ? S * f * 2 : 0);           // ... and the quantised h
   L.qx = take(q8 ? (size_t)T * d : 0);
   L.sx = take(q8 ? (size_t)T * ((d + 127) / 128) : 0);
   L.qh = take(q8 ? S * f : 0);
@@ -373,13 +374,27 @@ void launch_gemm(const moe_plan_s* p, int max_tiles, int N, int K, int T, const 
 }
 
 // y_dst: where the down projection writes y (NULL: the workspace).
+void launch_act_qdq(const uint16_t* x, uint16_t* y, long long R, int K, hipStream_t st) {
+  const int ng = (K + 127) / 128;
+  act_qdq_bf16<<<(unsigned)((R * ng + 15) / 16), 256, 0, st>>>(x, y, (int)R, K, ng);
+}
+
+// qdq (activation-quantised plans on the decode path): the gate/up kernels
+// read x's quantised values as bf16 and the down kernels h's (act_qdq_bf16
+// into workspace copies, launched inside the stages' timing events); h
+// itself stays the bf16 gate/up output.
 template <int FMT>
-moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, DMat U, DMat D,
-                               const Layout& L, char* ws, float* y_dst, hipStream_t st) {
+moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat G, DMat U, DMat D,
+                               const Layout& L, char* ws, float* y_dst, hipStream_t st, bool qdq = false) {
   const int d = p->d.d_model, f = p->d.d_ff;
+  const long long S_all = (long long)T * p->d.top_k;
+  uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq);
+  const uint16_t* x = qdq ? xq : x_in;
+  uint16_t* hq = reinterpret_cast<uint16_t*>(ws + L.hq);
   const int4* info = reinterpret_cast<const int4*>(ws + L.slot_info);
   const int32_t* tok_of = reinterpret_cast<const int32_t*>(ws + L.tok_of);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  const uint16_t* hd = qdq ? hq : h;  // what the down projection reads
   float* y = y_dst ? y_dst : reinterpret_cast<float*>(ws + L.y);
   // Persistent decode grid (CUs x persist workgroups walking (expert, row pair)
   // items) when each wavefront gets a few items: measured faster there, and
@@ -423,21 +438,24 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
           dec_mfma<FMT, true, 1, 2><<<g3, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
       } else {
         if (tall)
-          dec_mfma<FMT, false, 4, 2><<<g2, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+          dec_mfma<FMT, false, 4, 2><<<g2, blk, 0, st>>>(hd, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
         else
-          dec_mfma<FMT, false, 2, 2><<<g3, blk, 0, st>>>(h, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
+          dec_mfma<FMT, false, 2, 2><<<g3, blk, 0, st>>>(hd, h_bytes, D, D, tiles, n_tiles, tok_of, y, d, f, T);
       }
     };
     mark(p, MOE_STAGE_GATEUP, false, st);
+    if (qdq) launch_act_qdq(x_in, xq, T, d, st);
     run(true);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
+    if (qdq) launch_act_qdq(h, hq, S_all, f, st);
     run(false);
     mark(p, MOE_STAGE_DOWN, true, st);
   } else if (path_for(p, T) == MOE_PATH_DECODE && persist > 0) {
     const int32_t* n_act = reinterpret_cast<const int32_t*>(ws + L.n_active);
     const int blocks = p->cus * persist;
     mark(p, MOE_STAGE_GATEUP, false, st);
+    if (qdq) launch_act_qdq(x_in, xq, T, d, st);
     if (T == 1)
       dec_gateup_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
     else if (T <= 2)
@@ -446,19 +464,22 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, 
       dec_gateup_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
+    if (qdq) launch_act_qdq(h, hq, S_all, f, st);
     if (T == 1)
-      dec_down_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(h, D, info, n_act, y, d, f);
+      dec_down_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(hd, D, info, n_act, y, d, f);
     else if (T <= 2)
-      dec_down_persist<FMT, 2, 2><<<blocks, 256, 0, st>>>(h, D, info, n_act, y, d, f);
+      dec_down_persist<FMT, 2, 2><<<blocks, 256, 0, st>>>(hd, D, info, n_act, y, d, f);
     else
-      dec_down_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(h, D, info, n_act, y, d, f);
+      dec_down_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(hd, D, info, n_act, y, d, f);
     mark(p, MOE_STAGE_DOWN, true, st);
   } else if (path_for(p, T) == MOE_PATH_DECODE) {
     mark(p, MOE_STAGE_GATEUP, false, st);
+    if (qdq) launch_act_qdq(x_in, xq, T, d, st);
     launch_dec<FMT, true>(p, T, L.n_slots, f, d, x, nullptr, G, U, info, tok_of, h, nullptr, st);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
-    launch_dec<FMT, false>(p, T, L.n_slots, d, f, nullptr, h, D, D, info, tok_of, nullptr, y, st);
+    if (qdq) launch_act_qdq(h, hq, S_all, f, st);
+    launch_dec<FMT, false>(p, T, L.n_slots, d, f, nullptr, hd, D, D, info, tok_of, nullptr, y, st);
     mark(p, MOE_STAGE_DOWN, true, st);
   } else {
     const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
@@ -618,7 +639,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (d.path < MOE_PATH_AUTO || d.path > MOE_PATH_GROUPED) return MOE_ERR_BAD_SHAPE;
   if (d.act_fmt != MOE_ACT_BF16 && d.act_fmt != MOE_ACT_E4M3_G128) return MOE_ERR_BAD_SHAPE;
   if (d.act_fmt == MOE_ACT_E4M3_G128) {
-    if (d.wfmt == MOE_W_E2M1_E4M3_G16 || d.path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
+    if (d.wfmt == MOE_W_E2M1_E4M3_G16) return MOE_ERR_UNSUPPORTED;
     if (d.wfmt == MOE_W_E2M1_UE8M0_G32 && (d.d_model % 64 || d.d_ff % 64)) return MOE_ERR_UNSUPPORTED;
   }
   if (d.n_experts > MAX_E || d.top_k > MAX_K) return MOE_ERR_UNSUPPORTED;
@@ -691,8 +712,9 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
                 p->t_decode, GEMV_MAX_T, p->dec_mfma_min_t, p->gemm_kernel);
   p->info = buf;
   if (d.act_fmt == MOE_ACT_E4M3_G128)
-    p->info += "; activations: e4m3 per 128-input group (UE8M0 scales), grouped path only, "
-               "block-scaled MFMA 32x32x64 (fp8 x fp8 / fp8 x fp4), 128-input stages";
+    p->info += "; activations: e4m3 per 128-input group (UE8M0 scales); grouped path: "
+               "block-scaled MFMA 32x32x64 (fp8 x fp8 / fp8 x fp4); decode path: the decode "
+               "kernels on the quantised values as bf16";
   *out = p;
   return MOE_OK;
 }
@@ -960,14 +982,17 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   const DMat D{static_cast<const uint8_t*>(down->q), static_cast<const uint8_t*>(down->scale),
                down->q_expert_stride, down->s_expert_stride};
   float* y_dst = dense ? out : nullptr;
-  if (p->d.act_fmt == MOE_ACT_E4M3_G128)
+  // activation-quantised plans: the block-scaled GEMMs on the grouped path;
+  // on the decode path the decode kernels on the quantised values as bf16
+  const bool q8 = p->d.act_fmt == MOE_ACT_E4M3_G128;
+  if (q8 && path_for(p, T) == MOE_PATH_GROUPED)
     st = p->d.wfmt == MOE_W_E4M3_B128 ? launch_q8_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, y_dst, s)
                                       : launch_q8_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, y_dst, s);
   else
-  st = p->d.wfmt == MOE_W_E4M3_B128 ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, y_dst, s)
+  st = p->d.wfmt == MOE_W_E4M3_B128 ? launch_expert_stage<FMT_E4M3>(p, T, x, G, U, D, L, ws, y_dst, s, q8)
        : p->d.wfmt == MOE_W_E2M1_UE8M0_G32
-           ? launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, y_dst, s)
-           : launch_expert_stage<FMT_NVFP4>(p, T, x, G, U, D, L, ws, y_dst, s);
+           ? launch_expert_stage<FMT_E2M1>(p, T, x, G, U, D, L, ws, y_dst, s, q8)
+           : launch_expert_stage<FMT_NVFP4>(p, T, x, G, U, D, L, ws, y_dst, s, q8);
   if (st != MOE_OK) return st;
 
   // a6: fixed-order combine

@@ -25,10 +25,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // nearest x * 2^-E (exact product; ties to the even mantissa), the sign bit
 // taken from x.  16 lanes per group, 8 inputs per lane, 16 groups per
 // workgroup.
-__global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x,
-                                                      uint8_t* __restrict__ q,
-                                                      uint8_t* __restrict__ s, int R, int K,
-                                                      int ng) {
+// DEQ: write the quantised values themselves as bf16 (code * 2^E is a bf16
+// value: at most 5 significant bits), in place allowed, for the decode
+// kernels, which take bf16 activations; the same values as the codes give.
+template <bool DEQ>
+__device__ __forceinline__ void act_quant_rows(const uint16_t* x, uint8_t* q, uint8_t* s, uint16_t* y,
+                                               int R, int K, int ng) {
   const long long gid = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
   const bool live = gid < (long long)R * ng;
@@ -68,14 +70,34 @@ __global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict
     // a / 2^(ee - 3): an integer 0..16 after rounding; codes are contiguous
     // across binade edges and from the subnormals into the normals
     const float r = __builtin_rintf(a * __uint_as_float((uint32_t)(130 - ee) << 23));
-    code[i] = ((__float_as_uint(f[i]) >> 31) << 7) | (uint32_t)(8 * (ee + 6) + (int)r);
+    if constexpr (DEQ)  // the value r 2^(ee - 3) 2^E, the sign of x
+      code[i] = f32_to_bf16_rne(copysignf(ldexpf(r, ee - 3 + E), f[i]));
+    else
+      code[i] = ((__float_as_uint(f[i]) >> 31) << 7) | (uint32_t)(8 * (ee + 6) + (int)r);
   }
   if (in) {
-    *reinterpret_cast<u32x2*>(q + (size_t)row * K + k) =
-        u32x2{code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
-              code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24};
-    if (j == 0) s[(size_t)row * ng + g] = (uint8_t)(E + 127);
+    if constexpr (DEQ) {
+      *reinterpret_cast<u32x4*>(y + (size_t)row * K + k) =
+          u32x4{code[0] | code[1] << 16, code[2] | code[3] << 16, code[4] | code[5] << 16, code[6] | code[7] << 16};
+    } else {
+      *reinterpret_cast<u32x2*>(q + (size_t)row * K + k) =
+          u32x2{code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+                code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24};
+      if (j == 0) s[(size_t)row * ng + g] = (uint8_t)(E + 127);
+    }
   }
+}
+
+__global__ __launch_bounds__(256) void act_quant_e4m3(const uint16_t* __restrict__ x,
+                                                      uint8_t* __restrict__ q,
+                                                      uint8_t* __restrict__ s, int R, int K,
+                                                      int ng) {
+  act_quant_rows<false>(x, q, s, nullptr, R, K, ng);
+}
+
+// The quantised values as bf16 rows (x and y may be the same buffer).
+__global__ __launch_bounds__(256) void act_qdq_bf16(const uint16_t* x, uint16_t* y, int R, int K, int ng) {
+  act_quant_rows<true>(x, nullptr, nullptr, y, R, K, ng);
 }
 
 // ---------------------------------------------------------------------------

@@ -39,11 +39,10 @@ def test_status_strings():
     (dict(d_model=200), 3), (dict(d_ff=96), 3), (dict(wfmt=7), 3),
     (dict(wfmt=1, d_model=48), 3), (dict(wfmt=1, d_ff=80), 3),
     (dict(wfmt=2, d_model=48), 3), (dict(wfmt=2, d_ff=80), 3), (dict(wfmt=3), 3),
-    # the activation-quantised variant: unknown act_fmt; NVFP4 weights; the
-    # decode path; e2m1 dims that are multiples of 32 but not of 64
+    # the activation-quantised variant: unknown act_fmt; NVFP4 weights; e2m1
+    # dims that are multiples of 32 but not of 64
     (dict(act_fmt=2), 2), (dict(act_fmt=-1), 2), (dict(act_fmt=1, wfmt=2), 3),
-    (dict(act_fmt=1, path=1), 3), (dict(act_fmt=1, wfmt=1, d_model=160), 3),
-    (dict(act_fmt=1, wfmt=1, d_ff=96), 3),
+    (dict(act_fmt=1, wfmt=1, d_model=160), 3), (dict(act_fmt=1, wfmt=1, d_ff=96), 3),
 ])
 def test_descriptor_validation_before_device(fields, status):
     import mixture_experts_layer_f32_amd as m

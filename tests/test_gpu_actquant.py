@@ -18,6 +18,8 @@ from gpu_util import check_out, check_routing, device_weights, log, omat, out_er
 
 pytestmark = pytest.mark.gpu
 
+DECODE, GROUPED = 1, 2
+
 WLS = {
     "e4m3": synth.Workload("aq-e4m3", 256, 384, 6, 2, "e4m3", False, (37,), False, 5101),
     "e2m1": synth.Workload("aq-e2m1", 192, 320, 8, 3, "e2m1", True, (70,), False, 5102),
@@ -59,15 +61,20 @@ def test_act_quant_bit_exact(R, K):
     assert np.array_equal(q.cpu().numpy(), rq), "codes differ"
 
 
-def run_q8(wl, W, batch, tm=None):
+def run_q8(wl, W, batch, tm=None, path=None):
+    """The activation-quantised plan; a tile height (tm) selects the grouped
+    path, else `path` (default AUTO: decode sizes run the decode kernels on
+    the quantised values as bf16)."""
     import torch
     from mixture_experts_layer_f32_amd.device import Runner, to_dev
     T = batch.x.shape[0]
+    if path is None:
+        path = GROUPED if tm is not None else 0
     old = os.environ.get("MOE_Q8_TM")
     if tm is not None:
         os.environ["MOE_Q8_TM"] = str(tm)
     try:
-        run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, act_fmt=1)
+        run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path, act_fmt=1)
     finally:
         if old is None:
             os.environ.pop("MOE_Q8_TM", None)
@@ -188,3 +195,23 @@ def test_act_quant_dense_branch(fmt):
     check_h_q8(g["h"], ref.h)
     _, out_ref = q8_reference(wl, layer, batch, ref, g["h"], np.arange(100))
     check_out(g["out"], out_ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("T,path", [(1, DECODE), (8, DECODE), (37, DECODE), (37, GROUPED)])
+def test_act_quant_decode_route(fmt, T, path):
+    """The decode path of the activation-quantised plan: x and h replaced by
+    their quantised values as bf16 (exact: code * 2^E has at most 5
+    significant bits), then the decode kernels (matvec at one token, MFMA
+    tiles above); the grouped path at the same size for comparison.  Both
+    against the oracle's quantised layer."""
+    wl, layer, W = get(fmt)
+    batch = synth.make_batch(wl, layer, T)
+    ref = oracle_q8(wl, layer, batch)
+    g = run_q8(wl, W, batch, path=path)
+    check_routing(g, ref)
+    eq = check_h_q8(g["h"], ref.h)
+    _, out_ref = q8_reference(wl, layer, batch, ref, g["h"], np.arange(T))
+    mx, rms, mrel = check_out(g["out"], out_ref)
+    log(f"act-quant {fmt} T={T} path={path}: h equal {eq:.4f}, max|err| {mx:.3e} mean rel {mrel:.3e}")
+
