@@ -180,3 +180,34 @@ def forward(x_bits, w_router, bias, mats, k, renorm, fmt, act_quant=False):
             acc = acc + wts[t, j] * Y[int(e), t]
         out[t] = acc
     return ids, wts, out
+
+
+def bf16_bits_of(v):
+    """float64 values already on the bf16 grid -> their bit patterns (torch's cast,
+    exact on such values)."""
+    t = torch.tensor(np.asarray(v, np.float64)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def block_forward(x_bits, gamma_bits, eps, w_router, bias, mats, k, renorm, fmt, dense_mats,
+                  residual_bits):
+    """Dense evaluation of the transformer-block steps around the layer: RMS
+    normalisation of the hidden rows (float64, one nearest-value bf16 rounding),
+    the routed layer by forward() on the normed rows, the shared expert as a
+    one-expert layer by forward() on the same rows, and the add into the
+    residual stream with the two layer outputs taken as f32 values.
+    Returns (xn bits, routed f64, dense f64, block out bits)."""
+    xf = bf16_bits_to_f64(x_bits)
+    g = bf16_bits_to_f64(gamma_bits)
+    T, d = xf.shape
+    xn_val = np.zeros((T, d))
+    for t in range(T):
+        ms = math.fsum(float(v) * float(v) for v in xf[t]) / d
+        xn_val[t] = bf16_round(xf[t] / math.sqrt(ms + eps) * g)
+    xn = bf16_bits_of(xn_val)
+    _, _, routed = forward(xn, w_router, bias, mats, k, renorm, fmt)
+    _, _, dense = forward(xn, np.zeros((1, d), np.float32), None, dense_mats, 1, True, fmt)
+    acc = (routed.astype(np.float32).astype(np.float64)
+           + dense.astype(np.float32).astype(np.float64))
+    out = bf16_bits_of(bf16_round(bf16_bits_to_f64(residual_bits) + acc))
+    return xn, routed, dense, out

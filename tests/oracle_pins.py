@@ -395,6 +395,69 @@ def pin_act_quant_forward(om, name):
     assert not np.array_equal(r.out, run(om, wl, layer, batch).out)
 
 
+def _block_case(om, fmt="e4m3"):
+    """A routed layer plus a shared expert of the same format (one expert with a
+    leading axis of 1), hidden rows of mixed magnitudes and a gain."""
+    name = {"e4m3": "e4m3-nonsquare", "e2m1": "e2m1-small"}[fmt]
+    wl, layer, batch = case(name)
+    dwl = synth.Workload(wl.name + "-shared", wl.d, wl.f, 1, 1, wl.fmt, True, (), False, wl.seed + 50)
+    dl = synth.make_layer(dwl)
+    rng = np.random.default_rng(wl.seed + 7)
+    T = batch.x.shape[0]
+    hid = _bf16(rng.standard_normal((T, wl.d)) * np.ldexp(1.0, rng.integers(-3, 4, (T, 1))))
+    gamma = _bf16(rng.uniform(0.5, 1.5, wl.d))
+    return wl, layer, dl, hid, gamma
+
+
+def _block(om, wl, layer, dl, hid, gamma, eps, residual=None):
+    g, u, d = mats(om, layer)
+    dense = mats(om, dl)
+    return om.block_forward(hid, gamma, eps, layer.w_router, None, g, u, d, wl.k, wl.renorm, wl.fmt,
+                            dense=dense, residual=residual)
+
+
+def pin_block_forward(om, fmt="e4m3"):
+    """The block steps composed (B1 -> layer -> B2 -> B3) against an independent
+    dense brute force of the block; invariance of both branches to a
+    power-of-two rescale of the hidden rows (eps = 0: they read the normed
+    rows only); the residual defaults to the hidden rows themselves (with all
+    down codes zero both branches are exactly 0 and the block returns its
+    residual unchanged); the shortcut layout's later residual is honoured."""
+    wl, layer, dl, hid, gamma = _block_case(om, fmt)
+    eps = 1e-6
+    xn, routed, dense, out = _block(om, wl, layer, dl, hid, gamma, eps)
+    bxn, brouted, bdense, bout = bf.block_forward(
+        hid, gamma, eps, layer.w_router, None,
+        (layer.gate.q, layer.gate.s, layer.up.q, layer.up.s, layer.down.q, layer.down.s), wl.k,
+        wl.renorm, wl.fmt, (dl.gate.q, dl.gate.s, dl.up.q, dl.up.s, dl.down.q, dl.down.s), hid)
+    assert np.array_equal(xn, bxn), "normed rows differ from the brute force"
+    assert_out_close(routed, brouted)
+    assert dense is not None
+    assert_out_close(dense, bdense)
+    # the add rounds once to bf16; the brute force's f32 terms may differ from
+    # the oracle's by an f32 ulp, which can move a rounding at a bf16 boundary
+    a, b = om.bf16_to_f64(out), om.bf16_to_f64(bout)
+    assert np.all(np.abs(a - b) <= 2.0 ** -8 * np.abs(b) + 1e-30), "block out off by > 1 bf16 ulp"
+    assert float(np.mean(out == bout)) >= 0.99
+    # rescaling the hidden rows by 2^3 with eps = 0 leaves xn, and so both branches, unchanged
+    xn0, r0, d0, _ = _block(om, wl, layer, dl, hid, gamma, 0.0)
+    hid8 = _bf16(om.bf16_to_f64(hid) * 8.0)
+    xn8, r8, d8, out8 = _block(om, wl, layer, dl, hid8, gamma, 0.0)
+    assert np.array_equal(xn0, xn8) and np.array_equal(r0, r8) and np.array_equal(d0, d8)
+    # the residual is the hidden rows unless given: out8 = bf16(8 hid + branches)
+    assert not np.array_equal(out8, _block(om, wl, layer, dl, hid, gamma, 0.0)[3])
+    # zero down codes: both branches vanish and the block returns its residual exactly
+    zl = synth.Layer(layer.wl, layer.w_router, layer.gate, layer.up,
+                     synth.QMat(np.zeros_like(layer.down.q), layer.down.s, layer.down.N, layer.down.K))
+    zd = synth.Layer(dl.wl, dl.w_router, dl.gate, dl.up,
+                     synth.QMat(np.zeros_like(dl.down.q), dl.down.s, dl.down.N, dl.down.K))
+    xz, rz, dz, oz = _block(om, wl, zl, zd, hid, gamma, eps)
+    assert np.all(rz == 0) and np.all(dz == 0)
+    assert np.array_equal(oz, hid), "the default residual is not the hidden rows"
+    later = _bf16(om.bf16_to_f64(hid) * 0.5 + 1.0)
+    assert np.array_equal(_block(om, wl, zl, zd, hid, gamma, eps, residual=later)[3], later)
+
+
 FAST_PINS = [
     lambda om: pin_bruteforce(om, "tiny"),
     lambda om: pin_bruteforce(om, "e4m3-nonsquare", biased=True),
@@ -403,6 +466,7 @@ FAST_PINS = [
     pin_onehot, pin_routing_closed_form, pin_router_exact, pin_topk_ties, pin_permute, pin_silu,
     pin_scale_doubling, pin_identical_experts, pin_relabel, pin_zero_input, pin_single_expert,
     pin_lossless_grid, pin_token_subset, pin_rmsnorm, pin_residual_add, pin_act_quant,
+    pin_block_forward, lambda om: pin_block_forward(om, "e2m1"),
     lambda om: pin_act_quant_forward(om, "e4m3-nonsquare"),
     lambda om: pin_act_quant_forward(om, "e2m1-small"),
 ]

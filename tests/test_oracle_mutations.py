@@ -11,7 +11,7 @@ import oracle_pins as P
 _orig = {name: getattr(om, name) for name in (
     "unpack_e2m1", "dequant", "routing_weights", "router_logits", "select_topk", "silu",
     "expert_ffn", "combine", "permute", "bf16_rne", "rmsnorm", "residual_add", "ue8m0_for",
-    "act_quant_e4m3", "e4m3_rne")}
+    "act_quant_e4m3", "e4m3_rne", "block_forward")}
 
 
 def m_nibble_swap(q, K):
@@ -175,6 +175,30 @@ def m_actq_h_unquantised(xf, Wg, Wu, Wd, act_q=False):
     return _orig["expert_ffn"](xf, Wg, Wu, Wd)
 
 
+def _block_variant(dense_input, default_residual):
+    """block_forward with the dense branch fed `dense_input` ("xn" or "hidden")
+    and the residual defaulting to `default_residual` ("hidden" or "xn")."""
+    def f(x_hidden, gamma, eps, w_router, bias, gate, up, down, k, renorm, fmt, dense=None,
+          residual=None):
+        xn = om.rmsnorm(x_hidden, gamma, eps)
+        routed = om.moe_forward(xn, w_router, bias, gate, up, down, k, renorm, fmt).out
+        dense_out = None
+        if dense is not None:
+            dg, du, dd = dense
+            xf = om.bf16_to_f64(xn if dense_input == "xn" else x_hidden)
+            Wg = om.dequant(dg.q[0], dg.s[0], fmt, dg.K)
+            Wu = om.dequant(du.q[0], du.s[0], fmt, du.K)
+            Wd = om.dequant(dd.q[0], dd.s[0], fmt, dd.K)
+            dense_out = om.expert_ffn(xf, Wg, Wu, Wd)[1].astype(np.float32)
+        res = (x_hidden if default_residual == "hidden" else xn) if residual is None else residual
+        return xn, routed, dense_out, om.residual_add(res, routed, dense_out)
+    return f
+
+
+m_block_dense_unnormed = _block_variant("hidden", "hidden")
+m_block_residual_normed = _block_variant("xn", "xn")
+
+
 MUTATIONS = {
     "act_quant_scale_one_binade_low": ("ue8m0_for", m_actq_scale_low),
     "act_quant_group_64": ("act_quant_e4m3", m_actq_group64),
@@ -184,6 +208,8 @@ MUTATIONS = {
     "rmsnorm_sum_not_mean": ("rmsnorm", m_rmsnorm_sum_not_mean),
     "rmsnorm_eps_outside_sqrt": ("rmsnorm", m_rmsnorm_eps_outside),
     "residual_add_drops_dense": ("residual_add", m_residual_drops_dense),
+    "block_dense_branch_unnormed": ("block_forward", m_block_dense_unnormed),
+    "block_residual_defaults_to_normed": ("block_forward", m_block_residual_normed),
     "nibble_swap": ("unpack_e2m1", m_nibble_swap),
     "scale_block_transposed": ("dequant", m_scale_transposed),
     "scale_divided": ("dequant", m_scale_divided),

@@ -16,7 +16,8 @@ def test_bruteforce_small(name, biased):
                                  P.pin_topk_ties, P.pin_permute, P.pin_silu, P.pin_scale_doubling,
                                  P.pin_identical_experts, P.pin_relabel, P.pin_zero_input,
                                  P.pin_single_expert, P.pin_lossless_grid, P.pin_token_subset,
-                                 P.pin_rmsnorm, P.pin_residual_add, P.pin_act_quant])
+                                 P.pin_rmsnorm, P.pin_residual_add, P.pin_act_quant,
+                                 P.pin_block_forward])
 def test_pin(pin):
     pin(om)
 
