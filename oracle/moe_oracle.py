@@ -156,18 +156,22 @@ def unpack_e2m1(q: np.ndarray, K: int) -> np.ndarray:
 
 
 def dequant(q: np.ndarray, s: np.ndarray, fmt: str, K: int) -> np.ndarray:
-    """One expert matrix [N, K] in float64 (O7)."""
+    """One expert matrix [N, K] in float64 (O7): each element is its code's
+    value times its block's or group's scale, one exact float64 product (the
+    scale is broadcast over its block in place)."""
+    N = q.shape[0]
     if fmt == "e4m3":
-        scale = np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1)
-        return E4M3[q] * scale
+        W = E4M3[q]
+        W.reshape(N // 128, 128, K // 128, 128)[...] *= s.astype(np.float64)[:, None, :, None]
+        return W
     if fmt == "e2m1":
-        codes = unpack_e2m1(q, K)
-        scale = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=1)
-        return E2M1[codes] * scale
+        W = E2M1[unpack_e2m1(q, K)]
+        W.reshape(N, K // 32, 32)[...] *= np.ldexp(1.0, s.astype(np.int64) - 127)[:, :, None]
+        return W
     if fmt == "nvfp4":
-        codes = unpack_e2m1(q, K)
-        scale = np.repeat(E4M3[s], 16, axis=1)
-        return E2M1[codes] * scale
+        W = E2M1[unpack_e2m1(q, K)]
+        W.reshape(N, K // 16, 16)[...] *= E4M3[s][:, :, None]
+        return W
     raise ValueError(fmt)
 
 
@@ -337,12 +341,15 @@ class Result:
 
 
 def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm: bool,
-                fmt: str, tokens: Optional[Sequence[int]] = None, act_quant: bool = False) -> Result:
+                fmt: str, tokens: Optional[Sequence[int]] = None, act_quant: bool = False,
+                workers: int = 1) -> Result:
     """The whole layer (O1-O10).  With `tokens`, routing is computed for every
     token (the permutation needs all of them) but the expert FFN and the
     combine only for the listed tokens; `out` then has one row per listed
     token and h/y are not returned.  With `act_quant`, the activation-quantised
-    variant (Q1-Q2)."""
+    variant (Q1-Q2).  `workers` > 1 runs the per-expert step (O7-O9) of
+    different experts on that many threads; each expert's rows are computed by
+    the same code either way, so the result does not depend on it."""
     T, d = x.shape
     E = w_router.shape[0]
     f = gate.q.shape[1]
@@ -355,12 +362,13 @@ def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm
     want = np.ones(S, bool) if tokens is None else np.isin(np.arange(S) // k, list(tokens))
     h = np.zeros((S, f), np.uint16)
     y = np.zeros((S, d), np.float64)
-    for e in range(E):
+
+    def one_expert(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         pos = np.arange(lo, hi)
         pos = pos[want[perm[lo:hi]]]
         if pos.size == 0:
-            continue
+            return
         rows = perm[pos] // k
         Wg = dequant(gate.q[e], gate.s[e], fmt, gate.K)
         Wu = dequant(up.q[e], up.s[e], fmt, up.K)
@@ -369,6 +377,14 @@ def moe_forward(x, w_router, bias, gate: Mat, up: Mat, down: Mat, k: int, renorm
             h[pos], y[pos] = expert_ffn(xf[rows], Wg, Wu, Wd, act_q=True)
         else:
             h[pos], y[pos] = expert_ffn(xf[rows], Wg, Wu, Wd)
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, range(E)))
+    else:
+        for e in range(E):
+            one_expert(e)
     if tokens is None:
         out = combine(y, w, inv_perm)
         return Result(logits, ids, w, counts, offsets, perm, inv_perm, h, y, out)
