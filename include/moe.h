@@ -24,8 +24,9 @@
  *
  * Memory: every pointer passed to moe_forward is HIP device memory owned by
  * the caller.  The library allocates no device memory: all scratch lives in
- * the caller's workspace.  A plan holds host metadata only and is immutable,
- * so forwards on different streams with different workspaces may overlap.
+ * the caller's workspace.  A plan holds host metadata only; once its options
+ * are set (moe_plan_set) it is only read by moe_forward, so forwards on
+ * different streams with different workspaces may overlap.
  *
  * Errors: every check runs on the host before the first launch, so a call
  * that returns an error has written nothing.  moe_forward is asynchronous on
@@ -134,6 +135,34 @@ typedef struct {
  * On success *out holds a plan (host memory only).  Shape errors are
  * reported before the device is queried. */
 moe_status moe_plan(const moe_desc* desc, moe_plan_t* out);
+
+/* Kernel choices a plan makes from its shape, and the values that override
+ * them.  A fresh plan needs none of this; the overrides exist so that every
+ * variant a plan can run is reachable by the parity tests (and by tuning
+ * sweeps).  Each variant computes the same layer. */
+typedef enum {
+  /* decode expert stage: 1 = 16-row MFMA tiles (from MOE_OPT_DEC_MFMA_MIN_T
+   * tokens, the default), 0 = the wavefront matvec at every T */
+  MOE_OPT_DEC_KERNEL = 0,
+  /* fewest tokens for the MFMA decode tiles (default 2: one token takes the
+   * matvec); >= 1 */
+  MOE_OPT_DEC_MFMA_MIN_T = 1,
+  /* grouped-GEMM tile height in tokens: 128, 192 or 256; 0 = by the mean
+   * slots per expert (the default) */
+  MOE_OPT_GROUPED_TILE = 2,
+  /* grouped-GEMM tile height of activation-quantised plans: 64, 128 or 192;
+   * 0 = by the mean slots per expert (the default) */
+  MOE_OPT_Q8_TILE = 3,
+  /* top-k and permute in one workgroup up to this many tokens (1..64);
+   * 0 = by the expert count (64 with at most 64 experts, else 16) */
+  MOE_OPT_SMALL_ROUTE_T = 4
+} moe_option;
+
+/* Sets one option of a plan.  MOE_ERR_UNSUPPORTED for an unknown option,
+ * MOE_ERR_BAD_SHAPE for a value outside the listed ones.  Call it before the
+ * plan's forwards (it changes the plan, so it must not race with them) and
+ * query moe_workspace_size afterwards: the workspace layout may change. */
+moe_status moe_plan_set(moe_plan_t plan, int32_t option, int32_t value);
 
 /* Bytes of device workspace a forward over n_tokens tokens needs (0 if
  * n_tokens <= 0 or the plan is NULL).  256-byte alignment is required. */

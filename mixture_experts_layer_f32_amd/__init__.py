@@ -20,6 +20,8 @@ MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
 MOE_W_E4M3_B128, MOE_W_E2M1_UE8M0_G32, MOE_W_E2M1_E4M3_G16 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_GROUPED = 0, 1, 2
 MOE_ACT_BF16, MOE_ACT_E4M3_G128 = 0, 1
+MOE_OPT_DEC_KERNEL, MOE_OPT_DEC_MFMA_MIN_T, MOE_OPT_GROUPED_TILE = 0, 1, 2
+MOE_OPT_Q8_TILE, MOE_OPT_SMALL_ROUTE_T = 3, 4
 STAGES = ("router", "topk", "permute", "gateup", "down", "combine")
 WFMT = {"e4m3": MOE_W_E4M3_B128, "e2m1": MOE_W_E2M1_UE8M0_G32, "nvfp4": MOE_W_E2M1_E4M3_G16}
 
@@ -59,6 +61,8 @@ def _load():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.moe_plan.argtypes = [ctypes.POINTER(moe_desc), ctypes.POINTER(vp)]
     L.moe_plan.restype = ctypes.c_int
+    L.moe_plan_set.argtypes = [vp, i32, i32]
+    L.moe_plan_set.restype = ctypes.c_int
     L.moe_workspace_size.argtypes = [vp, i32]
     L.moe_workspace_size.restype = sz
     L.moe_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(moe_mat),
@@ -131,6 +135,13 @@ def moe_plan_status(desc: moe_desc) -> int:
     if h.value:
         lib.moe_plan_free(h.value)
     return st
+
+
+def moe_plan_set(plan: Plan, option: int, value: int) -> None:
+    """Override one of the plan's shape-based kernel choices (MOE_OPT_*)."""
+    st = lib.moe_plan_set(plan.handle, int(option), int(value))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_plan_set")
 
 
 def moe_workspace_size(plan: Plan, n_tokens: int) -> int:

@@ -42,20 +42,12 @@ struct moe_plan_s {
   int cus = 0;
   std::string arch;
   int t_decode = 0;  // AUTO: decode variant for T <= t_decode
-  int dec_nrg = 0;     // decode row groups per wavefront (0: chosen from the shape)
-  int dec_stream = 0;  // 1: register-resident activations + row-group prefetch variant
-  int dec_persist = -1; // >0: persistent decode grid of CUs * dec_persist blocks; <0: by shape
-  int dec_wpb = 4;     // wavefronts per decode workgroup
-  int dec_kernel = 1;  // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
+  // kernel choices a fresh plan makes from the shape; moe_plan_set overrides them
+  int dec_kernel = 1;     // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
-  int dec_tall = -1;      // MFMA decode tiles of 32/64 rows: -1 by shape, 0 never, 1 always
-  int router_split = 0;   // most router K-slices (1..8), 0 = by shape
   int small_route_t = 0;  // top-k + permute in one workgroup up to this many tokens (<= 64), 0 = by shape
-  int dec_ks = 0;         // MFMA decode wavefronts per workgroup (k-split), 0 = by shape
-  int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (11, 12, 22, 23, 24), 0 = by shape
+  int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (22, 23, 24), 0 = by shape
   int q8_tm = 0;          // gemm_q8 token chunks per wavefront (tile 64 * tm tokens), 0 = by shape
-  int gemm_kernel = 3;    // grouped expert stage: 3 = gemm_big (default), 1 = register-weight tiles,
-                          // 2 = gemm_dma, 0 = LDS weight tiles
   std::string info;
   std::string last_error;
   // instrumentation (moe_timing_*)
@@ -82,21 +74,13 @@ int router_split(const moe_plan_s* p, int T, int* slice) {
   const int target = T <= GEMV_MAX_T ? 2 * p->cus : 4 * p->cus;
   // few tokens: at most 4 slices, so the top-k sums its slice partials in
   // one round of loads (measured 0.3-1.5 % per step against 6-8 slices)
-  const int cap = p->router_split > 0 ? std::min(p->router_split, MAX_SPLIT)
-                                      : (T <= GEMV_MAX_T ? 4 : MAX_SPLIT);
+  const int cap = T <= GEMV_MAX_T ? 4 : MAX_SPLIT;
   int n = std::max(1, std::min(std::min(d / 256, cap), (target + blocks - 1) / blocks));
   int w = (d + n - 1) / n;
   w = (w + 31) / 32 * 32;
   n = (d + w - 1) / w;
   if (slice) *slice = w;
   return n;
-}
-
-// Rows per grouped-GEMM tile from the mean slots per expert.
-int gemm_bm(const moe_plan_s* p, int T) {
-  const long long S = (long long)T * p->d.top_k;
-  const long long per = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
-  return per >= 96 ? 128 : (per >= 40 ? 64 : 32);
 }
 
 // The MFMA decode addresses activations with 32-bit buffer offsets.
@@ -119,8 +103,7 @@ bool use_dec_mfma(const moe_plan_s* p, int T) {
 // Wavefronts splitting a decode tile's nkb k-units: all of them up to 4,
 // else 4, 3 or 2, whichever divides nkb (a wavefront with fewer units than
 // its neighbours waits for them at every tile's reduction), else 4.
-int dec_ks(const moe_plan_s* p, int nkb) {
-  if (p->dec_ks > 0) return std::min(p->dec_ks, nkb);
+int dec_ks(int nkb) {
   if (nkb <= 4) return nkb;
   for (int ks = 4; ks >= 2; --ks)
     if (nkb % ks == 0) return ks;
@@ -128,9 +111,9 @@ int dec_ks(const moe_plan_s* p, int nkb) {
 }
 
 // Shape of gemm_big's tiles, as 10 * WGM + TM (tile height 32 * WGM * TM),
-// from the mean slots per expert: measured on every grouped workload over all
-// five shapes, 128-token tiles won up to 16 slots per expert (the fp4 layer at
-// 16 and 1024 tokens; even with one slot, ahead of the wide short tiles),
+// from the mean slots per expert: measured on every grouped workload,
+// 128-token tiles won up to 16 slots per expert (the fp4 layer at 16 and 1024
+// tokens; even with one slot, ahead of 32- and 64-token tiles of 256 rows),
 // 192-token tiles at 64 to 128 (the skewed OLMoE shape at 512 tokens, whose
 // hot experts hold about 150, and the d = 7168 layer at 4096) and 256-token
 // tiles at 256 (the skewed OLMoE shape at 2048).
@@ -160,9 +143,8 @@ int q8_tm(const moe_plan_s* p, int T) {
 int tile_rows(const moe_plan_s* p, int T) {
   if (p->d.act_fmt == MOE_ACT_E4M3_G128 && path_for(p, T) == MOE_PATH_GROUPED) return 64 * q8_tm(p, T);
   if (use_dec_mfma(p, T)) return 16;
-  if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel == 3) return big_rows(big_cfg(p, T));
-  if (path_for(p, T) == MOE_PATH_GROUPED && p->gemm_kernel >= 1) return 64;
-  return gemm_bm(p, T);
+  if (path_for(p, T) == MOE_PATH_GROUPED) return big_rows(big_cfg(p, T));
+  return 16;  // the matvec reads slot_info, not the tile list
 }
 
 Layout layout(const moe_plan_s* p, int T) {
@@ -222,114 +204,30 @@ moe_status hip_fail(moe_plan_s* p, hipError_t err, const char* what) {
   return MOE_ERR_HIP;
 }
 
-// Decode matvec configuration for rows of K inputs: CPL chunks of 16 inputs
-// per lane (0: rows longer than 8 passes take the looping kernel), slots per
-// pass TG (activations of TG slots x CPL chunks stay in registers), rows per
-// load group RPW.
-constexpr int dec_rpw(int cpl) { return (cpl == 0 || cpl <= 4) ? 2 : 1; }
-constexpr int dec_tgmax(int cpl) { return cpl == 0 ? 4 : (cpl == 1 ? 8 : (cpl == 2 ? 4 : (cpl <= 4 ? 2 : 1))); }
-inline int dec_cpl(int K) {
-  const int c = (K / 16 + WAVE - 1) / WAVE;
-  return c <= 8 ? c : 0;
-}
-
-template <int FMT, bool GATEUP, int TG, int CPL>
-void launch_dec_cfg(int grid_x, int N, int K, int rpw_total, int wpb, int T, const uint16_t* x,
-                    const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
-                    uint16_t* hout, float* y, hipStream_t st) {
-  const int rows_per_block = wpb * rpw_total;
-  const dim3 g(grid_x, (N + rows_per_block - 1) / rows_per_block);
-  if (GATEUP)
-    dec_gateup<FMT, TG, CPL, dec_rpw(CPL)><<<g, WAVE * wpb, 0, st>>>(x, A, B, info, tok_of, hout, K,
-                                                                    N, T, rpw_total);
-  else
-    dec_down<FMT, TG, CPL, dec_rpw(CPL)><<<g, WAVE * wpb, 0, st>>>(hin, A, info, y, N, K,
-                                                                  rpw_total);
-}
-
-template <int FMT, bool GATEUP, int CPL>
-void launch_dec_cpl(int T, int grid_x, int N, int K, int rpw_total, int wpb, const uint16_t* x,
-                    const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
-                    uint16_t* hout, float* y, hipStream_t st) {
-  if (T == 1)
-    launch_dec_cfg<FMT, GATEUP, 1, CPL>(grid_x, N, K, rpw_total, wpb, T, x, hin, A, B, info,
-                                        tok_of, hout, y, st);
-  else
-    launch_dec_cfg<FMT, GATEUP, dec_tgmax(CPL), CPL>(grid_x, N, K, rpw_total, wpb, T, x, hin, A, B,
-                                                     info, tok_of, hout, y, st);
-}
-
-// Gate/up (N = f rows of K = d inputs) or down (N = d rows of K = f inputs).
+// Decode matvec (the wavefront matvec of dec_gateup / dec_down): one
+// workgroup of 4 wavefronts per (selected expert, 8 rows), each wavefront 2
+// rows; up to 4 slots of the expert per pass (1 for a single token).
 template <int FMT, bool GATEUP>
-void launch_dec(moe_plan_s* p, int T, int n_slots, int N, int K, const uint16_t* x,
-                const uint16_t* hin, DMat A, DMat B, const int4* info, const int32_t* tok_of,
-                uint16_t* hout, float* y, hipStream_t st) {
-  const int cpl = p->dec_stream ? dec_cpl(K) : 0;
-  const int rpw = dec_rpw(cpl);
-  // rows per wavefront: enough blocks to cover the chip a few times over
-  int nrg = p->dec_nrg;
-  if (nrg <= 0 && cpl == 0) nrg = 1;
-  if (nrg <= 0) {
-    const long long rows = (long long)n_slots * N;
-    nrg = (int)std::max(1LL, std::min(8LL, rows / (4LL * rpw * 4 * p->cus)));
+void launch_dec(int T, int n_slots, int N, int K, const uint16_t* x, const uint16_t* hin, DMat A,
+                DMat B, const int4* info, const int32_t* tok_of, uint16_t* hout, float* y,
+                hipStream_t st) {
+  constexpr int RPW = 2, WPB = 4;
+  const dim3 g(n_slots, (N + WPB * RPW - 1) / (WPB * RPW));
+  if (T == 1) {
+    if (GATEUP)
+      dec_gateup<FMT, 1, RPW><<<g, WAVE * WPB, 0, st>>>(x, A, B, info, tok_of, hout, K, N, T, RPW);
+    else
+      dec_down<FMT, 1, RPW><<<g, WAVE * WPB, 0, st>>>(hin, A, info, y, N, K, RPW);
+  } else {
+    if (GATEUP)
+      dec_gateup<FMT, 4, RPW><<<g, WAVE * WPB, 0, st>>>(x, A, B, info, tok_of, hout, K, N, T, RPW);
+    else
+      dec_down<FMT, 4, RPW><<<g, WAVE * WPB, 0, st>>>(hin, A, info, y, N, K, RPW);
   }
-  const int rpw_total = rpw * nrg;
-#define MOE_DEC_CASE(C)                                                                        \
-  case C:                                                                                      \
-    launch_dec_cpl<FMT, GATEUP, C>(T, n_slots, N, K, rpw_total, p->dec_wpb, x, hin, A, B, info, \
-                                   tok_of, hout, y, st);                                       \
-    break;
-  switch (cpl) {
-    MOE_DEC_CASE(0)
-    MOE_DEC_CASE(1)
-    MOE_DEC_CASE(2)
-    MOE_DEC_CASE(3)
-    MOE_DEC_CASE(4)
-    MOE_DEC_CASE(5)
-    MOE_DEC_CASE(6)
-    MOE_DEC_CASE(7)
-    MOE_DEC_CASE(8)
-  }
-#undef MOE_DEC_CASE
 }
 
-// Grouped GEMM launch: grid (column blocks of N, tile-list entries), LDS
-// sized per configuration (above the 64 KB static limit, set once).
-// Super-block order of the grouped kernels: about the workgroups one XCD
-// holds at once (2 per CU).
-struct GemmOrder {
-  int nb, gc, gt, ntb;
-  long long grid;
-};
-GemmOrder gemm_order(const moe_plan_s* p, int max_tiles, int N, int bnm, int per_cu = 2) {
-  GemmOrder o;
-  o.nb = (N + bnm - 1) / bnm;
-  o.gc = std::max(1, std::min(4, (o.nb + 7) / 8));
-  o.gt = std::max(1, (p->cus / 8) * per_cu / o.gc);
-  o.ntb = (max_tiles + o.gt - 1) / o.gt;
-  const int ncb = (o.nb + 8 * o.gc - 1) / (8 * o.gc);
-  o.grid = 8LL * o.gc * o.gt * o.ntb * ncb;
-  return o;
-}
-
-template <int FMT, bool GATEUP, int TNW>
-void launch_dma(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
-                DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
-                void* out, hipStream_t st) {
-  const GemmOrder o = gemm_order(p, max_tiles, N, DmaCfg<FMT, GATEUP, TNW>::BNM);
-  gemm_dma<FMT, GATEUP, TNW><<<dim3((unsigned)o.grid), 256, 0, st>>>(
-      act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
-}
-
-template <int FMT, bool GATEUP, int TNW, int PD, int BM = 64>
-void launch_rw(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
-               DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of,
-               void* out, hipStream_t st) {
-  const GemmOrder o = gemm_order(p, max_tiles, N, RWCfg<FMT, GATEUP, TNW, BM>::BNM, BM == 64 ? 2 : 1);
-  gemm_rw<FMT, GATEUP, TNW, PD, BM><<<dim3((unsigned)o.grid), 256, 0, st>>>(
-      act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, o.nb, o.gc, o.gt, o.ntb);
-}
-
+// Grouped GEMM launch: a 1-D grid of (tile-list entry, column block) pairs
+// in the XCD order gemm_big decodes.
 template <int FMT, bool GATEUP, int TNW, int TM, int WGM>
 void launch_big_cfg(int max_tiles, int N, int K, int T, const uint16_t* act, DMat W0, DMat W1,
                     const int4* tiles, const int32_t* n_tiles, const int32_t* tok_of, void* out,
@@ -347,30 +245,11 @@ void launch_big(const moe_plan_s* p, int max_tiles, int N, int K, int T, const u
 #define MOE_BIG(TM, WGM) \
   launch_big_cfg<FMT, GATEUP, TNW, TM, WGM>(max_tiles, N, K, T, act, W0, W1, tiles, n_tiles, tok_of, out, st)
   switch (big_cfg(p, T)) {
-    case 11: MOE_BIG(1, 1); break;
-    case 12: MOE_BIG(2, 1); break;
     case 22: MOE_BIG(2, 2); break;
     case 23: MOE_BIG(3, 2); break;
     default: MOE_BIG(4, 2); break;
   }
 #undef MOE_BIG
-}
-
-template <int FMT, bool GATEUP, int BM, int WM, int TN, int BK, int PF>
-void launch_gemm(const moe_plan_s* p, int max_tiles, int N, int K, int T, const uint16_t* act,
-                 DMat W0, DMat W1, const int4* tiles, const int32_t* n_tiles,
-                 const int32_t* tok_of, void* out, hipStream_t st) {
-  using C = G2<FMT, GATEUP ? 2 : 1, BM, WM, TN, BK>;
-  auto kern = &gemm_expert<FMT, GATEUP, BM, WM, TN, BK, PF>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
-    attr_set = true;
-  }
-  const GemmOrder o = gemm_order(p, max_tiles, N, C::BNM);
-  kern<<<dim3((unsigned)o.grid), 256, C::SMEM, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K,
-                                                     T, o.nb, o.gc, o.gt, o.ntb);
 }
 
 // y_dst: where the down projection writes y (NULL: the workspace).
@@ -396,15 +275,6 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat 
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   const uint16_t* hd = qdq ? hq : h;  // what the down projection reads
   float* y = y_dst ? y_dst : reinterpret_cast<float*>(ws + L.y);
-  // Persistent decode grid (CUs x persist workgroups walking (expert, row pair)
-  // items) when each wavefront gets a few items: measured faster there, and
-  // slower with one item or with tens of items per wavefront.
-  int persist = p->dec_persist;
-  if (persist < 0) {
-    const long long items = (long long)std::min(T * p->d.top_k, p->d.n_experts) * (f / 2);
-    const long long per_wave = items / (6LL * 4 * p->cus);
-    persist = (per_wave >= 2 && per_wave <= 8) ? 6 : 0;
-  }
   if (use_dec_mfma(p, T)) {
     const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
@@ -420,7 +290,7 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat 
     auto run = [&](bool gateup) {
       const int K = gateup ? d : f;
       const int ku = FMT == FMT_E4M3 ? 128 : 256;
-      const int ks = dec_ks(p, (K + ku - 1) / ku);
+      const int ks = dec_ks((K + ku - 1) / ku);
       const dim3 blk(WAVE * ks);
       // about 12 (tall: 8) wavefronts per CU whatever the split
       const int g3 = p->cus * 12 / ks, g2 = p->cus * 8 / ks;
@@ -428,9 +298,8 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat 
       // outweighs the weights once the tiles' token columns fill; taller tiles
       // then share it over more rows (measured: faster at 8 slots per expert,
       // slower at 4)
-      bool tall = big(gateup ? f : d, gateup ? 32 : 64) &&
-                  (FMT == FMT_E4M3 || S >= 8LL * p->d.n_experts);
-      if (p->dec_tall >= 0) tall = p->dec_tall == 1;
+      const bool tall = big(gateup ? f : d, gateup ? 32 : 64) &&
+                        (FMT == FMT_E4M3 || S >= 8LL * p->d.n_experts);
       if (gateup) {
         if (tall)
           dec_mfma<FMT, true, 2, FMT == FMT_E4M3 ? 3 : 2><<<g2, blk, 0, st>>>(x, x_bytes, G, U, tiles, n_tiles, tok_of, h, f, d, T);
@@ -451,88 +320,23 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat 
     if (qdq) launch_act_qdq(h, hq, S_all, f, st);
     run(false);
     mark(p, MOE_STAGE_DOWN, true, st);
-  } else if (path_for(p, T) == MOE_PATH_DECODE && persist > 0) {
-    const int32_t* n_act = reinterpret_cast<const int32_t*>(ws + L.n_active);
-    const int blocks = p->cus * persist;
-    mark(p, MOE_STAGE_GATEUP, false, st);
-    if (qdq) launch_act_qdq(x_in, xq, T, d, st);
-    if (T == 1)
-      dec_gateup_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
-    else if (T <= 2)
-      dec_gateup_persist<FMT, 2, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
-    else
-      dec_gateup_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(x, G, U, info, n_act, tok_of, h, d, f, T);
-    mark(p, MOE_STAGE_GATEUP, true, st);
-    mark(p, MOE_STAGE_DOWN, false, st);
-    if (qdq) launch_act_qdq(h, hq, S_all, f, st);
-    if (T == 1)
-      dec_down_persist<FMT, 1, 2><<<blocks, 256, 0, st>>>(hd, D, info, n_act, y, d, f);
-    else if (T <= 2)
-      dec_down_persist<FMT, 2, 2><<<blocks, 256, 0, st>>>(hd, D, info, n_act, y, d, f);
-    else
-      dec_down_persist<FMT, 4, 2><<<blocks, 256, 0, st>>>(hd, D, info, n_act, y, d, f);
-    mark(p, MOE_STAGE_DOWN, true, st);
   } else if (path_for(p, T) == MOE_PATH_DECODE) {
     mark(p, MOE_STAGE_GATEUP, false, st);
     if (qdq) launch_act_qdq(x_in, xq, T, d, st);
-    launch_dec<FMT, true>(p, T, L.n_slots, f, d, x, nullptr, G, U, info, tok_of, h, nullptr, st);
+    launch_dec<FMT, true>(T, L.n_slots, f, d, x, nullptr, G, U, info, tok_of, h, nullptr, st);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
     if (qdq) launch_act_qdq(h, hq, S_all, f, st);
-    launch_dec<FMT, false>(p, T, L.n_slots, d, f, nullptr, hd, D, D, info, tok_of, nullptr, y, st);
+    launch_dec<FMT, false>(T, L.n_slots, d, f, nullptr, hd, D, D, info, tok_of, nullptr, y, st);
     mark(p, MOE_STAGE_DOWN, true, st);
   } else {
     const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
-    const int bm = gemm_bm(p, T);
-    if (p->gemm_kernel == 2) {
-      mark(p, MOE_STAGE_GATEUP, false, st);
-      launch_dma<FMT, true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
-      mark(p, MOE_STAGE_GATEUP, true, st);
-      mark(p, MOE_STAGE_DOWN, false, st);
-      launch_dma<FMT, false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
-      mark(p, MOE_STAGE_DOWN, true, st);
-      return MOE_OK;
-    }
-    if (p->gemm_kernel == 3) {
-      mark(p, MOE_STAGE_GATEUP, false, st);
-      launch_big<FMT, true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
-      mark(p, MOE_STAGE_GATEUP, true, st);
-      mark(p, MOE_STAGE_DOWN, false, st);
-      launch_big<FMT, false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
-      mark(p, MOE_STAGE_DOWN, true, st);
-      return MOE_OK;
-    }
-    if (p->gemm_kernel == 1) {
-      mark(p, MOE_STAGE_GATEUP, false, st);
-      launch_rw<FMT, true, 1, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
-      mark(p, MOE_STAGE_GATEUP, true, st);
-      mark(p, MOE_STAGE_DOWN, false, st);
-      launch_rw<FMT, false, 2, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
-      mark(p, MOE_STAGE_DOWN, true, st);
-      return MOE_OK;
-    }
     mark(p, MOE_STAGE_GATEUP, false, st);
-    if (bm == 128)
-      launch_gemm<FMT, true, 128, 2, 1, 64, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
-                                               tok_of, h, st);
-    else if (bm == 64)
-      launch_gemm<FMT, true, 64, 2, 1, 64, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
-                                              tok_of, h, st);
-    else
-      launch_gemm<FMT, true, 32, 1, 1, 64, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles,
-                                              tok_of, h, st);
+    launch_big<FMT, true, 1>(p, L.max_tiles, f, d, T, x, G, U, tiles, n_tiles, tok_of, h, st);
     mark(p, MOE_STAGE_GATEUP, true, st);
     mark(p, MOE_STAGE_DOWN, false, st);
-    if (bm == 128)
-      launch_gemm<FMT, false, 128, 2, 2, 64, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
-                                                tok_of, y, st);
-    else if (bm == 64)
-      launch_gemm<FMT, false, 64, 2, 2, 64, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
-                                               tok_of, y, st);
-    else
-      launch_gemm<FMT, false, 32, 1, 1, 64, 1>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles,
-                                               tok_of, y, st);
+    launch_big<FMT, false, 2>(p, L.max_tiles, d, f, T, h, D, D, tiles, n_tiles, tok_of, y, st);
     mark(p, MOE_STAGE_DOWN, true, st);
   }
   hipError_t err = hipGetLastError();
@@ -677,39 +481,17 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   // grouped at 384), 14*E for fp4 (the e2m1 and NVFP4 layers: decode ahead at
   // 768 by 6 and 4 %, grouped at 1024 by 12 and 14 %).
   p->t_decode = std::max(1, (d.wfmt == MOE_W_E4M3_B128 ? 10 : 14) * d.n_experts / d.top_k);
-  // tuning knobs of the decode matvec
-  if (const char* v = std::getenv("MOE_DEC_NRG")) p->dec_nrg = std::atoi(v);
-  if (const char* v = std::getenv("MOE_DEC_STREAM")) p->dec_stream = std::atoi(v);
-  if (const char* v = std::getenv("MOE_DEC_PERSIST")) p->dec_persist = std::atoi(v);
-  if (const char* v = std::getenv("MOE_DEC_WPB")) p->dec_wpb = std::max(1, std::min(16, std::atoi(v)));
-  if (const char* v = std::getenv("MOE_DEC_KERNEL")) p->dec_kernel = std::atoi(v) == 0 ? 0 : 1;
-  if (const char* v = std::getenv("MOE_DEC_MFMA_MIN_T")) p->dec_mfma_min_t = std::max(1, std::atoi(v));
-  if (const char* v = std::getenv("MOE_DEC_TALL")) p->dec_tall = std::max(-1, std::min(1, std::atoi(v)));
-  if (const char* v = std::getenv("MOE_ROUTER_SPLIT")) p->router_split = std::max(0, std::min(8, std::atoi(v)));
-  if (const char* v = std::getenv("MOE_SMALL_ROUTE_T")) p->small_route_t = std::max(1, std::min(64, std::atoi(v)));
-  if (const char* v = std::getenv("MOE_DEC_KS")) p->dec_ks = std::max(0, std::min(4, std::atoi(v)));
-  if (const char* v = std::getenv("MOE_Q8_TM")) p->q8_tm = std::max(0, std::min(3, std::atoi(v)));
-  if (const char* v = std::getenv("MOE_BIG_CFG")) {
-    const int c = std::atoi(v);
-    p->big_cfg = (c == 11 || c == 12 || c == 22 || c == 23 || c == 24) ? c : 0;
-  }
-  // the 128..256-token direct-to-LDS tiles (gemm_big) measured fastest on
-  // every grouped shape of every format (OLMoE shape at 128, 512 and 2048
-  // tokens, the d = 7168 layer at 512 and 4096, the fp4 layer at 1024)
-  p->gemm_kernel = 3;
-  if (const char* v = std::getenv("MOE_GEMM")) p->gemm_kernel = std::max(0, std::min(3, std::atoi(v)));
   char buf[512];
   std::snprintf(buf, sizeof buf,
                 "device %d %s (%d CUs); d=%d f=%d E=%d k=%d fmt=%s renorm=%d; path=%s "
                 "(decode for T<=%d); router: wavefront gemv up to %d tokens, else 64x64 bf16x3 MFMA tiles, split-K; "
-                "decode: MFMA 16-row tiles from %d tokens, matvec below; grouped kernel %d "
-                "(3: 128/192/256-token tiles by slots per expert, direct-to-LDS; 0: LDS-decoded weight tiles), "
-                "MFMA 32x32x16 bf16, BK 64",
+                "decode: MFMA 16-row tiles from %d tokens, matvec below; grouped: 128/192/256-token "
+                "tiles by slots per expert, direct-to-LDS, MFMA 32x32x16 bf16",
                 dev, p->arch.c_str(), p->cus, d.d_model, d.d_ff, d.n_experts, d.top_k,
                 d.wfmt == MOE_W_E4M3_B128 ? "e4m3/128x128"
                 : d.wfmt == MOE_W_E2M1_UE8M0_G32 ? "e2m1/ue8m0x32" : "e2m1/e4m3x16", d.renorm,
                 d.path == MOE_PATH_AUTO ? "auto" : (d.path == MOE_PATH_DECODE ? "decode" : "grouped"),
-                p->t_decode, GEMV_MAX_T, p->dec_mfma_min_t, p->gemm_kernel);
+                p->t_decode, GEMV_MAX_T, p->dec_mfma_min_t);
   p->info = buf;
   if (d.act_fmt == MOE_ACT_E4M3_G128)
     p->info += "; activations: e4m3 per 128-input group (UE8M0 scales); grouped path: "
@@ -717,6 +499,33 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
                "kernels on the quantised values as bf16";
   *out = p;
   return MOE_OK;
+}
+
+moe_status moe_plan_set(moe_plan_t p, int32_t option, int32_t value) {
+  if (p == nullptr) return MOE_ERR_NULL_ARG;
+  switch (option) {
+    case MOE_OPT_DEC_KERNEL:
+      if (value != 0 && value != 1) return MOE_ERR_BAD_SHAPE;
+      p->dec_kernel = value;
+      return MOE_OK;
+    case MOE_OPT_DEC_MFMA_MIN_T:
+      if (value < 1) return MOE_ERR_BAD_SHAPE;
+      p->dec_mfma_min_t = value;
+      return MOE_OK;
+    case MOE_OPT_GROUPED_TILE:
+      if (value != 0 && value != 128 && value != 192 && value != 256) return MOE_ERR_BAD_SHAPE;
+      p->big_cfg = value == 0 ? 0 : 20 + value / 64;
+      return MOE_OK;
+    case MOE_OPT_Q8_TILE:
+      if (value != 0 && value != 64 && value != 128 && value != 192) return MOE_ERR_BAD_SHAPE;
+      p->q8_tm = value / 64;
+      return MOE_OK;
+    case MOE_OPT_SMALL_ROUTE_T:
+      if (value < 0 || value > 64) return MOE_ERR_BAD_SHAPE;
+      p->small_route_t = value;
+      return MOE_OK;
+  }
+  return MOE_ERR_UNSUPPORTED;
 }
 
 moe_status moe_rmsnorm(int32_t n_tokens, int32_t d, const uint16_t* x, const uint16_t* gamma,
@@ -759,7 +568,8 @@ moe_status moe_act_quant(int32_t rows, int32_t K, const uint16_t* x, uint8_t* q,
 
 moe_status moe_timing_disable(moe_plan_t p) {
   if (p == nullptr) return MOE_ERR_NULL_ARG;
-  for (hipEvent_t e : p->timing_ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->timing_ev)
+    if (e != nullptr) (void)hipEventDestroy(e);  // stages outside the mask have none
   p->timing_ev.clear();
   p->timing_done.clear();
   p->timing_mask = 0;
@@ -847,11 +657,15 @@ int32_t moe_plan_path(moe_plan_t p, int32_t T) {
   return path_for(p, T);
 }
 
-moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* w_router,
-                       const float* logit_bias, const moe_mat* gate, const moe_mat* up,
-                       const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
-                       int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float* w_router,
+                        const float* logit_bias, const moe_mat* gate, const moe_mat* up,
+                        const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (p == nullptr) return MOE_ERR_NULL_ARG;
   if (T < 0 || T > p->d.max_tokens) return MOE_ERR_BAD_SHAPE;
   if (T == 0) return MOE_OK;
@@ -1014,6 +828,19 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
   err = hipGetLastError();
   if (err != hipSuccess) return hip_fail(p, err, "combine launch");
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* w_router,
+                       const float* logit_bias, const moe_mat* gate, const moe_mat* up,
+                       const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return forward_impl(p, T, x, w_router, logit_bias, gate, up, down, out, topk_ids, topk_w, counts,
+                      offsets, perm, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -260,101 +260,10 @@ __device__ __forceinline__ void dec_matvec(const uint8_t* const (&q)[NM],
   }
 }
 
-// Streaming variant for rows that fit one pass (K <= 16 * 64 * CPL): every
-// lane owns chunks lane, lane+64, ..., lane+64*(CPL-1) of every row.  A
-// wavefront walks NRG groups of RPW consecutive rows of one expert: the
-// slots' activation chunks are loaded into registers once, and the next
-// row group's weights are loaded before the current group is decoded,
-// multiplied and reduced, so the weight stream does not stall on the
-// reductions.
-template <int FMT, int NM, int TG, int CPL, int RPW, typename ActRow, typename Store>
-__device__ __forceinline__ void dec_stream(const uint8_t* const (&q)[NM],
-                                           const uint8_t* const (&s)[NM], int n0, int nrows,
-                                           int K, int cnt, ActRow act_row, Store store) {
-  const int lane = lane_id();
-  const int nch = K / 16;
-  const int64_t rb = row_bytes<FMT>(K);
-  typedef typename Chunk<FMT>::raw raw;
-  for (int t0 = 0; t0 < cnt; t0 += TG) {
-    const int ntok = min(TG, cnt - t0);
-    uint32_t xv[TG][CPL][8];
-#pragma unroll
-    for (int t = 0; t < TG; ++t)
-      if (t < ntok) {
-        const uint16_t* a = act_row(t0 + t);
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = lane + WAVE * j;
-          if (c < nch) load_act16(a, c, xv[t][j]);
-        }
-      }
-    raw wc[NM][RPW][CPL], wn[NM][RPW][CPL];
-    auto load_group = [&](raw (&w)[NM][RPW][CPL], int r0) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            const int c = lane + WAVE * j;
-            if (c < nch && r0 + r < nrows) w[m][r][j] = Chunk<FMT>::load(q[m] + (r0 + r) * rb, c);
-          }
-    };
-    load_group(wc, 0);
-    for (int r0 = 0; r0 < nrows; r0 += RPW) {
-      if (r0 + RPW < nrows) load_group(wn, r0 + RPW);
-      float acc[NM][RPW][TG];
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-          for (int t = 0; t < TG; ++t) acc[m][r][t] = 0.0f;
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            const int c = lane + WAVE * j;
-            if (c < nch) {
-              const float sc = Chunk<FMT>::scale(s[m], n0 + r0 + r, c, K);
-              bf16x2 wb[8];
-              Chunk<FMT>::decode(wc[m][r][j], sc, wb);
-#pragma unroll
-              for (int t = 0; t < TG; ++t)
-                if (t < ntok) {
-                  const float p = dot16(wb, xv[t][j]);
-                  acc[m][r][t] = Chunk<FMT>::kPostScale ? fmaf(p, sc, acc[m][r][t])
-                                                        : acc[m][r][t] + p;
-                }
-            }
-          }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int t = 0; t < TG; ++t)
-          if (t < ntok && r0 + r < nrows) {
-            float v[NM];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) v[m] = wave_sum(acc[m][r][t]);
-            if (lane == r * TG + t) store(t0 + t, r0 + r, v);
-          }
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) wc[m][r][j] = wn[m][r][j];
-    }
-  }
-}
-
 // Gate/up + SwiGLU: for every slot of the expert (sorted position p),
 // h[p][n] = bf16(silu(g[n]) * u[n]).  grid.x: slot_info entry; grid.y:
-// blocks of (blockDim / 64) wavefronts x `rpw_total` rows.  CPL = 0 selects the looping
-// matvec (rows longer than one pass).
-template <int FMT, int TG, int CPL, int RPW>
+// blocks of (blockDim / 64) wavefronts x `rpw_total` rows.
+template <int FMT, int TG, int RPW>
 __global__ __launch_bounds__(1024) void dec_gateup(
     const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ slot_info,
     const int32_t* __restrict__ tok_of, uint16_t* __restrict__ h, int d, int f, int T,
@@ -374,20 +283,16 @@ __global__ __launch_bounds__(1024) void dec_gateup(
   auto store = [&](int i, int r, const float (&v)[2]) {
     h[(size_t)(p0 + i) * f + n0 + r] = (uint16_t)f32_to_bf16_rne(silu(v[0]) * v[1]);
   };
-  if (CPL == 0) {
-    for (int r0 = 0; r0 < nrows; r0 += RPW) {
-      const uint8_t* const qq[2] = {q[0] + r0 * rb, q[1] + r0 * rb};
-      auto st2 = [&](int i, int r, const float (&v)[2]) { store(i, r0 + r, v); };
-      dec_matvec<FMT, 2, TG, RPW, 2>(qq, s, n0 + r0, d, cnt, act_row, st2);
-    }
-  } else {
-    dec_stream<FMT, 2, TG, (CPL > 0 ? CPL : 1), RPW>(q, s, n0, nrows, d, cnt, act_row, store);
+  for (int r0 = 0; r0 < nrows; r0 += RPW) {
+    const uint8_t* const qq[2] = {q[0] + r0 * rb, q[1] + r0 * rb};
+    auto st2 = [&](int i, int r, const float (&v)[2]) { store(i, r0 + r, v); };
+    dec_matvec<FMT, 2, TG, RPW, 2>(qq, s, n0 + r0, d, cnt, act_row, st2);
   }
 }
 
 // Down projection: y[p][m] = sum_n h[p][n] Wd[m][n] (f32) for every sorted
 // position p of the expert.
-template <int FMT, int TG, int CPL, int RPW>
+template <int FMT, int TG, int RPW>
 __global__ __launch_bounds__(1024) void dec_down(
     const uint16_t* __restrict__ h, DMat down, const int4* __restrict__ slot_info,
     float* __restrict__ y, int d, int f, int rpw_total) {
@@ -402,63 +307,10 @@ __global__ __launch_bounds__(1024) void dec_down(
   const uint8_t* const s[1] = {down.s + e * down.ss};
   auto act_row = [&](int i) -> const uint16_t* { return h + (size_t)(p0 + i) * f; };
   auto store = [&](int i, int r, const float (&v)[1]) { y[(size_t)(p0 + i) * d + m0 + r] = v[0]; };
-  if (CPL == 0) {
-    for (int r0 = 0; r0 < nrows; r0 += RPW) {
-      const uint8_t* const qq[1] = {q[0] + r0 * rb};
-      auto st1 = [&](int i, int r, const float (&v)[1]) { store(i, r0 + r, v); };
-      dec_matvec<FMT, 1, TG, RPW, 2>(qq, s, m0 + r0, f, cnt, act_row, st1);
-    }
-  } else {
-    dec_stream<FMT, 1, TG, (CPL > 0 ? CPL : 1), RPW>(q, s, m0, nrows, f, cnt, act_row, store);
-  }
-}
-
-// Persistent variant: a fixed grid of wavefronts walks the work items
-// (expert slot i, group of RPW rows) in a grid-stride loop, item = i * G + g
-// with G = ceil(N / RPW), so neighbouring wavefronts read neighbouring rows
-// of the same expert and no workgroup is launched per item.
-template <int FMT, int TG, int RPW>
-__global__ __launch_bounds__(256) void dec_gateup_persist(
-    const uint16_t* __restrict__ x, DMat gate, DMat up, const int4* __restrict__ slot_info,
-    const int32_t* __restrict__ n_active, const int32_t* __restrict__ tok_of,
-    uint16_t* __restrict__ h, int d, int f, int T) {
-  const int G = (f + RPW - 1) / RPW;
-  const int items = *n_active * G;
-  const int W = gridDim.x * 4;
-  const int64_t rb = row_bytes<FMT>(d);
-  for (int item = blockIdx.x * 4 + wave_id(); item < items; item += W) {
-    const int i = item / G, n0 = (item - i * G) * RPW;
-    const int4 info = slot_info[i];
-    const int e = info.x, p0 = info.y, cnt = info.z;
-    const uint8_t* const q[2] = {gate.q + e * gate.qs + n0 * rb, up.q + e * up.qs + n0 * rb};
-    const uint8_t* const s[2] = {gate.s + e * gate.ss, up.s + e * up.ss};
-    auto act_row = [&](int j) -> const uint16_t* {
-      return x + (size_t)min((uint32_t)tok_of[p0 + j], (uint32_t)(T - 1)) * d;
-    };
-    auto store = [&](int j, int r, const float (&v)[2]) {
-      h[(size_t)(p0 + j) * f + n0 + r] = (uint16_t)f32_to_bf16_rne(silu(v[0]) * v[1]);
-    };
-    dec_matvec<FMT, 2, TG, RPW, 2>(q, s, n0, d, cnt, act_row, store);
-  }
-}
-
-template <int FMT, int TG, int RPW>
-__global__ __launch_bounds__(256) void dec_down_persist(
-    const uint16_t* __restrict__ h, DMat down, const int4* __restrict__ slot_info,
-    const int32_t* __restrict__ n_active, float* __restrict__ y, int d, int f) {
-  const int G = (d + RPW - 1) / RPW;
-  const int items = *n_active * G;
-  const int W = gridDim.x * 4;
-  const int64_t rb = row_bytes<FMT>(f);
-  for (int item = blockIdx.x * 4 + wave_id(); item < items; item += W) {
-    const int i = item / G, m0 = (item - i * G) * RPW;
-    const int4 info = slot_info[i];
-    const int e = info.x, p0 = info.y, cnt = info.z;
-    const uint8_t* const q[1] = {down.q + e * down.qs + m0 * rb};
-    const uint8_t* const s[1] = {down.s + e * down.ss};
-    auto act_row = [&](int j) -> const uint16_t* { return h + (size_t)(p0 + j) * f; };
-    auto store = [&](int j, int r, const float (&v)[1]) { y[(size_t)(p0 + j) * d + m0 + r] = v[0]; };
-    dec_matvec<FMT, 1, TG, RPW, 2>(q, s, m0, f, cnt, act_row, store);
+  for (int r0 = 0; r0 < nrows; r0 += RPW) {
+    const uint8_t* const qq[1] = {q[0] + r0 * rb};
+    auto st1 = [&](int i, int r, const float (&v)[1]) { store(i, r0 + r, v); };
+    dec_matvec<FMT, 1, TG, RPW, 2>(qq, s, m0 + r0, f, cnt, act_row, st1);
   }
 }
 

@@ -9,8 +9,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (MOE_PATH_AUTO, Plan, mat, moe_forward, moe_plan, moe_workspace_h_offset,
-               moe_workspace_size)
+from . import (MOE_PATH_AUTO, Plan, mat, moe_forward, moe_plan, moe_plan_set,
+               moe_workspace_h_offset, moe_workspace_size)
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -56,10 +56,13 @@ class Runner:
     """A plan for one layer shape plus a workspace sized for `max_tokens`."""
 
     def __init__(self, d: int, f: int, E: int, k: int, fmt: str, renorm: bool, max_tokens: int,
-                 path: int = MOE_PATH_AUTO, device="cuda", act_fmt: int = 0):
+                 path: int = MOE_PATH_AUTO, device="cuda", act_fmt: int = 0,
+                 options: Optional[dict] = None):
         self.d, self.f, self.E, self.k = d, f, E, k
         self.device = device
         self.plan: Plan = moe_plan(d, f, E, k, max_tokens, fmt, renorm, path, act_fmt)
+        for opt, val in (options or {}).items():
+            moe_plan_set(self.plan, opt, val)
         self.max_tokens = max_tokens
         nbytes = max(moe_workspace_size(self.plan, max_tokens), 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)

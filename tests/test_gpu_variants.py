@@ -1,18 +1,18 @@
-"""GPU parity of the expert-stage kernels that the default dispatch does not
-pick for these shapes but that a plan can be switched to (MOE_GEMM and
-MOE_BIG_CFG for the grouped path, MOE_DEC_KERNEL / MOE_DEC_MFMA_MIN_T for the
-decode path): each
-one against the CPU oracle with the same bars as the default path.  The
-shapes carry the tails the kernels guard: K = 160 (an fp4 k-tail of 32
-inputs against 64-input stages), N = 96 and 384 (partial 128- and 256-row
-column blocks), 37 and 70 tokens (partial 64-token tiles), and one expert
-holding every slot (several 64-token tiles of one expert)."""
-import os
-
+"""GPU parity of the expert-stage and routing variants that the default
+dispatch does not pick for these shapes but that a plan can be switched to
+with moe_plan_set (MOE_OPT_GROUPED_TILE for the grouped path,
+MOE_OPT_DEC_KERNEL / MOE_OPT_DEC_MFMA_MIN_T for the decode path,
+MOE_OPT_SMALL_ROUTE_T for the routing stage): each one against the CPU
+oracle with the same bars as the default path.  The shapes carry the tails
+the kernels guard: K = 160 (an fp4 k-tail of 32 inputs against 64-input
+stages), N = 96 and 384 (partial 128- and 256-row column blocks), 37, 70 and
+150 tokens (partial tiles), and one expert holding every slot (several tiles
+of one expert)."""
 import numpy as np
 import pytest
 
 import synth
+import mixture_experts_layer_f32_amd as moe
 from gpu_util import check_h, check_out, check_routing, device_weights, gpu_run, oracle_run
 
 pytestmark = pytest.mark.gpu
@@ -35,19 +35,9 @@ def get(fmt):
     return _cache[fmt]
 
 
-def run_with_env(env, wl, W, batch, path):
-    """Plan, forward and outputs with the given tuning switches set while the
-    plan is made (moe_plan reads them)."""
-    old = {k: os.environ.get(k) for k in env}
-    os.environ.update(env)
-    try:
-        g, run = gpu_run(wl, W, batch, path)
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+def run_with_options(opts, wl, W, batch, path):
+    """Plan with the given options set (moe_plan_set), forward, outputs."""
+    g, run = gpu_run(wl, W, batch, path, options=opts)
     return g
 
 
@@ -58,29 +48,15 @@ def check_all(g, ref):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("gemm", ["0", "1", "2", "3"])
-def test_grouped_kernels(fmt, gemm):
+@pytest.mark.parametrize("tile", [128, 192, 256])
+def test_grouped_tiles(fmt, tile):
+    """Every tile height of the grouped kernel on a batch of a few tokens per
+    expert (partial tiles, chunks past the rows)."""
     wl, layer, W = get(fmt)
     T = wl.batches[0]
     batch = synth.make_batch(wl, layer, T)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_env({"MOE_GEMM": gemm}, wl, W, batch, GROUPED), ref)
-
-
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("gemm", ["0", "1", "2", "3"])
-def test_grouped_kernels_one_expert_many_tiles(fmt, gemm):
-    """A large bias on expert 1 sends all 150 tokens there: that expert spans
-    three 64-token tiles (the last one partial), the others share the rest."""
-    wl, layer, W = get(fmt)
-    T = 150
-    batch = synth.make_batch(wl, layer, T)
-    bias = np.zeros((T, wl.E), np.float32)
-    bias[:, 1] = 100.0
-    batch = synth.Batch(batch.x, bias)
-    ref = oracle_run(wl, layer, batch)
-    assert ref.counts[1] == T
-    check_all(run_with_env({"MOE_GEMM": gemm}, wl, W, batch, GROUPED), ref)
+    check_all(run_with_options({moe.MOE_OPT_GROUPED_TILE: tile}, wl, W, batch, GROUPED), ref)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
@@ -90,7 +66,7 @@ def test_decode_matvec_kernel(fmt, T):
     wl, layer, W = get(fmt)
     batch = synth.make_batch(wl, layer, T)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_env({"MOE_DEC_KERNEL": "0"}, wl, W, batch, DECODE), ref)
+    check_all(run_with_options({moe.MOE_OPT_DEC_KERNEL: 0}, wl, W, batch, DECODE), ref)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
@@ -99,15 +75,16 @@ def test_decode_mfma_one_token(fmt):
     wl, layer, W = get(fmt)
     batch = synth.make_batch(wl, layer, 1)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_env({"MOE_DEC_MFMA_MIN_T": "1"}, wl, W, batch, DECODE), ref)
+    check_all(run_with_options({moe.MOE_OPT_DEC_MFMA_MIN_T: 1}, wl, W, batch, DECODE), ref)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("cfg", ["11", "12", "22", "23", "24"])
-def test_big_tile_shapes(fmt, cfg):
-    """Every tile shape of the default grouped kernel (MOE_GEMM=3): 32 x 256,
-    64 x 256, 128 x 128, 192 x 128 and 256 x 128 tokens x rows per matrix, on
-    the one-expert batch (one expert spans several tiles of the small shapes)."""
+@pytest.mark.parametrize("tile", [128, 192, 256])
+def test_grouped_tiles_one_expert_many_tiles(fmt, tile):
+    """A large bias on expert 1 sends all 150 tokens there: at 128-token tiles
+    that expert spans two tiles (the last one partial), at 192 and 256 one
+    partial tile; the chunks of a tile are shared out between the wavefront
+    rows, so every count of active chunks per wavefront occurs."""
     wl, layer, W = get(fmt)
     T = 150
     batch = synth.make_batch(wl, layer, T)
@@ -115,18 +92,34 @@ def test_big_tile_shapes(fmt, cfg):
     bias[:, 1] = 100.0
     batch = synth.Batch(batch.x, bias)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_env({"MOE_GEMM": "3", "MOE_BIG_CFG": cfg}, wl, W, batch, GROUPED), ref)
+    assert ref.counts[1] == T
+    check_all(run_with_options({moe.MOE_OPT_GROUPED_TILE: tile}, wl, W, batch, GROUPED), ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
+@pytest.mark.parametrize("T", [33, 65, 97, 129, 161, 193, 225, 256])
+def test_grouped_chunk_counts(fmt, T):
+    """One expert holding T slots in one 256-token tile: 2..8 active 32-row
+    chunks, so each wavefront row takes every count from 1 to 4 (and odd
+    splits, where the two rows differ by one chunk)."""
+    wl, layer, W = get(fmt)
+    batch = synth.make_batch(wl, layer, T)
+    bias = np.zeros((T, wl.E), np.float32)
+    bias[:, 1] = 100.0
+    batch = synth.Batch(batch.x, bias)
+    ref = oracle_run(wl, layer, batch)
+    check_all(run_with_options({moe.MOE_OPT_GROUPED_TILE: 256}, wl, W, batch, GROUPED), ref)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("T,path", [(17, DECODE), (37, DECODE), (64, GROUPED)])
 def test_one_workgroup_routing_up_to_64_tokens(fmt, T, path):
-    """Top-k and permute in one workgroup (MOE_SMALL_ROUTE_T) for 17..64 tokens:
+    """Top-k and permute in one workgroup (MOE_OPT_SMALL_ROUTE_T) for 17..64 tokens:
     several row-group tiles per expert in the tile list, against the oracle."""
     wl, layer, W = get(fmt)
     batch = synth.make_batch(wl, layer, T)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_env({"MOE_SMALL_ROUTE_T": "64"}, wl, W, batch, path), ref)
+    check_all(run_with_options({moe.MOE_OPT_SMALL_ROUTE_T: 64}, wl, W, batch, path), ref)
 
 
 def test_one_workgroup_routing_olmoe_shape():
@@ -136,4 +129,4 @@ def test_one_workgroup_routing_olmoe_shape():
     W = device_weights(layer)
     batch = synth.make_batch(wl, layer, 64)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_env({"MOE_SMALL_ROUTE_T": "64"}, wl, W, batch, DECODE), ref)
+    check_all(run_with_options({moe.MOE_OPT_SMALL_ROUTE_T: 64}, wl, W, batch, DECODE), ref)
