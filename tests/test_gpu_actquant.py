@@ -4,17 +4,19 @@ zero groups, values far below their group's maximum, negative zeros and rows
 whose length is not a multiple of 128), and the whole layer with x and h
 quantised, on e4m3 and e2m1 weights, every tile height of the block-scaled
 GEMM, with k-tails (e2m1: K = 192 and 320, a 64-input last group), partial
-column blocks and one expert spanning several tiles.  Routing is bit-exact;
-out within the same bars as the default path, against the oracle's own
-quantised layer."""
-import os
-
+column blocks and one expert spanning several tiles.  Routing is bit-exact.
+out is checked twice: end to end against the oracle's own quantised layer
+(on the decode route, whose bf16 MFMA sums the exact quantised values, at the
+default bars; on the grouped path, whose fp8 MFMA rounds inside, at the
+variant's own bars, derived in gpu_util), and step by step against the
+oracle's down projection fed the GPU's own h at the default bars."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_util import check_out, check_routing, device_weights, log, omat, out_errors
+from gpu_util import (check_h, check_out, check_out_actq, check_routing, device_weights, log,
+                      omat)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,26 +68,28 @@ def run_q8(wl, W, batch, tm=None, path=None):
     path, else `path` (default AUTO: decode sizes run the decode kernels on
     the quantised values as bf16)."""
     import torch
+    import mixture_experts_layer_f32_amd as m
     from mixture_experts_layer_f32_amd.device import Runner, to_dev
     T = batch.x.shape[0]
     if path is None:
         path = GROUPED if tm is not None else 0
-    old = os.environ.get("MOE_Q8_TM")
-    if tm is not None:
-        os.environ["MOE_Q8_TM"] = str(tm)
-    try:
-        run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path, act_fmt=1)
-    finally:
-        if old is None:
-            os.environ.pop("MOE_Q8_TM", None)
-        else:
-            os.environ["MOE_Q8_TM"] = old
+    opts = {m.MOE_OPT_Q8_TILE: 64 * tm} if tm is not None else None
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path, act_fmt=1, options=opts)
     outs = run.outputs(T)
     run.forward(W, to_dev(batch.x), to_dev(batch.bias) if batch.bias is not None else None, outs)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in outs.items()}
     res["h"] = run.h(T).cpu().numpy().view(np.uint16)
+    res["path"] = "decode" if m.moe_plan_path(run.plan, T) == DECODE else "grouped"
     return res
+
+
+def check_out_q8_e2e(g, ref_out, rows=None):
+    """out against the oracle's own quantised layer: the decode route's h
+    equals the oracle's bit for bit, so it is held to the default bars; the
+    grouped path's to the variant's own."""
+    got = g["out"] if rows is None else g["out"][rows]
+    return check_out(got, ref_out) if g["path"] == "decode" else check_out_actq(got, ref_out)
 
 
 def q8_reference(wl, layer, batch, ref, g_h, tokens):
@@ -159,9 +163,10 @@ def test_act_quant_layer(fmt, T, tm):
     eq = check_h_q8(g["h"], ref.h)
     _, out_ref = q8_reference(wl, layer, batch, ref, g["h"], np.arange(T))
     mx, rms, mrel = check_out(g["out"], out_ref)
-    _, _, mrel_o = out_errors(g["out"], ref.out)
-    log(f"act-quant {fmt} T={T} tm={tm}: h equal {eq:.4f}, max|err| {mx:.3e} rms {rms:.3e} "
-        f"mean rel {mrel:.3e} (against the oracle's own h: mean rel {mrel_o:.3e})")
+    mx_o, _, mrel_o = check_out_q8_e2e(g, ref.out)
+    log(f"act-quant {fmt} T={T} tm={tm} ({g['path']}): h equal {eq:.4f}; against the oracle's "
+        f"down fed this h: max|err| {mx:.3e} rms {rms:.3e} mean rel {mrel:.3e}; end to end: "
+        f"max|err| {mx_o:.3e} mean rel {mrel_o:.3e}")
 
 
 def test_act_quant_differs_from_bf16_layer():
@@ -195,6 +200,7 @@ def test_act_quant_dense_branch(fmt):
     check_h_q8(g["h"], ref.h)
     _, out_ref = q8_reference(wl, layer, batch, ref, g["h"], np.arange(100))
     check_out(g["out"], out_ref)
+    check_out_q8_e2e(g, ref.out)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
@@ -213,5 +219,9 @@ def test_act_quant_decode_route(fmt, T, path):
     eq = check_h_q8(g["h"], ref.h)
     _, out_ref = q8_reference(wl, layer, batch, ref, g["h"], np.arange(T))
     mx, rms, mrel = check_out(g["out"], out_ref)
-    log(f"act-quant {fmt} T={T} path={path}: h equal {eq:.4f}, max|err| {mx:.3e} mean rel {mrel:.3e}")
+    mx_o, _, mrel_o = check_out_q8_e2e(g, ref.out)
+    if path == DECODE:  # the bf16 MFMA on exact quantised values: the default path's h bars
+        check_h(g["h"], ref.h)
+    log(f"act-quant {fmt} T={T} path={path}: h equal {eq:.4f}, max|err| {mx:.3e} mean rel "
+        f"{mrel:.3e}; end to end max|err| {mx_o:.3e} mean rel {mrel_o:.3e}")
 

@@ -253,9 +253,9 @@ def test_largest_expert_count_and_top_k(wl, T, path):
 @pytest.mark.parametrize("T", [1, 16, 100])
 def test_largest_expert_count_and_top_k_act_quant(T):
     """The same limits (1024 experts, top-16) on the activation-quantised plan:
-    routing bit-exact, h and out against the oracle's quantised layer (down
-    fed the GPU's own h)."""
-    from test_gpu_actquant import check_h_q8, oracle_q8, q8_reference, run_q8
+    routing bit-exact, h and out against the oracle's quantised layer, end to
+    end and with the down projection fed the GPU's own h."""
+    from test_gpu_actquant import check_h_q8, check_out_q8_e2e, oracle_q8, q8_reference, run_q8
     L, W = get(WL_MAX)
     batch = synth.make_batch(WL_MAX, L, T)
     ref = oracle_q8(WL_MAX, L, batch)
@@ -264,3 +264,35 @@ def test_largest_expert_count_and_top_k_act_quant(T):
     check_h_q8(g["h"], ref.h)
     _, out_ref = q8_reference(WL_MAX, L, batch, ref, g["h"], np.arange(T))
     check_out(g["out"], out_ref)
+    check_out_q8_e2e(g, ref.out)
+
+
+@pytest.mark.parametrize("stages", [("gateup",), ("router", "combine"), None])
+def test_stage_timing_leaves_no_error(stages):
+    """Stage timing with any subset of stages: the recorded times are positive
+    for the timed stages and zero for the others, and after the timing is
+    switched off the next forward runs and matches the oracle (destroying the
+    timing events must not leave an error behind for the next launch check)."""
+    import torch
+    import mixture_experts_layer_f32_amd as moe
+    from mixture_experts_layer_f32_amd.device import Runner, to_dev
+    wl = WL
+    L, W = get(wl)
+    T = 8
+    batch = synth.make_batch(wl, L, T)
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T)
+    outs = run.outputs(T)
+    x = to_dev(batch.x)
+    sel = moe.STAGES if stages is None else stages
+    moe.moe_timing_enable(run.plan, sel, max_forwards=4)
+    for _ in range(3):
+        run.forward(W, x, None, outs)
+    ms, n = moe.moe_timing_collect(run.plan)
+    moe.moe_timing_disable(run.plan)
+    assert n == 3
+    assert all(ms[s] > 0 for s in ("gateup",) if s in sel)
+    assert all(ms[s] == 0 for s in moe.STAGES if s not in sel)
+    run.forward(W, x, None, outs)
+    torch.cuda.synchronize()
+    ref = oracle_run(wl, L, batch)
+    check_out(outs["out"].cpu().numpy(), ref.out)
