@@ -186,6 +186,33 @@ moe_status moe_forward(moe_plan_t plan, int32_t n_tokens, const uint16_t* x, con
                        int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The same forward for callers that cannot allocate device memory or bring
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments and results as moe_forward, without the
+ * workspace: the kernels use instead a scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * (statically, until the process ends; its address is looked up once per
+ * device when the first plan is made there).  This call allocates nothing and
+ * calls no allocating routine.
+ *   - MOE_ERR_WORKSPACE if moe_workspace_size(plan, n_tokens) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES (64 MiB: every decode size of the layers in
+ *     this repository, and grouped batches up to a few hundred tokens);
+ *   - MOE_ERR_HIP if the scratch address could not be found for the plan's
+ *     device.
+ * Every call on one device shares that device's scratch and leaves its
+ * contents there (the kernels need no cleared scratch): calls that overlap
+ * in time on one device, on any streams, race and corrupt each other's
+ * results; serialise them (one stream, or events). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(moe_plan_t plan, int32_t n_tokens, const uint16_t* x,
+                               const float* w_router, const float* logit_bias,
+                               const moe_mat* gate, const moe_mat* up, const moe_mat* down,
+                               float* out, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                               int32_t* offsets, int32_t* perm, void* stream);
+
+/* MOE_NOALLOC_SCRATCH_BYTES, as a function for bindings that do not read the header. */
+size_t moe_noalloc_scratch_bytes(void);
+
 /* Byte offset, inside the workspace of a forward over n_tokens tokens, of
  * the expert hidden activations h: bf16 bits [T*k][d_ff] in sorted-slot
  * order (row p belongs to slot perm[p]).  -1 if the plan is NULL or

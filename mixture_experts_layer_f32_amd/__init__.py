@@ -69,6 +69,12 @@ def _load():
                               ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat), vp, vp, vp, vp,
                               vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
+    L.moe_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(moe_mat),
+                                      ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat), vp, vp,
+                                      vp, vp, vp, vp, vp]
+    L.moe_forward_noalloc.restype = ctypes.c_int
+    L.moe_noalloc_scratch_bytes.argtypes = []
+    L.moe_noalloc_scratch_bytes.restype = sz
     L.moe_workspace_h_offset.argtypes = [vp, i32]
     L.moe_workspace_h_offset.restype = i64
     L.moe_plan_path.argtypes = [vp, i32]
@@ -199,6 +205,23 @@ def moe_forward(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_ma
                          _ptr(workspace), int(workspace_bytes), stream or None)
     if st != MOE_OK:
         raise MoeError(st, "moe_forward", moe_plan_info(plan))
+
+
+def moe_forward_noalloc(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_mat,
+                        up: moe_mat, down: moe_mat, out, topk_ids=None, topk_w=None, counts=None,
+                        offsets=None, perm=None, stream=None) -> None:
+    """moe_forward without a workspace: the library's per-device scratch array
+    (moe_noalloc_scratch_bytes()) serves instead.  Raises MoeError."""
+    st = lib.moe_forward_noalloc(plan.handle, int(n_tokens), _ptr(x), _ptr(w_router),
+                                 _ptr(logit_bias), ctypes.byref(gate), ctypes.byref(up),
+                                 ctypes.byref(down), _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(counts), _ptr(offsets), _ptr(perm), _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_forward_noalloc", moe_plan_info(plan))
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return int(lib.moe_noalloc_scratch_bytes())
 
 
 def _stream(stream) -> Optional[int]:

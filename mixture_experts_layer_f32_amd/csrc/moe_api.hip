@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -33,6 +34,43 @@ struct Layout {
       tiles, n_tiles, h, y, xq, hq, qx, sx, qh, sh, total;
   int nchunk, max_tiles, n_slots;
 };
+
+}  // namespace
+
+// Scratch of moe_forward_noalloc: one array per device that runs the library,
+// held until the process ends and shared by every such call on that device.
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, taken once per device (with
+// that device current) when the first plan is made there.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES] = {};
+bool scratch_tried[MAX_DEVICES] = {};
+
+// Records the device address of `scratch` for device `dev` (the current
+// device); a failed lookup leaves it NULL, and the no-alloc entry point then
+// reports MOE_ERR_HIP.
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_tried[dev]) return;
+  scratch_tried[dev] = true;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess)
+    scratch_dev[dev] = ptr;
+  else
+    (void)hipGetLastError();
+}
+
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  return scratch_dev[dev];
+}
 
 }  // namespace
 
@@ -468,6 +506,7 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
 
+  scratch_setup(dev);
   moe_plan_s* p = new (std::nothrow) moe_plan_s();
   if (p == nullptr) return MOE_ERR_HIP;
   p->d = d;
@@ -841,6 +880,22 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                        size_t workspace_bytes, void* stream) {
   return forward_impl(p, T, x, w_router, logit_bias, gate, up, down, out, topk_ids, topk_w, counts,
                       offsets, perm, workspace, workspace_bytes, stream);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return MOE_NOALLOC_SCRATCH_BYTES; }
+
+moe_status moe_forward_noalloc(moe_plan_t p, int32_t T, const uint16_t* x, const float* w_router,
+                               const float* logit_bias, const moe_mat* gate, const moe_mat* up,
+                               const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, void* stream) {
+  if (p == nullptr) return MOE_ERR_NULL_ARG;
+  if (T < 0 || T > p->d.max_tokens) return MOE_ERR_BAD_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (layout(p, T).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_ptr(p->device);
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return forward_impl(p, T, x, w_router, logit_bias, gate, up, down, out, topk_ids, topk_w, counts,
+                      offsets, perm, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"
