@@ -147,8 +147,10 @@ typedef enum {
   /* fewest tokens for the MFMA decode tiles (default 2: one token takes the
    * matvec); >= 1 */
   MOE_OPT_DEC_MFMA_MIN_T = 1,
-  /* grouped-GEMM tile height in tokens: 128, 192 or 256; 0 = by the mean
-   * slots per expert (the default) */
+  /* grouped-GEMM tile shape, 10 * R + C: R wavefront rows (1 or 2) of C
+   * 32-token chunks each, so 32 R C tokens x 256 / R weight rows per matrix:
+   * 13, 14, 15 (96, 128, 160 tokens x 256 rows), 22, 23, 24 (128, 192, 256
+   * tokens x 128 rows); 0 = by the mean slots per expert (the default) */
   MOE_OPT_GROUPED_TILE = 2,
   /* grouped-GEMM tile height of activation-quantised plans: 64, 128 or 192;
    * 0 = by the mean slots per expert (the default) */

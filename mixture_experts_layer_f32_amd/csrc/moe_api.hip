@@ -84,7 +84,7 @@ struct moe_plan_s {
   int dec_kernel = 1;     // decode expert stage: 1 = MFMA tiles, 0 = wavefront matvec
   int dec_mfma_min_t = 2; // MFMA tiles from this many tokens (matvec below)
   int small_route_t = 0;  // top-k + permute in one workgroup up to this many tokens (<= 64), 0 = by shape
-  int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (22, 23, 24), 0 = by shape
+  int big_cfg = 0;        // gemm_big tile shape 10 * WGM + TM (13, 14, 15, 22, 23, 24), 0 = by shape
   int q8_tm = 0;          // gemm_q8 token chunks per wavefront (tile 64 * tm tokens), 0 = by shape
   std::string info;
   std::string last_error;
@@ -149,17 +149,25 @@ int dec_ks(int nkb) {
 }
 
 // Shape of gemm_big's tiles, as 10 * WGM + TM (tile height 32 * WGM * TM),
-// from the mean slots per expert: measured on every grouped workload,
-// 128-token tiles won up to 16 slots per expert (the fp4 layer at 16 and 1024
-// tokens; even with one slot, ahead of 32- and 64-token tiles of 256 rows),
-// 192-token tiles at 64 to 128 (the skewed OLMoE shape at 512 tokens, whose
-// hot experts hold about 150, and the d = 7168 layer at 4096) and 256-token
-// tiles at 256 (the skewed OLMoE shape at 2048).
+// from the mean slots per expert, as measured on every grouped workload:
+// 128-token tiles of two wavefront rows up to 32 slots per expert (the fp4
+// layer at 16 and 1024 tokens), 192-token tiles up to 96 (the skewed OLMoE
+// shape at 512 tokens, whose hot experts hold about 150), and for e4m3 the
+// 160-token tiles of one wavefront row up to 160 (the d = 7168 layer at 4096
+// tokens, 128 per expert: every wavefront decodes only its own weight rows
+// and the activations are shared by 256 rather than 128 weight rows per
+// matrix, and each refills its own weight rows before the stage barrier;
+// 2.06 against 2.26 ms for the gate/up stage), else 128-token tiles of one
+// row (the skewed OLMoE shape at 2048, 256 per expert: 176 against 189 us
+// for 256-token tiles of two rows).  fp4 keeps two rows (its 128-input stages
+// need them): 192-token tiles up to 160, else 256.
 int big_cfg(const moe_plan_s* p, int T) {
   if (p->big_cfg > 0) return p->big_cfg;
   const long long S = (long long)T * p->d.top_k;
   const long long mean = S / std::max(1LL, std::min<long long>(p->d.n_experts, S));
-  return mean <= 32 ? 22 : (mean <= 160 ? 23 : 24);
+  if (mean <= 32) return 22;
+  if (p->d.wfmt == MOE_W_E4M3_B128) return mean <= 96 ? 23 : (mean <= 160 ? 15 : 14);
+  return mean <= 160 ? 23 : 24;
 }
 int big_rows(int cfg) { return 32 * (cfg / 10) * (cfg % 10); }
 
@@ -283,6 +291,9 @@ void launch_big(const moe_plan_s* p, int max_tiles, int N, int K, int T, const u
 #define MOE_BIG(TM, WGM) \
   launch_big_cfg<FMT, GATEUP, TNW, TM, WGM>(max_tiles, N, K, T, act, W0, W1, tiles, n_tiles, tok_of, out, st)
   switch (big_cfg(p, T)) {
+    case 13: MOE_BIG(3, 1); break;
+    case 14: MOE_BIG(4, 1); break;
+    case 15: MOE_BIG(5, 1); break;
     case 22: MOE_BIG(2, 2); break;
     case 23: MOE_BIG(3, 2); break;
     default: MOE_BIG(4, 2); break;
@@ -552,8 +563,10 @@ moe_status moe_plan_set(moe_plan_t p, int32_t option, int32_t value) {
       p->dec_mfma_min_t = value;
       return MOE_OK;
     case MOE_OPT_GROUPED_TILE:
-      if (value != 0 && value != 128 && value != 192 && value != 256) return MOE_ERR_BAD_SHAPE;
-      p->big_cfg = value == 0 ? 0 : 20 + value / 64;
+      if (value != 0 && value != 13 && value != 14 && value != 15 && value != 22 && value != 23 &&
+          value != 24)
+        return MOE_ERR_BAD_SHAPE;
+      p->big_cfg = value;
       return MOE_OK;
     case MOE_OPT_Q8_TILE:
       if (value != 0 && value != 64 && value != 128 && value != 192) return MOE_ERR_BAD_SHAPE;

@@ -121,6 +121,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / WAVE; }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigma(g), the logistic by the hardware reciprocal (1 ulp; the
+// result is rounded to bf16 next, 2^16 times coarser).  For g below about -88
+// exp overflows, the reciprocal of infinity is 0 and silu is -0.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace moe

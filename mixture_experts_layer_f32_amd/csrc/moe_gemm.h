@@ -24,7 +24,9 @@
 
 namespace moe {
 
-constexpr int MAX_KBLK = 128;  // e4m3 grouped GEMM: K <= 128 * 128 (scales held in 2 VGPRs)
+// e4m3 grouped GEMM: K <= 127 * 128 (one lane per 128-deep block in 2 VGPRs,
+// and a lane for the block after the last one)
+constexpr int MAX_KBLK = 127;
 
 // Row index (within the 32x32 tile) of accumulator register v for this lane;
 // the column is lane % 32.
@@ -56,6 +58,12 @@ __device__ __forceinline__ void lds_dma_u16(const void* g, const uint32_t* l) {
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint32_t*)l);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(a) : "m0");
 }
+// The same from a uniform base (an SGPR pair) plus a 32-bit per-lane byte
+// offset, to the LDS byte address `lds`: the offsets stay in registers for the
+// whole K loop and only the base advances.
+__device__ __forceinline__ void lds_dma16_so(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
@@ -77,7 +85,9 @@ __device__ __forceinline__ void stage_barrier() {
 // number of active chunks of the wavefront, so its body has no branches
 // between chunks.  All tile bytes move by direct-to-LDS loads into NS slots
 // (as many as the 160 KB of LDS holds, at most 6; NS - 1 stages in flight),
-// one workgroup per CU.
+// one workgroup per CU.  With one wavefront row, each wavefront's weight rows
+// are its own: it reloads them right after its own compute of a stage, ahead
+// of the barrier that the shared activation rows need.
 // LDS layouts (64 banks of 4 bytes; a 16-byte read serves 16 lanes per
 // pass): activation row r (128 bytes per 64-input stage) holds its 16-byte
 // chunk c at slot c ^ ((r >> 1) & 7), or (256 bytes per 128-input stage) at
@@ -90,13 +100,15 @@ __device__ __forceinline__ void stage_barrier() {
 // e4m3 block scales without a second accumulator: a block scale s = 2^e * m
 // (1 <= |m| < 2) is split; 2^e goes into the fp8 -> bf16 conversion (exact:
 // an e4m3 value times a power of two is a bf16 value), and the running sum is
-// kept in units of the current block's m: at each block boundary
-// R <- R * (m_prev / m) in f32, then the block's MFMAs add into R, and the
-// output is R * m_last.  This is the f32 sum of the scaled block products up
-// to two f32 roundings per block (the ratio and the product; relative 2^-24
-// each).  The ratios and powers of two of all of a column's blocks are
-// computed once per workgroup, one block per lane.  fp4 scales are applied
-// exactly in the conversion, so there is no rescale.
+// kept in units of the current block's m: after a block's last MFMAs
+// R <- R * (m / m_next) in f32, then the next block's MFMAs add into R, and
+// the output is R * m_last.  This is the f32 sum of the scaled block products
+// up to two f32 roundings per block (the ratio and the product; relative
+// 2^-24 each).  The ratios and powers of two of all of a column's blocks are
+// computed once per workgroup, one block per lane.  The rescale of a token
+// chunk's accumulators follows that chunk's last MFMAs of the block, so it
+// overlaps the next chunk's MFMAs.  fp4 scales are applied exactly in the
+// conversion, so there is no rescale.
 template <int FMT, bool GATEUP, int TNW, int TM_, int WGM_>
 struct BigCfg {
   static constexpr bool FP4 = FMT != FMT_E4M3;
@@ -202,31 +214,36 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   const int nact = min(max((nch - wm + WGM - 1) / WGM, 0), TM);
 
   // activation loads of this lane: AL per stage, rows (AL w + i) * (64 / ACH)
-  // + lane / ACH mod BM (a short tile's rows are loaded twice, to the same
-  // place; rows past the tile repeat its last row, their outputs are not
-  // stored), LDS slot lane % ACH of the row holding chunk slot ^ aswz(row):
+  // + lane / ACH (rows past the tile repeat its last row, their outputs are
+  // not stored; a load whose first row is past the tile is not issued), LDS
+  // slot lane % ACH of the row holding chunk slot ^ aswz(row):
   // 128-byte rows (8 chunks) swizzle by (row >> 1) & 7, 256-byte rows (16
   // chunks) by row & 15, so each 16-lane pass of a fragment read touches 16
   // bank groups
   auto aswz = [](int r) { return C::ACH == 8 ? ((r >> 1) & 7) : (r & 15); };
   const uint16_t* asrc[AL];
   int achunk[AL];
+  uint32_t aoff[AL];  // e4m3: byte offset of the lane's chunk from act + 2 k0
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = ((AL * w + i) * (64 / C::ACH) + lane / C::ACH) % BM;
+    const int r = min((AL * w + i) * (64 / C::ACH) + lane / C::ACH, BM - 1);
     const int rr = min(r, rows - 1);
     const size_t src = GATEUP ? (size_t)min((uint32_t)tok_of[p_start + rr], (uint32_t)(T - 1))
                               : (size_t)(p_start + rr);
     asrc[i] = act + src * K;
     achunk[i] = (lane % C::ACH) ^ aswz(r);
+    aoff[i] = (uint32_t)(src * K * 2 + 16 * achunk[i]);
   }
+  // LDS byte addresses of the two rings
+  const uint32_t lds_a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)&sA[0][0];
+  const uint32_t lds_w = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)&sW[0][0];
   // activation loads of this wavefront that hold rows of the tile (its first
   // n_a; a load of 8 rows all past `rows` is skipped: the MFMAs of rows past
   // `rows` only reach outputs that are not stored, so their LDS bytes may be
   // stale)
   int n_a = 0;
 #pragma unroll
-  for (int i = 0; i < AL; ++i) n_a += (((AL * w + i) * (64 / C::ACH)) % BM) < rows ? 1 : 0;
+  for (int i = 0; i < AL; ++i) n_a += (AL * w + i) * (64 / C::ACH) < min(rows, BM) ? 1 : 0;
   // the weight tiles this wavefront loads: WGM = 2: tile wm of its column
   // (the other wavefront of the column loads the other); WGM = 1: both.  Tile
   // t is matrix t for gate/up, rows 32 t .. of the column for down; rows are
@@ -241,6 +258,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   const int64_t rbytes = FP4 ? (int64_t)K / 2 : (int64_t)K;
   const int sgroups = FMT == FMT_NVFP4 ? K >> 4 : K >> 5;
   int tls[TPW];
+  const uint8_t* wbase[TPW];  // e4m3: the matrix of the tile (uniform)
+  uint32_t woff[TPW][2];      // e4m3: byte offset of the lane's 16 bytes from wbase + k0
   const uint8_t* wsrc[TPW][2];
   const uint8_t* wsrc16[TPW];  // fp4 with 128-input stages: the rows of load 1 (16 further)
   int wchunk[2] = {0, 0};
@@ -251,11 +270,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     const int ml = GATEUP ? tl : 0, jl = GATEUP ? 0 : tl;
     const DMat& WL = ml == 0 ? W0 : W1;
     if constexpr (!FP4) {
+      wbase[u] = WL.q + e * WL.qs;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int tr = 16 * j + (lane >> 2);
-        wsrc[u][j] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes +
-                     16 * ((lane & 3) ^ ((tr >> 2) & 3));
+        woff[u][j] = (uint32_t)((int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes +
+                                16 * ((lane & 3) ^ ((tr >> 2) & 3)));
+        wsrc[u][j] = nullptr;
       }
       wsrc16[u] = nullptr;
     } else if constexpr (CPL == 1) {
@@ -276,8 +297,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   }
   // e4m3: for k-block kb = lane + 64 q of this column's 128-row block (lane
   // kb % 64 of register kb / 64), the power of two of its scale and the ratio
-  // of the previous block's mantissa to its own (1 for block 0); m_last, the
-  // last block's mantissa, scales the output
+  // of the previous block's mantissa to its own (1 for block 0 and for the
+  // block after the last); m_last, the last block's mantissa, scales the
+  // output
   float pw[NMAT][2], rt[NMAT][2], mlast[NMAT];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
@@ -304,18 +326,37 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   const int nk = (K + BK - 1) / BK;
   // stage kk's loads into slot `slot` (addresses clamped into the rows at a
   // k-tail; those inputs are zeroed at decode)
+  // e4m3 (K a multiple of 128: no chunk of a stage runs past the row): the
+  // activation and the weight loads of stage kk into slot `slot`
+  auto issue_act = [&](int kk, int slot) {
+    const uint8_t* abase = reinterpret_cast<const uint8_t*>(act) + 2 * (size_t)(kk * BK);
+#pragma unroll
+    for (int i = 0; i < AL; ++i)
+      if (i < n_a) lds_dma16_so(abase, aoff[i], lds_a + 16 * (slot * C::A_V4 + (AL * w + i) * 64));
+  };
+  auto issue_wt = [&](int kk, int slot) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        lds_dma16_so(wbase[u] + kk * BK, woff[u][j],
+                     lds_w + 16 * (slot * (C::W_V4 + C::S_V4) + ((wn * NW + tls[u]) * 2 + j) * 64));
+  };
   auto issue = [&](int kk, int slot) {
     const int k0 = kk * BK;
+    if constexpr (!FP4) {
+      issue_act(kk, slot);
+      issue_wt(kk, slot);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < AL; ++i)
       if (i < n_a)
-        lds_dma16(asrc[i] + min(k0 + 8 * achunk[i], K - 8), &sA[slot][((AL * w + i) * 64) % C::A_V4]);
+        lds_dma16(asrc[i] + min(k0 + 8 * achunk[i], K - 8), &sA[slot][(AL * w + i) * 64]);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tl = tls[u];
       if constexpr (!FP4) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) lds_dma16(wsrc[u][j] + k0, &sW[slot][((wn * NW + tl) * 2 + j) * 64]);
       } else {
         const int tile = wn * NW + tl;
         if constexpr (CPL == 1) {
@@ -344,6 +385,23 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   // that slot, compute stage ks.  Past the last issue the waits drain all.
   // loads per lane and stage of this wavefront: LD minus its skipped activation loads
   constexpr int LDW = C::LOADS - AL;
+  // One wavefront row (e4m3): a wavefront's weight rows are its own, so it
+  // refills its weight region of a slot right after its own compute of the
+  // stage there (weights of stage ks + NS), before the next barrier; the
+  // activations, shared by all wavefronts, follow the barrier as before.
+  // Per wavefront the issue order is then ... A(ks), W(ks + 1), A(ks + 1),
+  // ..., W(ks + NS - 1) when stage ks is waited for: all but the last
+  // LDW + (NS - 2) (LDW + n_a) loads must be done.
+  constexpr bool EARLYW = !FP4 && WGM == 1;
+  auto wait_early = [&]() {
+    switch (n_a) {
+      case 0: wait_vm<LDW + (NS - 2) * LDW>(); break;
+      case 1: wait_vm<LDW + (NS - 2) * (LDW + 1)>(); break;
+      case 2: wait_vm<LDW + (NS - 2) * (LDW + (AL >= 2 ? 2 : 1))>(); break;
+      case 3: wait_vm<LDW + (NS - 2) * (LDW + (AL >= 3 ? 3 : 1))>(); break;
+      default: wait_vm<LDW + (NS - 2) * (LDW + AL)>(); break;
+    }
+  };
   auto wait_stage = [&]() {  // all but the NS - 2 most recent stages' loads done
     switch (n_a) {
       case 0: wait_vm<(NS - 2) * LDW>(); break;
@@ -369,18 +427,24 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     for (int m = 0; m < NMAT; ++m) p2[m] = FP4 ? 1.0f : lane_of(pw[m], 0);
 
     // stage ks from LDS slot `slot`; NEWBLK (e4m3): the stage opens a 128-deep
-    // scale block (at block 0 the rescale multiplies zeros by 1)
+    // scale block (its power of two goes into the conversions); otherwise it
+    // closes one, and each chunk's accumulators are rescaled to the next
+    // block's mantissa after the chunk's MFMAs (the block after the last has
+    // ratio 1)
     auto compute = [&](int ks, int slot, auto newblk_c) {
       constexpr bool NEWBLK = decltype(newblk_c)::value;
+      constexpr bool ENDBLK = !FP4 && !NEWBLK;
       if constexpr (NA > 0) {
         float ratio[NMAT];
         if constexpr (NEWBLK) {
           const int kb = ks >> 1;
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) {
-            ratio[m] = lane_of(rt[m], kb);
-            p2[m] = lane_of(pw[m], kb);
-          }
+          for (int m = 0; m < NMAT; ++m) p2[m] = lane_of(pw[m], kb);
+        }
+        if constexpr (ENDBLK) {
+          const int kb = (ks >> 1) + 1;
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) ratio[m] = lane_of(rt[m], kb);
         }
         const u32x4* a_s = sA[slot];
         const u32x4* w_s = sW[slot];
@@ -420,20 +484,20 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
         }
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-          if constexpr (NEWBLK) {
-#pragma unroll
-            for (int t = 0; t < NW; ++t) {
-              const float r = ratio[GATEUP ? t : 0];
-#pragma unroll
-              for (int v = 0; v < 16; ++v) R[i][t][v] *= r;
-            }
-          }
           const int mrow = 32 * (WGM * i + wm) + r32;
 #pragma unroll
           for (int s = 0; s < NSTEP; ++s) {
             const bf16x8 a = __builtin_bit_cast(bf16x8, a_s[mrow * C::ACH + ((NSTEP * h + s) ^ aswz(mrow))]);
 #pragma unroll
             for (int t = 0; t < NW; ++t) R[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[t][s], R[i][t], 0, 0, 0);
+          }
+          if constexpr (ENDBLK) {
+#pragma unroll
+            for (int t = 0; t < NW; ++t) {
+              const float r = ratio[GATEUP ? t : 0];
+#pragma unroll
+              for (int v = 0; v < 16; ++v) R[i][t][v] *= r;
+            }
           }
         }
       }
@@ -444,6 +508,22 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
         constexpr int j = decltype(j_c)::value;
         const int ks = ks0 + j;
         if (ks >= nk) return;
+        if constexpr (EARLYW) {
+          if (ks + NS - 1 < nk)
+            wait_early();
+          else
+            wait_vm<0>();
+          stage_barrier();
+          if (ks + NS - 1 < nk) issue_act(ks + NS - 1, (j + NS - 1) % NS);
+          compute(ks, j % NS, std::integral_constant<bool, !FP4 && j % 2 == 0>{});
+          if (ks + NS < nk) {
+            // this wavefront's reads of the slot have returned before the
+            // slot's weight region is written again
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_wt(ks + NS, j % NS);
+          }
+          return;
+        }
         if (ks + NS - 2 < nk)
           wait_stage();
         else
@@ -477,6 +557,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < nk) issue(p, p);
+  if constexpr (EARLYW)
+    if (NS - 1 < nk) issue_wt(NS - 1, NS - 1);
   dispatch_count<TM>(nact, run);
 }
 

@@ -48,7 +48,7 @@ def check_all(g, ref):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("tile", [128, 192, 256])
+@pytest.mark.parametrize("tile", [13, 14, 15, 22, 23, 24])
 def test_grouped_tiles(fmt, tile):
     """Every tile height of the grouped kernel on a batch of a few tokens per
     expert (partial tiles, chunks past the rows)."""
@@ -79,12 +79,12 @@ def test_decode_mfma_one_token(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("tile", [128, 192, 256])
+@pytest.mark.parametrize("tile", [13, 14, 15, 22, 23, 24])
 def test_grouped_tiles_one_expert_many_tiles(fmt, tile):
-    """A large bias on expert 1 sends all 150 tokens there: at 128-token tiles
-    that expert spans two tiles (the last one partial), at 192 and 256 one
-    partial tile; the chunks of a tile are shared out between the wavefront
-    rows, so every count of active chunks per wavefront occurs."""
+    """A large bias on expert 1 sends all 150 tokens there: at 96- and
+    128-token tiles that expert spans two tiles (the last one partial), at 160
+    to 256 one partial tile; the chunks of a tile are shared out between the
+    wavefront rows, so many counts of active chunks per wavefront occur."""
     wl, layer, W = get(fmt)
     T = 150
     batch = synth.make_batch(wl, layer, T)
@@ -97,18 +97,21 @@ def test_grouped_tiles_one_expert_many_tiles(fmt, tile):
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "nvfp4"])
-@pytest.mark.parametrize("T", [33, 65, 97, 129, 161, 193, 225, 256])
-def test_grouped_chunk_counts(fmt, T):
-    """One expert holding T slots in one 256-token tile: 2..8 active 32-row
-    chunks, so each wavefront row takes every count from 1 to 4 (and odd
-    splits, where the two rows differ by one chunk)."""
+@pytest.mark.parametrize("T,tile", [(33, 24), (65, 24), (97, 24), (129, 24), (161, 24), (193, 24),
+                                    (225, 24), (256, 24), (1, 15), (40, 15), (70, 15), (100, 15),
+                                    (130, 15), (160, 15)])
+def test_grouped_chunk_counts(fmt, T, tile):
+    """One expert holding T slots in one tile: at 256-token tiles 2..8 active
+    32-row chunks, so each wavefront row takes every count from 1 to 4 (and
+    odd splits, where the two rows differ by one chunk); at 160-token tiles of
+    one wavefront row every count from 1 to 5."""
     wl, layer, W = get(fmt)
     batch = synth.make_batch(wl, layer, T)
     bias = np.zeros((T, wl.E), np.float32)
     bias[:, 1] = 100.0
     batch = synth.Batch(batch.x, bias)
     ref = oracle_run(wl, layer, batch)
-    check_all(run_with_options({moe.MOE_OPT_GROUPED_TILE: 256}, wl, W, batch, GROUPED), ref)
+    check_all(run_with_options({moe.MOE_OPT_GROUPED_TILE: tile}, wl, W, batch, GROUPED), ref)
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
