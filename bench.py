@@ -3,20 +3,25 @@
 
 One step = one forward of the whole layer (router, top-k, permute, gate/up +
 SwiGLU, down, combine) over one batch of T synthetic tokens whose inputs are
-already resident in HBM.  Default workload: the OLMoE-1B-7B-shaped decode
-layer (d=2048, f=1024, 64 experts, top-8, e4m3 weights with 128x128 f32 block
-scales, no renormalisation) at T=8 tokens.
+already resident in HBM.  The headline workload is the largest single-GPU
+layer: d=7168, f=2048, 256 experts, top-8 renormalised, e4m3 weights with
+128x128 f32 block scales (11.3 GB), at T=4096 tokens.  The same run measures
+every (layer, T) point of the five workloads (`per_config`).
 
-Prints one JSON line with the throughput, the roofline of the dominant kernel
-(its duration measured with HIP events recorded on the launch stream by the
-library's own timing hooks) and the CPU oracle's throughput on a bounded
-sample of the same workload on this host.
+Per point: tokens/s from the wall clock over the timed steps (eager launches),
+the per-step device span (HIP events before and after each step on the launch
+stream; median and min), a HIP-graph replay of the captured forward (launch
+overhead removed), an A/A rerun of the timed loop, the dominant kernel's
+duration (HIP events around that stage only, recorded by the library on the
+launch stream) with its roofline fraction, and the CPU oracle on a bounded
+sample of the same batch on this host.
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -29,6 +34,19 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the activation-quantised variant)
 KERNEL_SOURCES = ["moe_common.h", "moe_route.h", "moe_decode.h", "moe_gemm.h", "moe_block.h", "moe_q8.h",
                   "moe_api.hip"]
+
+# The five workloads at the token counts they are defined with; the headline
+# is the largest layer at its largest batch.
+POINTS = [("tiny", 4), ("olmoe-decode", 1), ("olmoe-decode", 8), ("olmoe-prefill-skewed", 512),
+          ("olmoe-prefill-skewed", 2048), ("large-e4m3", 1), ("large-e4m3", 64),
+          ("large-e4m3", 4096), ("fp4-e2m1", 1), ("fp4-e2m1", 16), ("fp4-e2m1", 1024)]
+HEADLINE = ("large-e4m3", 4096)
+# tokens of each batch the CPU oracle evaluates (its routing covers the whole
+# batch; the expert step and the combine only these tokens)
+ORACLE_TOKENS = {("tiny", 4): 4, ("olmoe-decode", 1): 1, ("olmoe-decode", 8): 8,
+                 ("olmoe-prefill-skewed", 512): 4, ("olmoe-prefill-skewed", 2048): 4,
+                 ("large-e4m3", 1): 1, ("large-e4m3", 64): 2, ("large-e4m3", 4096): 8,
+                 ("fp4-e2m1", 1): 1, ("fp4-e2m1", 16): 2, ("fp4-e2m1", 1024): 4}
 
 
 def kernel_source_hash() -> str:
@@ -54,6 +72,24 @@ def expert_stage_bytes(wl, U, T):
     gateup = U * gu + T * d * 2 + S * f * 2          # weights, x rows, h (bf16) out
     down = U * dn + S * f * 2 + S * d * 4            # weights, h in, y (f32) out
     return gateup, down
+
+
+def roofline_of(wl, U, T, stage, us, act_quant=False, grouped=True):
+    """Roofline of one expert stage from its duration: HBM or MFMA by the
+    stage's arithmetic intensity against the balance point of its peak."""
+    gu_bytes, dn_bytes = expert_stage_bytes(wl, U, T)
+    S = T * wl.k
+    flops = {"gateup": 4.0 * S * wl.d * wl.f, "down": 2.0 * S * wl.d * wl.f}[stage]
+    nbytes = {"gateup": gu_bytes, "down": dn_bytes}[stage]
+    dur_s = us * 1e-6
+    peak_mfma = PEAK_FP8_TFLOPS if act_quant and grouped else PEAK_BF16_TFLOPS
+    if flops / nbytes > peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved, peak, unit, bound = flops / dur_s / 1e12, peak_mfma, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = nbytes / dur_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "kernel": stage, "kernel_us": round(us, 3),
+            "algorithmic_bytes": int(nbytes), "algorithmic_flops": int(flops)}
 
 
 COPY_BYTES = 512 * 2 ** 20
@@ -117,16 +153,244 @@ def write_traffic(args):
     print(json.dumps(out["entries"][key]))
 
 
-def bench_block(args, wl, T, layer, xs, Ws, copies, run, outs, stream, moe, np, torch, synth,
-                DeviceWeights, Runner, to_dev):
+def host_cpu():
+    """CPU model of this host and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def log(msg):
+    print(f"# {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ one layer on the device
+
+
+class DeviceLayer:
+    """A workload's layer generated on the host, uploaded, and copied until at
+    least `copy_gib` GiB of weights are cycled (so consecutive steps do not
+    find their experts in the 256 MB Infinity Cache)."""
+
+    def __init__(self, wl, copy_gib):
+        import torch
+        import synth
+        from mixture_experts_layer_f32_amd.device import DeviceWeights
+        t0 = time.time()
+        self.wl = wl
+        self.layer = synth.make_layer(wl)
+        W0 = DeviceWeights.upload(self.layer.w_router, self.layer.gate.q, self.layer.gate.s,
+                                  self.layer.up.q, self.layer.up.s, self.layer.down.q,
+                                  self.layer.down.s)
+        nbytes = W0.nbytes()
+        free, _ = torch.cuda.mem_get_info()
+        self.copies = max(1, min(math.ceil(copy_gib * 2 ** 30 / nbytes),
+                                 int(0.5 * free // nbytes) + 1, 16))
+        self.Ws = [W0] + [DeviceWeights(*(t.clone() for t in (W0.w_router, W0.gate_q, W0.gate_s,
+                                                               W0.up_q, W0.up_s, W0.down_q,
+                                                               W0.down_s)))
+                          for _ in range(self.copies - 1)]
+        log(f"{wl.name}: layer generated and uploaded ({nbytes / 1e9:.2f} GB x {self.copies}) "
+            f"in {time.time() - t0:.1f}s")
+
+
+def oracle_sample(wl, layer, batch, n_tok, act_quant, workers):
+    """The CPU oracle on the first n_tok tokens of the batch (routing over the
+    whole batch): (tokens/s, seconds, tokens)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    M = lambda m: oracle.Mat(m.q, m.s, m.K)  # noqa: E731
+    toks = list(range(min(n_tok, batch.x.shape[0])))
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        oracle.moe_forward(batch.x, layer.w_router, batch.bias, M(layer.gate), M(layer.up),
+                           M(layer.down), wl.k, wl.renorm, wl.fmt, tokens=toks,
+                           act_quant=act_quant, workers=workers)
+        el = time.perf_counter() - t0
+    return len(toks) / el, el, len(toks)
+
+
+def measure(dl, T, args, act_quant=False, path_opt="auto", oracle_tokens=0, oracle_1thread=False,
+            steps=None):
+    """All timings of one (layer, T) point; returns a dict.  `steps` timed
+    steps (default: --steps; for the other points of the default run enough
+    to cover about 0.2 s, at least --steps and at most 1000)."""
+    import numpy as np
+    import torch
+    import synth
+    import mixture_experts_layer_f32_amd as moe
+    from mixture_experts_layer_f32_amd.device import Runner, to_dev
+    wl, layer, Ws, copies = dl.wl, dl.layer, dl.Ws, dl.copies
+    nb = args.batches if args.batches else (16 if T <= 64 else 4)
+    t0 = time.time()
+    batches = [synth.make_batch(wl, layer, T, batch_index=i) for i in range(nb)]
+    xs = [to_dev(b.x) for b in batches]
+    biases = [to_dev(b.bias) if b.bias is not None else None for b in batches]
+    path = {"auto": moe.MOE_PATH_AUTO, "decode": moe.MOE_PATH_DECODE,
+            "grouped": moe.MOE_PATH_GROUPED}[path_opt]
+    opts = {moe.MOE_OPT_GROUPED_TILE: args.tile} if args.tile else None
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path,
+                 act_fmt=moe.MOE_ACT_E4M3_G128 if act_quant else moe.MOE_ACT_BF16, options=opts)
+    outs = run.outputs(T)
+    used_path = "decode" if moe.moe_plan_path(run.plan, T) == moe.MOE_PATH_DECODE else "grouped"
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        run.forward(Ws[i % copies], xs[i % nb], biases[i % nb], outs, stream)
+
+    # distinct experts per batch (U) from the GPU's own counts
+    Us = []
+    for i in range(nb):
+        step(i)
+        torch.cuda.synchronize()
+        Us.append(int((outs["counts"] > 0).sum().item()))
+    U = float(np.mean(Us))
+    warm = max(args.warmup, 1)
+    torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t_w) / warm
+    if steps is None:
+        steps = args.steps
+    elif steps < 0:
+        steps = int(min(1000, max(args.steps, 0.2 / max(per_step, 1e-6))))
+    n = steps
+
+    # timed eager loop (twice: A/A): wall clock only, nothing recorded in between
+    def timed_loop():
+        torch.cuda.synchronize()
+        t_a = time.perf_counter()
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t_a) * 1e3 / n
+
+    wall_a = timed_loop()
+    wall_b = timed_loop()
+    # device span of each step: HIP events before and after it on the stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for i in range(n):
+        ev[2 * i].record(stream)
+        step(i)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    spans = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
+
+    # dominant expert stage: all stages once to find it, then that stage alone
+    moe.moe_timing_enable(run.plan, moe.STAGES, max_forwards=n)
+    for i in range(n):
+        step(i)
+    stage_ms, n_fw = moe.moe_timing_collect(run.plan)
+    moe.moe_timing_disable(run.plan)
+    stages_us = {k: 1e3 * v / n_fw for k, v in stage_ms.items()}
+    dom = max(("gateup", "down"), key=lambda s: stages_us[s])
+    moe.moe_timing_enable(run.plan, (dom,), max_forwards=n)
+    for i in range(n):
+        step(i)
+    dom_ms, n_fw = moe.moe_timing_collect(run.plan)
+    moe.moe_timing_disable(run.plan)
+    dom_us = 1e3 * dom_ms[dom] / n_fw
+
+    # HIP-graph replay: one captured forward per (weight copy, x batch) pair,
+    # replayed round-robin between two events
+    n_g = max(1, min(copies, nb, 4))
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run.forward(Ws[0], xs[0], biases[0], outs, side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for gi in range(n_g):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run.forward(Ws[gi], xs[gi], biases[gi], outs, torch.cuda.current_stream())
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for gi in range(n_g):
+        graphs[gi].replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        graphs[i % n_g].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / n
+    del graphs
+
+    roof = roofline_of(wl, U, T, dom, dom_us, act_quant, used_path == "grouped")
+    res = {
+        "workload": f"{wl.name}: d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.fmt} "
+                    f"renorm={int(wl.renorm)}, T={T}",
+        "name": wl.name, "T": T, "path": used_path, "tokens_per_s": round(T / (wall_a * 1e-3), 2),
+        "ms_per_step": round(wall_a, 5), "steps": n, "warmup": warm,
+        "aa_rerun": {"tokens_per_s": round(T / (wall_b * 1e-3), 2), "ms_per_step": round(wall_b, 5),
+                     "ratio": round(wall_b / wall_a, 4)},
+        "device_span_ms": {"median": round(statistics.median(spans), 5),
+                           "min": round(min(spans), 5)},
+        "graph_replay": {"ms_per_step": round(graph_ms, 5),
+                         "tokens_per_s": round(T / (graph_ms * 1e-3), 2), "graphs": n_g},
+        "stages_us": {k: round(v, 3) for k, v in stages_us.items()},
+        "distinct_experts_per_step": U, "weight_copies_rotated": copies, "x_batches_rotated": nb,
+        "roofline": roof,
+    }
+    if oracle_tokens:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        tps, el, n = oracle_sample(wl, layer, batches[0], oracle_tokens, act_quant, workers)
+        res["oracle"] = {"tokens_per_s": round(tps, 3), "seconds": round(el, 2), "tokens": n,
+                         "threads": workers}
+        if oracle_1thread:
+            tps1, el1, _ = oracle_sample(wl, layer, batches[0], oracle_tokens, act_quant, 1)
+            res["oracle"]["tokens_per_s_1thread"] = round(tps1, 3)
+            res["oracle"]["seconds_1thread"] = round(el1, 2)
+    log(f"{wl.name} T={T} ({used_path}): {res['tokens_per_s']:.0f} tokens/s, "
+        f"{wall_a * 1e3:.1f} us/step (A/A {wall_b * 1e3:.1f}), graph {graph_ms * 1e3:.1f} us, "
+        f"{dom} {dom_us:.1f} us = {roof['frac']:.3f} {roof['bound']} ({time.time() - t0:.1f}s)")
+    return res
+
+
+def traffic_for(args, wl, T, path, dom, act_quant):
+    """HBM bytes per launch of the dominant kernel from profiles/traffic.json,
+    if measured on the current kernel sources; else None."""
+    key = f"{wl.name}/T={T}/{path}{'-q8' if act_quant else ''}/{dom}"
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            ent = json.load(f).get("entries", {}).get(key)
+        if ent and ent.get("kernel_source") == kernel_source_hash():
+            return ent["bytes_per_launch"]
+    return None
+
+
+def bench_block(args, wl, T, dl):
     """One step = RMSNorm of the bf16 hidden rows -> the routed layer on them ->
     the dense branch (a one-expert top-1 plan, weight exactly 1) -> the add of
-    both into the residual stream.  Each piece timed with events on `stream`."""
+    both into the residual stream.  Each piece timed with events on the stream."""
+    import numpy as np
+    import torch
+    import synth
+    import mixture_experts_layer_f32_amd as moe
+    from mixture_experts_layer_f32_amd.device import DeviceWeights, Runner, to_dev
     d = wl.d
+    layer, Ws, copies = dl.layer, dl.Ws, dl.copies
+    batches = [synth.make_batch(wl, layer, T, batch_index=i) for i in range(4)]
+    xs = [to_dev(b.x) for b in batches]
+    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T)
+    outs = run.outputs(T)
+    stream = torch.cuda.current_stream()
     dwl = synth.Workload(wl.name + "-dense", d, wl.f, 1, 1, wl.fmt, True, (), False, wl.seed + 100)
-    dl = synth.make_layer(dwl)
-    WD = DeviceWeights.upload(dl.w_router, dl.gate.q, dl.gate.s, dl.up.q, dl.up.s, dl.down.q,
-                              dl.down.s)
+    dlay = synth.make_layer(dwl)
+    WD = DeviceWeights.upload(dlay.w_router, dlay.gate.q, dlay.gate.s, dlay.up.q, dlay.up.s,
+                              dlay.down.q, dlay.down.s)
     WDs = [WD] + [DeviceWeights(*(t.clone() for t in (WD.w_router, WD.gate_q, WD.gate_s, WD.up_q,
                                                       WD.up_s, WD.down_q, WD.down_s)))
                   for _ in range(copies - 1)]
@@ -201,17 +465,18 @@ def bench_block(args, wl, T, layer, xs, Ws, copies, run, outs, stream, moe, np, 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="olmoe-decode")
-    ap.add_argument("--tokens", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="measure this workload only (default: the headline plus every point)")
+    ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--path", choices=["auto", "decode", "grouped"], default="auto")
-    ap.add_argument("--batches", type=int, default=16, help="distinct x batches rotated")
+    ap.add_argument("--batches", type=int, default=0,
+                    help="distinct x batches rotated (0: 16 up to 64 tokens, else 4)")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="rotate weight copies until this many GiB are cycled (defeats the 256 MB "
                          "Infinity Cache)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="bounded CPU-oracle sample (0 disables)")
+    ap.add_argument("--no-oracle", action="store_true", help="skip the CPU oracle samples")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 --pmc")
     ap.add_argument("--copy-probe", action="store_true",
@@ -226,8 +491,10 @@ def main():
     ap.add_argument("--act-quant", action="store_true",
                     help="the activation-quantised variant: x and h as e4m3 per 128-input group "
                          "(UE8M0 scales), block-scaled fp8 MFMA; opt-in, it changes results")
-    ap.add_argument("--traffic-key", default="olmoe-decode/T=8/decode/gateup")
-    ap.add_argument("--traffic-kernel", default="dec_mfma<0, true")
+    ap.add_argument("--tile", type=int, default=0,
+                    help="grouped-GEMM tile shape code (MOE_OPT_GROUPED_TILE; 0: by shape)")
+    ap.add_argument("--traffic-key", default="large-e4m3/T=4096/grouped/gateup")
+    ap.add_argument("--traffic-kernel", default="gemm_big<0, true")
     args = ap.parse_args()
 
     if args.write_traffic:
@@ -241,177 +508,102 @@ def main():
               "build runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
     import synth
-    import mixture_experts_layer_f32_amd as moe
-    from mixture_experts_layer_f32_amd.device import DeviceWeights, Runner, to_dev
+    import mixture_experts_layer_f32_amd  # noqa: F401  (fails loudly without libmoe.so)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
-    T = args.tokens
-    t_gen = time.time()
-    layer = synth.make_layer(wl)
-    batches = [synth.make_batch(wl, layer, T, batch_index=i) for i in range(args.batches)]
-    print(f"# generated {wl.name} layer + {len(batches)} batches of T={T} in "
-          f"{time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    cpu_model, cpu_cores = host_cpu()
 
-    W0 = DeviceWeights.upload(layer.w_router, layer.gate.q, layer.gate.s, layer.up.q, layer.up.s,
-                              layer.down.q, layer.down.s)
-    layer_bytes = W0.nbytes()
-    free, _ = torch.cuda.mem_get_info()
-    copies = max(1, min(math.ceil(args.copy_gib * 2 ** 30 / layer_bytes),
-                        int(0.5 * free // layer_bytes) + 1, 16))
-    Ws = [W0] + [DeviceWeights(*(t.clone() for t in (W0.w_router, W0.gate_q, W0.gate_s, W0.up_q,
-                                                      W0.up_s, W0.down_q, W0.down_s)))
-                 for _ in range(copies - 1)]
-    xs = [to_dev(b.x) for b in batches]
-    biases = [to_dev(b.bias) if b.bias is not None else None for b in batches]
-    path = {"auto": moe.MOE_PATH_AUTO, "decode": moe.MOE_PATH_DECODE,
-            "grouped": moe.MOE_PATH_GROUPED}[args.path]
-    act_fmt = moe.MOE_ACT_E4M3_G128 if args.act_quant else moe.MOE_ACT_BF16
-    run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, path, act_fmt=act_fmt)
-    outs = run.outputs(T)
-    used_path = "decode" if moe.moe_plan_path(run.plan, T) == moe.MOE_PATH_DECODE else "grouped"
-    # expert-stage arithmetic (the router is f32 throughout): bf16 products
-    # into f32, by MFMA except in the decode matvec, which the plan picks for
-    # one token (or always, under MOE_DEC_KERNEL=0)
-    mfma = used_path == "grouped" or (os.environ.get("MOE_DEC_KERNEL", "1") != "0"
-                                      and T >= int(os.environ.get("MOE_DEC_MFMA_MIN_T", "2")))
-    dtype = "bf16-mfma/f32-acc" if mfma else "bf16-dot2/f32-acc"
-    if args.act_quant and used_path == "grouped":
-        dtype = "e4m3xe4m3-mfma/f32-acc" if wl.fmt == "e4m3" else "e4m3xe2m1-mfma/f32-acc"
-    elif args.act_quant:  # the decode kernels on the quantised activations as bf16
-        dtype = "e4m3-act-dequantised/" + dtype
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        run.forward(Ws[i % copies], xs[i % len(xs)], biases[i % len(xs)], outs, stream)
-
-    if args.block:
-        block_line = bench_block(args, wl, T, layer, xs, Ws, copies, run, outs, stream, moe, np,
-                                 torch, synth, DeviceWeights, Runner, to_dev)
-        print(json.dumps(block_line), flush=True)
-        return
-
-    # distinct experts per batch (U) from the GPU's own counts
-    Us = []
-    for i in range(len(xs)):
-        step(i)
-        torch.cuda.synchronize()
-        Us.append(int((outs["counts"] > 0).sum().item()))
-    U = float(np.mean(Us))
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    tokens_per_s = T * args.steps / (t1 - t0)
-
-    # live per-stage durations: HIP events recorded by the library on `stream`
-    moe.moe_timing_enable(run.plan, moe.STAGES, max_forwards=args.steps)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    stage_ms, n_fw = moe.moe_timing_collect(run.plan)
-    t3 = time.perf_counter()
-    moe.moe_timing_disable(run.plan)
-    stage_avg_us = {k: 1e3 * v / n_fw for k, v in stage_ms.items()}
-    timed_ms_per_step = (t3 - t2) * 1e3 / args.steps
-
-    gu_bytes, dn_bytes = expert_stage_bytes(wl, U, T)
-    S = T * wl.k
-    flops = {"gateup": 4.0 * S * wl.d * wl.f, "down": 2.0 * S * wl.d * wl.f}
-    nbytes = {"gateup": gu_bytes, "down": dn_bytes}
-    dom = max(("gateup", "down"), key=lambda s: stage_avg_us[s])
-    dur_s = stage_avg_us[dom] * 1e-6
-    intensity = flops[dom] / nbytes[dom]
-    peak_mfma = PEAK_FP8_TFLOPS if args.act_quant and used_path == "grouped" else PEAK_BF16_TFLOPS
-    if intensity > peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved, peak, unit, bound = flops[dom] / dur_s / 1e12, peak_mfma, "TFLOP/s", "mfma"
+    if args.workload is not None:
+        wl = synth.WORKLOADS[args.workload]
+        T = args.tokens if args.tokens is not None else wl.batches[-1]
+        points, head = [(wl.name, T)], (wl.name, T)
     else:
-        achieved, peak, unit, bound = nbytes[dom] / dur_s / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+        points, head = list(POINTS), HEADLINE
+    by_wl = {}
+    for name, T in points:
+        by_wl.setdefault(name, []).append(T)
+    results = {}
+    for name, Ts in by_wl.items():
+        dl = DeviceLayer(synth.WORKLOADS[name], args.copy_gib)
+        if args.block:
+            print(json.dumps(bench_block(args, dl.wl, Ts[-1], dl)), flush=True)
+            return
+        for T in Ts:
+            n_or = 0 if args.no_oracle else ORACLE_TOKENS.get((name, T), 4)
+            steps = None
+            if (name, T) != head:  # the other points: about 0.2 s of steps each
+                steps = -1
+            results[(name, T)] = measure(dl, T, args, args.act_quant, args.path, n_or,
+                                         oracle_1thread=name in ("tiny", "olmoe-decode"),
+                                         steps=steps)
+        del dl
+        torch.cuda.empty_cache()
 
-    traffic = None
-    ksrc = kernel_source_hash()
-    key = f"{wl.name}/T={T}/{used_path}{'-q8' if args.act_quant else ''}/{dom}"
-    if os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        ent = tr.get("entries", {}).get(key)
-        if ent and ent.get("kernel_source") == ksrc:
-            traffic = ent["bytes_per_launch"]
-
-    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
-                "kernel_us": round(stage_avg_us[dom], 3),
-                "algorithmic_bytes": int(nbytes[dom]), "algorithmic_flops": int(flops[dom])}
-
+    h = results[head]
+    wl = synth.WORKLOADS[head[0]]
+    grouped = h["path"] == "grouped"
+    # dtype: the type the products are taken in; "arithmetic" says how
+    dtype, arith = "bf16", "bf16 MFMA, f32 accumulate"
+    if h["path"] == "decode" and head[1] < 2:
+        arith = "bf16 dot2, f32 accumulate"
+    if args.act_quant and grouped:
+        dtype = "fp8"
+        arith = "e4m3 x " + ("e4m3" if wl.fmt == "e4m3" else "e2m1") + " MFMA, f32 accumulate"
+    elif args.act_quant:
+        arith = "e4m3 activations dequantised to bf16; " + arith
+    roof = dict(h["roofline"])
+    roof["traffic"] = traffic_for(args, wl, head[1], h["path"], roof["kernel"], args.act_quant)
     cpu = None
-    if args.cpu_seconds > 0:
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()
-                         if p.get("user_api") == "blas"] or [1])
-        except Exception:  # noqa: BLE001
-            cores = 1
-        M = lambda m: oracle.Mat(m.q, m.s, m.K)  # noqa: E731
-        done, tok, tc0 = 0, 0, time.perf_counter()
-        while True:
-            b = batches[done % len(batches)]
-            oracle.moe_forward(b.x, layer.w_router, b.bias, M(layer.gate), M(layer.up),
-                               M(layer.down), wl.k, wl.renorm, wl.fmt, act_quant=args.act_quant)
-            done += 1
-            tok += T
-            if time.perf_counter() - tc0 >= args.cpu_seconds:
-                break
-        el = time.perf_counter() - tc0
-        cpu = {"value": round(tok / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"{done} full forwards of T={T} tokens of the {wl.name} workload "
-                         f"({el:.1f} s, float64 numpy oracle)"}
-
+    if "oracle" in h:
+        o = h["oracle"]
+        cpu = {"value": o["tokens_per_s"], "unit": "tokens/s", "cores": o["threads"],
+               "kind": "oracle", "cpu_model": cpu_model, "cores_available": cpu_cores,
+               "sample": f"the first {o['tokens']} tokens of a T={head[1]} batch of the {wl.name} "
+                         f"workload (routing over all {head[1]} tokens; each touched expert "
+                         f"dequantised once), {o['seconds']} s on {o['threads']} threads "
+                         f"(float64 numpy oracle, BLAS 1 thread per worker)"}
     line = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 2),
+        "value": h["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded; random-init weights quantised to the workload's format)",
         "config": {
-            "workload": f"{wl.name}: d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.fmt} "
-                        f"renorm={int(wl.renorm)}, T={T} tokens per step",
-            "tokens_per_step": T,
-            "path": used_path,
+            "workload": h["workload"] + " tokens per step",
+            "tokens_per_step": head[1],
+            "path": h["path"],
             "weights": {"e4m3": "e4m3 + f32 128x128 block scales",
                         "e2m1": "e2m1 + ue8m0 per 32",
                         "nvfp4": "e2m1 + e4m3 per 16 (nvfp4)"}[wl.fmt],
             "activations": "e4m3 per 128-input group, ue8m0 scales" if args.act_quant else "bf16",
-            "distinct_experts_per_step": U,
-            "weight_copies_rotated": copies,
-            "x_batches_rotated": len(xs),
+            "arithmetic": arith,
+            "distinct_experts_per_step": h["distinct_experts_per_step"],
+            "weight_copies_rotated": h["weight_copies_rotated"],
+            "x_batches_rotated": h["x_batches_rotated"],
             "parallelism": "single GPU",
         },
-        "roofline": roofline,
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "stages_us": {k: round(v, 3) for k, v in stage_avg_us.items()},
-        "ms_per_step_with_stage_events": round(timed_ms_per_step, 5),
-        "kernel_source": ksrc,
+        "device_span_ms": h["device_span_ms"],
+        "graph_replay": h["graph_replay"],
+        "aa_rerun": h["aa_rerun"],
+        "stages_us": h["stages_us"],
+        "host": {"cpu_model": cpu_model, "cores_available": cpu_cores},
+        "kernel_source": kernel_source_hash(),
     }
+    if len(results) > 1:
+        line["per_config"] = [{k: v for k, v in r.items() if k not in ("name",)}
+                              for r in results.values()]
     print(json.dumps(line), flush=True)
 
 
