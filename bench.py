@@ -372,9 +372,11 @@ def traffic_for(args, wl, T, path, dom, act_quant):
 
 
 def bench_block(args, wl, T, dl):
-    """One step = RMSNorm of the bf16 hidden rows -> the routed layer on them ->
-    the dense branch (a one-expert top-1 plan, weight exactly 1) -> the add of
-    both into the residual stream.  Each piece timed with events on the stream."""
+    """One step = RMSNorm of the bf16 hidden rows -> the layer with its shared
+    expert (one launch set: the shared expert's rows ride in the routed
+    experts' tile lists) -> the combine, which also adds the residual and
+    writes bf16.  The same block run unfused (routed layer, shared expert as a
+    one-expert plan, separate add) is timed beside it."""
     import numpy as np
     import torch
     import synth
@@ -384,16 +386,19 @@ def bench_block(args, wl, T, dl):
     layer, Ws, copies = dl.layer, dl.Ws, dl.copies
     batches = [synth.make_batch(wl, layer, T, batch_index=i) for i in range(4)]
     xs = [to_dev(b.x) for b in batches]
+    stream = torch.cuda.current_stream()
+    swl = synth.Workload(wl.name + "-shared", d, wl.f, 1, 1, wl.fmt, True, (), False, wl.seed + 100)
+    slay = synth.make_layer(swl)
+    WS = DeviceWeights.upload(slay.w_router, slay.gate.q, slay.gate.s, slay.up.q, slay.up.s,
+                              slay.down.q, slay.down.s)
+    WSs = [WS] + [DeviceWeights(*(t.clone() for t in (WS.w_router, WS.gate_q, WS.gate_s, WS.up_q,
+                                                      WS.up_s, WS.down_q, WS.down_s)))
+                  for _ in range(copies - 1)]
+    fused = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T, shared_expert=True)
+    fouts = fused.outputs(T)
+    del fouts["out"]  # the bf16 block output only
     run = Runner(wl.d, wl.f, wl.E, wl.k, wl.fmt, wl.renorm, T)
     outs = run.outputs(T)
-    stream = torch.cuda.current_stream()
-    dwl = synth.Workload(wl.name + "-dense", d, wl.f, 1, 1, wl.fmt, True, (), False, wl.seed + 100)
-    dlay = synth.make_layer(dwl)
-    WD = DeviceWeights.upload(dlay.w_router, dlay.gate.q, dlay.gate.s, dlay.up.q, dlay.up.s,
-                              dlay.down.q, dlay.down.s)
-    WDs = [WD] + [DeviceWeights(*(t.clone() for t in (WD.w_router, WD.gate_q, WD.gate_s, WD.up_q,
-                                                      WD.up_s, WD.down_q, WD.down_s)))
-                  for _ in range(copies - 1)]
     dense = Runner(d, wl.f, 1, 1, wl.fmt, True, T)
     douts = dense.outputs(T)
     rng = np.random.default_rng(wl.seed)
@@ -402,63 +407,74 @@ def bench_block(args, wl, T, dl):
     xn = torch.empty((T, d), dtype=torch.int16, device="cuda")
     hid = [x.clone() for x in xs]
     outb = torch.empty((T, d), dtype=torch.int16, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    acc = np.zeros(4)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
 
-    def bstep(i, timed=False):
+    def fstep(i, timed=False):
         j = i % len(xs)
         if timed:
             ev[0].record(stream)
         moe.moe_rmsnorm(hid[j], gamma, 1e-6, xn, stream)
         if timed:
             ev[1].record(stream)
-        run.forward(Ws[i % copies], xn, None, outs, stream)
+        fused.forward_block(Ws[i % copies], WSs[i % copies], xn, None, hid[j], outb, fouts, stream)
         if timed:
             ev[2].record(stream)
-        dense.forward(WDs[i % copies], xn, None, douts, stream)
+
+    def ustep(i, timed=False):
+        j = i % len(xs)
+        moe.moe_rmsnorm(hid[j], gamma, 1e-6, xn, stream)
         if timed:
             ev[3].record(stream)
-        moe.moe_residual_add(hid[j], outs["out"], douts["out"], outb, stream)
+        run.forward(Ws[i % copies], xn, None, outs, stream)
+        dense.forward(WSs[i % copies], xn, None, douts, stream)
         if timed:
             ev[4].record(stream)
+        moe.moe_residual_add(hid[j], outs["out"], douts["out"], outb, stream)
+        if timed:
+            ev[5].record(stream)
 
-    for i in range(args.warmup):
-        bstep(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        bstep(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    def wall(step):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    tf = wall(fstep)
+    tu = wall(ustep)
     n_t = min(args.steps, 200)
+    acc = np.zeros(4)
     for i in range(n_t):
-        bstep(i, True)
-        ev[4].synchronize()
-        acc += [ev[k].elapsed_time(ev[k + 1]) for k in range(4)]
+        fstep(i, True)
+        ev[2].synchronize()
+        ustep(i, True)
+        ev[5].synchronize()
+        acc += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
+                ev[3].elapsed_time(ev[4]), ev[4].elapsed_time(ev[5])]
     us = acc * 1e3 / n_t
     norm_bytes = 4 * T * d + 2 * d          # x in, xn out, gain
-    add_bytes = 2 * T * d + 8 * T * d + 2 * T * d  # residual, two f32 terms, bf16 out
     return {
-        "metric": "transformer-block MoE step tokens/s (RMSNorm + routed layer + dense branch + "
-                  "residual add)",
-        "value": round(T * args.steps / (t1 - t0), 2), "unit": "tokens/s", "n_gpus": 1,
+        "metric": "transformer-block MoE step tokens/s (RMSNorm + routed layer with its shared "
+                  "expert + residual add)",
+        "value": round(T * args.steps / tf, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 norm/add, layer as the main line",
+        "ms_per_step": round(tf * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded)",
-        "config": {"workload": f"{wl.name} block: d={d} routed E={wl.E} k={wl.k} f={wl.f}, dense "
-                               f"branch f={wl.f}, {wl.fmt}, T={T}", "tokens_per_step": T},
-        "pieces_us": {"rmsnorm": round(us[0], 3), "routed_layer": round(us[1], 3),
-                      "dense_branch": round(us[2], 3), "residual_add": round(us[3], 3)},
+        "config": {"workload": f"{wl.name} block: d={d} routed E={wl.E} k={wl.k} f={wl.f}, shared "
+                               f"expert f={wl.f}, {wl.fmt}, T={T}", "tokens_per_step": T},
+        "pieces_us": {"rmsnorm": round(us[0], 3), "layer_with_shared_and_add": round(us[1], 3)},
+        "unfused": {"ms_per_step": round(tu * 1e3 / args.steps, 5),
+                    "tokens_per_s": round(T * args.steps / tu, 2),
+                    "pieces_us": {"routed_layer_plus_shared_plan": round(us[2], 3),
+                                  "residual_add": round(us[3], 3)}},
         "rmsnorm_roofline": {"bound": "hbm", "achieved": round(norm_bytes / (us[0] * 1e-6) / 1e9, 2),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(norm_bytes / (us[0] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                              "algorithmic_bytes": norm_bytes},
-        "residual_add_roofline": {"bound": "hbm",
-                                  "achieved": round(add_bytes / (us[3] * 1e-6) / 1e9, 2),
-                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": round(add_bytes / (us[3] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                                  "algorithmic_bytes": add_bytes},
     }
 
 

@@ -110,6 +110,10 @@ typedef struct {
   int32_t renorm;      /* 1: divide the k weights by their sum; 0: keep softmax probabilities */
   int32_t path;        /* moe_path */
   int32_t act_fmt;     /* moe_act_fmt */
+  int32_t shared_expert; /* 1: the layer also has a shared (always-on) expert of the routed
+                          * experts' shape and format, run on every token with weight 1
+                          * (forwards through moe_forward_block); 0: none.  Not with
+                          * n_experts = top_k = 1. */
 } moe_desc;
 
 typedef struct moe_plan_s* moe_plan_t;
@@ -177,6 +181,8 @@ size_t moe_workspace_size(moe_plan_t plan, int32_t n_tokens);
  *   logit_bias f32 [T][E] added to the router logits, or NULL
  *   gate, up, down   expert matrices (see moe_mat)
  *   out        f32 [T][d], 16-byte aligned
+ * A plan with a shared expert runs through moe_forward_block instead
+ * (MOE_ERR_NULL_ARG here: its matrices are missing).
  * Optional outputs (NULL: kept inside the workspace instead):
  *   topk_ids int32 [T][k] (ascending per token), topk_w f32 [T][k],
  *   counts int32 [E], offsets int32 [E+1] (exclusive scan of counts),
@@ -187,6 +193,31 @@ moe_status moe_forward(moe_plan_t plan, int32_t n_tokens, const uint16_t* x, con
                        const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
                        int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* The layer inside a transformer block (dragon.c page, summary and
+ * "Precision": the MoE reads the normed hidden state of sub-block 0, a dense
+ * per-sub-block branch is quantised like the routed experts, and the MoE
+ * output is added to the residual stream at the end of sub-block 1 in the
+ * shortcut-connected layout).  As moe_forward, plus:
+ *   shared_gate, shared_up, shared_down   the shared expert's matrices (one
+ *       expert; expert strides ignored), required exactly when the plan has
+ *       shared_expert = 1.  Its rows run inside the routed experts' launches
+ *       (the tile lists carry them after the routed experts'), and its output
+ *       is added to the combine in f32: out = sum_j w_j y_j + y_shared.
+ *   residual, out_bf16   bf16 bits [T][d], 8-byte aligned, both or neither:
+ *       out_bf16 = bf16_rne(residual + out), written by the combine (in place
+ *       allowed: out_bf16 may be residual).  The plain pre-norm block passes
+ *       its hidden rows; the shortcut layout passes a later point of the
+ *       stream.
+ *   out  f32 [T][d] as in moe_forward, optional when out_bf16 is given.
+ * A plan with one expert and top-1 takes no residual (MOE_ERR_UNSUPPORTED). */
+moe_status moe_forward_block(moe_plan_t plan, int32_t n_tokens, const uint16_t* x,
+                             const float* w_router, const float* logit_bias, const moe_mat* gate,
+                             const moe_mat* up, const moe_mat* down, const moe_mat* shared_gate,
+                             const moe_mat* shared_up, const moe_mat* shared_down,
+                             const uint16_t* residual, uint16_t* out_bf16, float* out,
+                             int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The same forward for callers that cannot allocate device memory or bring
  * a workspace: code under HIP graph capture, tight serving loops, harnesses

@@ -30,7 +30,8 @@ class moe_desc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("wfmt", ctypes.c_int32),
-                ("renorm", ctypes.c_int32), ("path", ctypes.c_int32), ("act_fmt", ctypes.c_int32)]
+                ("renorm", ctypes.c_int32), ("path", ctypes.c_int32), ("act_fmt", ctypes.c_int32),
+                ("shared_expert", ctypes.c_int32)]
 
 
 class moe_mat(ctypes.Structure):
@@ -69,6 +70,12 @@ def _load():
                               ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat), vp, vp, vp, vp,
                               vp, vp, vp, sz, vp]
     L.moe_forward.restype = ctypes.c_int
+    L.moe_forward_block.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(moe_mat),
+                                    ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat),
+                                    ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat),
+                                    ctypes.POINTER(moe_mat), vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                    vp]
+    L.moe_forward_block.restype = ctypes.c_int
     L.moe_forward_noalloc.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(moe_mat),
                                       ctypes.POINTER(moe_mat), ctypes.POINTER(moe_mat), vp, vp,
                                       vp, vp, vp, vp, vp]
@@ -122,11 +129,11 @@ class Plan:
 
 def moe_plan(d_model: int, d_ff: int, n_experts: int, top_k: int, max_tokens: int,
              wfmt: int | str, renorm: bool, path: int = MOE_PATH_AUTO,
-             act_fmt: int = MOE_ACT_BF16) -> Plan:
+             act_fmt: int = MOE_ACT_BF16, shared_expert: bool = False) -> Plan:
     if isinstance(wfmt, str):
         wfmt = WFMT[wfmt]
     desc = moe_desc(d_model, d_ff, n_experts, top_k, max_tokens, int(wfmt), int(bool(renorm)),
-                    int(path), int(act_fmt))
+                    int(path), int(act_fmt), int(bool(shared_expert)))
     h = ctypes.c_void_p()
     st = lib.moe_plan(ctypes.byref(desc), ctypes.byref(h))
     if st != MOE_OK:
@@ -205,6 +212,27 @@ def moe_forward(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_ma
                          _ptr(workspace), int(workspace_bytes), stream or None)
     if st != MOE_OK:
         raise MoeError(st, "moe_forward", moe_plan_info(plan))
+
+
+def moe_forward_block(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_mat,
+                      up: moe_mat, down: moe_mat, shared=None, residual=None, out_bf16=None,
+                      out=None, topk_ids=None, topk_w=None, counts=None, offsets=None, perm=None,
+                      workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """The layer inside a block: `shared` = (gate, up, down) moe_mats of the
+    shared expert (plans made with shared_expert=True), and out_bf16 =
+    bf16(residual + out) written by the combine.  Raises MoeError."""
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if hasattr(workspace, "numel") else 0)
+    sg, su, sd = (ctypes.byref(m) for m in shared) if shared is not None else (None, None, None)
+    st = lib.moe_forward_block(plan.handle, int(n_tokens), _ptr(x), _ptr(w_router),
+                               _ptr(logit_bias), ctypes.byref(gate), ctypes.byref(up),
+                               ctypes.byref(down), sg, su, sd, _ptr(residual), _ptr(out_bf16),
+                               _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+                               _ptr(offsets), _ptr(perm), _ptr(workspace), int(workspace_bytes),
+                               _stream(stream))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_forward_block", moe_plan_info(plan))
 
 
 def moe_forward_noalloc(plan: Plan, n_tokens: int, x, w_router, logit_bias, gate: moe_mat,

@@ -125,7 +125,7 @@ int router_split(const moe_plan_s* p, int T, int* slice) {
 bool dec_mfma_fits(const moe_plan_s* p, int T) {
   const long long lim = 1LL << 31;
   return (long long)T * p->d.d_model * 2 < lim &&
-         (long long)T * p->d.top_k * p->d.d_ff * 2 < lim;
+         (long long)T * (p->d.top_k + (p->d.shared_expert ? 1 : 0)) * p->d.d_ff * 2 < lim;
 }
 
 // MFMA tiles for the decode expert stage from dec_mfma_min_t tokens; for a
@@ -193,14 +193,21 @@ int tile_rows(const moe_plan_s* p, int T) {
   return 16;  // the matvec reads slot_info, not the tile list
 }
 
+// The sorted positions of a forward: T * k routed slots, then (a layer with a
+// shared expert) T more for the shared expert's rows.
+size_t positions(const moe_plan_s* p, int T) {
+  return (size_t)T * p->d.top_k + (p->d.shared_expert ? (size_t)T : 0);
+}
+
 Layout layout(const moe_plan_s* p, int T) {
   const size_t E = p->d.n_experts, k = p->d.top_k, d = p->d.d_model, f = p->d.d_ff;
-  const size_t S = (size_t)T * k;
+  const size_t S = (size_t)T * k, SP = positions(p, T);
   const size_t BM = tile_rows(p, T);
+  const size_t sh = p->d.shared_expert ? 1 : 0;
   Layout L;
   L.nchunk = (T + WAVE - 1) / WAVE;
-  L.max_tiles = (int)((S + BM - 1) / BM + std::min<size_t>(E, S));
-  L.n_slots = (int)std::min<size_t>(E, S);
+  L.max_tiles = (int)((S + BM - 1) / BM + std::min<size_t>(E, S) + sh * ((T + BM - 1) / BM));
+  L.n_slots = (int)(std::min<size_t>(E, S) + sh);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -214,7 +221,7 @@ Layout layout(const moe_plan_s* p, int T) {
   L.offsets = take((E + 1) * 4);
   L.perm = take(S * 4);
   L.inv_perm = take(S * 4);
-  L.tok_of = take(S * 4);
+  L.tok_of = take(SP * 4);
   L.rank = take(S * 4);
   L.hist = take((size_t)L.nchunk * E * 4);
   L.base = take((size_t)L.nchunk * E * 4);
@@ -222,15 +229,15 @@ Layout layout(const moe_plan_s* p, int T) {
   L.n_active = take(4);
   L.tiles = take((size_t)L.max_tiles * 16);
   L.n_tiles = take(4);
-  L.h = take(S * f * 2);
-  L.y = take(S * d * 4);
+  L.h = take(SP * f * 2);
+  L.y = take(SP * d * 4);
   const bool q8 = p->d.act_fmt == MOE_ACT_E4M3_G128;
   L.xq = take(q8 ? (size_t)T * d * 2 : 0);  // decode path: the quantised x as bf16
-  L.hq = take(q8 ? S * f * 2 : 0);           // ... and the quantised h
+  L.hq = take(q8 ? SP * f * 2 : 0);          // ... and the quantised h
   L.qx = take(q8 ? (size_t)T * d : 0);
   L.sx = take(q8 ? (size_t)T * ((d + 127) / 128) : 0);
-  L.qh = take(q8 ? S * f : 0);
-  L.sh = take(q8 ? S * ((f + 127) / 128) : 0);
+  L.qh = take(q8 ? SP * f : 0);
+  L.sh = take(q8 ? SP * ((f + 127) / 128) : 0);
   L.total = o;
   return L;
 }
@@ -315,7 +322,7 @@ template <int FMT>
 moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat G, DMat U, DMat D,
                                const Layout& L, char* ws, float* y_dst, hipStream_t st, bool qdq = false) {
   const int d = p->d.d_model, f = p->d.d_ff;
-  const long long S_all = (long long)T * p->d.top_k;
+  const long long S_all = (long long)positions(p, T);
   uint16_t* xq = reinterpret_cast<uint16_t*>(ws + L.xq);
   const uint16_t* x = qdq ? xq : x_in;
   uint16_t* hq = reinterpret_cast<uint16_t*>(ws + L.hq);
@@ -329,7 +336,7 @@ moe_status launch_expert_stage(moe_plan_s* p, int T, const uint16_t* x_in, DMat 
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
     const long long S = (long long)T * p->d.top_k;
     const uint32_t x_bytes = (uint32_t)((size_t)T * d * 2);
-    const uint32_t h_bytes = (uint32_t)((size_t)S * f * 2);
+    const uint32_t h_bytes = (uint32_t)((size_t)S_all * f * 2);
     // Tile height: 16-row groups per tile (more rows share one activation
     // operand), taken larger only while the tile list stays several times the
     // persistent grid (upper bound of the list: one entry per expert hit plus
@@ -425,7 +432,7 @@ template <int FMT>
 moe_status launch_q8_stage(moe_plan_s* p, int T, const uint16_t* x, DMat G, DMat U, DMat D,
                            const Layout& L, char* ws, float* y_dst, hipStream_t st) {
   const int d = p->d.d_model, f = p->d.d_ff;
-  const long long S = (long long)T * p->d.top_k;
+  const long long S = (long long)positions(p, T);
   const int4* tiles = reinterpret_cast<const int4*>(ws + L.tiles);
   const int32_t* n_tiles = reinterpret_cast<const int32_t*>(ws + L.n_tiles);
   const int32_t* tok_of = reinterpret_cast<const int32_t*>(ws + L.tok_of);
@@ -491,6 +498,8 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   if (d.renorm != 0 && d.renorm != 1) return MOE_ERR_BAD_SHAPE;
   if (d.path < MOE_PATH_AUTO || d.path > MOE_PATH_GROUPED) return MOE_ERR_BAD_SHAPE;
   if (d.act_fmt != MOE_ACT_BF16 && d.act_fmt != MOE_ACT_E4M3_G128) return MOE_ERR_BAD_SHAPE;
+  if (d.shared_expert != 0 && d.shared_expert != 1) return MOE_ERR_BAD_SHAPE;
+  if (d.shared_expert && d.n_experts == 1 && d.top_k == 1) return MOE_ERR_UNSUPPORTED;
   if (d.act_fmt == MOE_ACT_E4M3_G128) {
     if (d.wfmt == MOE_W_E2M1_E4M3_G16) return MOE_ERR_UNSUPPORTED;
     if (d.wfmt == MOE_W_E2M1_UE8M0_G32 && (d.d_model % 64 || d.d_ff % 64)) return MOE_ERR_UNSUPPORTED;
@@ -504,8 +513,11 @@ moe_status moe_plan(const moe_desc* desc, moe_plan_t* out) {
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
-  // int32 sorted positions and 32-bit grid sizes
+  // int32 sorted positions and 32-bit grid sizes; the grouped kernels address
+  // activation rows (x, h) with 32-bit byte offsets
   if ((int64_t)d.max_tokens * d.top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d.max_tokens * (d.top_k + 1) * std::max(d.d_model, d.d_ff) * 2 >= (int64_t)1 << 32)
+    return MOE_ERR_UNSUPPORTED;
 
   int dev = -1, ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
@@ -713,21 +725,42 @@ int32_t moe_plan_path(moe_plan_t p, int32_t T) {
 
 namespace {
 
+// The layer's inputs and outputs beyond moe_forward's: the shared expert's
+// matrices (NULL without one) and the residual add.
+struct BlockIO {
+  const moe_mat* sg = nullptr;
+  const moe_mat* su = nullptr;
+  const moe_mat* sd = nullptr;
+  const uint16_t* residual = nullptr;
+  uint16_t* out_bf16 = nullptr;
+};
+
 moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float* w_router,
                         const float* logit_bias, const moe_mat* gate, const moe_mat* up,
                         const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
                         int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, const BlockIO& io = BlockIO()) {
   if (p == nullptr) return MOE_ERR_NULL_ARG;
   if (T < 0 || T > p->d.max_tokens) return MOE_ERR_BAD_SHAPE;
   if (T == 0) return MOE_OK;
-  if (x == nullptr || w_router == nullptr || out == nullptr || workspace == nullptr)
+  if (x == nullptr || w_router == nullptr || workspace == nullptr) return MOE_ERR_NULL_ARG;
+  // at least one destination; a residual and its bf16 sum come together
+  if ((out == nullptr && io.out_bf16 == nullptr) || ((io.residual == nullptr) != (io.out_bf16 == nullptr)))
+    return MOE_ERR_NULL_ARG;
+  // a plan with a shared expert needs its three matrices, a plan without none
+  const bool shared = p->d.shared_expert != 0;
+  if (shared != (io.sg != nullptr) || shared != (io.su != nullptr) || shared != (io.sd != nullptr))
     return MOE_ERR_NULL_ARG;
   moe_status st;
   if ((st = check_mat(p, gate)) != MOE_OK || (st = check_mat(p, up)) != MOE_OK ||
       (st = check_mat(p, down)) != MOE_OK)
     return st;
-  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(out, 16) || !aligned(workspace, ALIGN))
+  if (shared && ((st = check_mat(p, io.sg)) != MOE_OK || (st = check_mat(p, io.su)) != MOE_OK ||
+                 (st = check_mat(p, io.sd)) != MOE_OK))
+    return st;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || (out && !aligned(out, 16)) ||
+      !aligned(workspace, ALIGN) || (io.residual && !aligned(io.residual, 8)) ||
+      (io.out_bf16 && !aligned(io.out_bf16, 8)))
     return MOE_ERR_ALIGNMENT;
   if ((logit_bias && !aligned(logit_bias, 4)) || (topk_ids && !aligned(topk_ids, 4)) ||
       (topk_w && !aligned(topk_w, 4)) || (counts && !aligned(counts, 4)) ||
@@ -757,6 +790,7 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
   // weight 1, so the router, the combine and the y buffer are skipped and
   // the down projection writes out directly (out = 1 * y exactly)
   const bool dense = E == 1 && k == 1;
+  if (dense && (io.residual || !out)) return MOE_ERR_UNSUPPORTED;  // the down projection writes out
   if (dense) {
     mark(p, MOE_STAGE_TOPK, false, s);
     route_dense<<<(std::max(T, L.max_tiles) + 255) / 256, 256, 0, s>>>(
@@ -799,7 +833,7 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
                                      reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots,     \
                                      reinterpret_cast<int4*>(ws + L.tiles),                      \
                                      reinterpret_cast<int32_t*>(ws + L.n_tiles), T, E, k,        \
-                                     p->d.renorm, tile_rows(p, T))
+                                     p->d.renorm, tile_rows(p, T), shared ? 1 : 0)
     switch (ngp) {
       case 1: MOE_SMALL(1); break;
       case 2: MOE_SMALL(2); break;
@@ -830,7 +864,8 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
   permute_scan<<<1, 1024, 0, s>>>(hist, base, cnt, off, reinterpret_cast<int4*>(ws + L.slot_info),
                                   reinterpret_cast<int32_t*>(ws + L.n_active), L.n_slots, reinterpret_cast<int4*>(ws + L.tiles),
                                   reinterpret_cast<int32_t*>(ws + L.n_tiles), L.nchunk, E, S,
-                                  tile_rows(p, T));
+                                  tile_rows(p, T), reinterpret_cast<int32_t*>(ws + L.tok_of),
+                                  shared ? T : 0);
   permute_scatter<<<(S + 255) / 256, 256, 0, s>>>(ids, rank, base, off, prm, inv,
                                                   reinterpret_cast<int32_t*>(ws + L.tok_of), S, E,
                                                   k);
@@ -841,12 +876,13 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
   if (err != hipSuccess) return hip_fail(p, err, "routing launch");
 
   // a4, a5: expert stage
-  const DMat G{static_cast<const uint8_t*>(gate->q), static_cast<const uint8_t*>(gate->scale),
-               gate->q_expert_stride, gate->s_expert_stride};
-  const DMat U{static_cast<const uint8_t*>(up->q), static_cast<const uint8_t*>(up->scale),
-               up->q_expert_stride, up->s_expert_stride};
-  const DMat D{static_cast<const uint8_t*>(down->q), static_cast<const uint8_t*>(down->scale),
-               down->q_expert_stride, down->s_expert_stride};
+  auto dmat = [](const moe_mat* m, const moe_mat* shm) {
+    return DMat{static_cast<const uint8_t*>(m->q), static_cast<const uint8_t*>(m->scale),
+                m->q_expert_stride, m->s_expert_stride,
+                shm ? static_cast<const uint8_t*>(shm->q) : nullptr,
+                shm ? static_cast<const uint8_t*>(shm->scale) : nullptr};
+  };
+  const DMat G = dmat(gate, io.sg), U = dmat(up, io.su), D = dmat(down, io.sd);
   float* y_dst = dense ? out : nullptr;
   // activation-quantised plans: the block-scaled GEMMs on the grouped path;
   // on the decode path the decode kernels on the quantised values as bf16
@@ -866,9 +902,12 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
   if (!dense) {
     const dim3 g(T, (d / 4 + 255) / 256);
     const float* y = reinterpret_cast<const float*>(ws + L.y);
+    const float* y_sh = shared ? y + (size_t)S * d : nullptr;  // the shared expert's rows
     switch (k) {
-#define MOE_COMBINE(KM) \
-  case KM: combine_fixed_order<KM><<<g, 256, 0, s>>>(y, w, inv, out, d); break;
+#define MOE_COMBINE(KM)                                                                          \
+  case KM:                                                                                       \
+    combine_fixed_order<KM><<<g, 256, 0, s>>>(y, w, inv, y_sh, io.residual, out, io.out_bf16, d); \
+    break;
       MOE_COMBINE(1) MOE_COMBINE(2) MOE_COMBINE(3) MOE_COMBINE(4) MOE_COMBINE(5) MOE_COMBINE(6)
       MOE_COMBINE(7) MOE_COMBINE(8) MOE_COMBINE(9) MOE_COMBINE(10) MOE_COMBINE(11) MOE_COMBINE(12)
       MOE_COMBINE(13) MOE_COMBINE(14) MOE_COMBINE(15) default: MOE_COMBINE(16)
@@ -891,8 +930,26 @@ moe_status moe_forward(moe_plan_t p, int32_t T, const uint16_t* x, const float* 
                        const moe_mat* down, float* out, int32_t* topk_ids, float* topk_w,
                        int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
                        size_t workspace_bytes, void* stream) {
+  if (out == nullptr) return MOE_ERR_NULL_ARG;
   return forward_impl(p, T, x, w_router, logit_bias, gate, up, down, out, topk_ids, topk_w, counts,
                       offsets, perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_forward_block(moe_plan_t p, int32_t T, const uint16_t* x, const float* w_router,
+                             const float* logit_bias, const moe_mat* gate, const moe_mat* up,
+                             const moe_mat* down, const moe_mat* shared_gate,
+                             const moe_mat* shared_up, const moe_mat* shared_down,
+                             const uint16_t* residual, uint16_t* out_bf16, float* out,
+                             int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* perm, void* workspace, size_t workspace_bytes, void* stream) {
+  BlockIO io;
+  io.sg = shared_gate;
+  io.su = shared_up;
+  io.sd = shared_down;
+  io.residual = residual;
+  io.out_bf16 = out_bf16;
+  return forward_impl(p, T, x, w_router, logit_bias, gate, up, down, out, topk_ids, topk_w, counts,
+                      offsets, perm, workspace, workspace_bytes, stream, io);
 }
 
 size_t moe_noalloc_scratch_bytes(void) { return MOE_NOALLOC_SCRATCH_BYTES; }

@@ -15,13 +15,23 @@ namespace moe {
 // 32 inputs of a row; NVFP4 = e2m1 + e4m3 scale per 16 inputs of a row.
 enum : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_NVFP4 = 2 };
 
-// One expert matrix family on the device: byte pointers and expert strides.
+// One expert matrix family on the device: byte pointers and expert strides,
+// and the same matrix of the shared (always-on) expert if the layer has one
+// (a work item whose flag is set reads those instead of expert e's).
 struct DMat {
   const uint8_t* q;
   const uint8_t* s;
   int64_t qs;  // bytes per expert, codes
   int64_t ss;  // bytes per expert, scales
+  const uint8_t* shq;  // shared expert: codes
+  const uint8_t* shs;  // shared expert: scales
 };
+__device__ __forceinline__ const uint8_t* mat_q(const DMat& m, int e, bool sh) {
+  return sh ? m.shq : m.q + e * m.qs;
+}
+__device__ __forceinline__ const uint8_t* mat_s(const DMat& m, int e, bool sh) {
+  return sh ? m.shs : m.s + e * m.ss;
+}
 
 // A "chunk" is 16 consecutive inputs of one weight row: 16 bytes of e4m3
 // codes or 8 bytes of e2m1 codes.  A chunk is decoded once into 8 exact bf16
@@ -275,8 +285,9 @@ __global__ __launch_bounds__(1024) void dec_gateup(
   if (n0 >= f) return;
   const int nrows = min(rpw_total, f - n0);
   const int64_t rb = row_bytes<FMT>(d);
-  const uint8_t* const q[2] = {gate.q + e * gate.qs + n0 * rb, up.q + e * up.qs + n0 * rb};
-  const uint8_t* const s[2] = {gate.s + e * gate.ss, up.s + e * up.ss};
+  const bool sh = info.w != 0;
+  const uint8_t* const q[2] = {mat_q(gate, e, sh) + n0 * rb, mat_q(up, e, sh) + n0 * rb};
+  const uint8_t* const s[2] = {mat_s(gate, e, sh), mat_s(up, e, sh)};
   auto act_row = [&](int i) -> const uint16_t* {
     return x + (size_t)min((uint32_t)tok_of[p0 + i], (uint32_t)(T - 1)) * d;
   };
@@ -303,8 +314,9 @@ __global__ __launch_bounds__(1024) void dec_down(
   if (m0 >= d) return;
   const int nrows = min(rpw_total, d - m0);
   const int64_t rb = row_bytes<FMT>(f);
-  const uint8_t* const q[1] = {down.q + e * down.qs + m0 * rb};
-  const uint8_t* const s[1] = {down.s + e * down.ss};
+  const bool sh = info.w != 0;
+  const uint8_t* const q[1] = {mat_q(down, e, sh) + m0 * rb};
+  const uint8_t* const s[1] = {mat_s(down, e, sh)};
   auto act_row = [&](int i) -> const uint16_t* { return h + (size_t)(p0 + i) * f; };
   auto store = [&](int i, int r, const float (&v)[1]) { y[(size_t)(p0 + i) * d + m0 + r] = v[0]; };
   for (int r0 = 0; r0 < nrows; r0 += RPW) {
@@ -482,10 +494,11 @@ __global__ __launch_bounds__(256) void dec_mfma(
     const int ti = tile / tpe, n0 = (tile - ti * tpe) * TR;
     const int4 info = tiles[ti];
     const int e = info.x, p0 = info.y, cnt = info.z;
+    const bool sh = info.w != 0;
     const int k0 = kb * KU;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const __amdgpu_buffer_rsrc_t wr = buf_rsrc(M[m].q + e * M[m].qs, q_bytes);
+      const __amdgpu_buffer_rsrc_t wr = buf_rsrc(mat_q(M[m], e, sh), q_bytes);
       if constexpr (FMT == FMT_E4M3) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
@@ -494,9 +507,9 @@ __global__ __launch_bounds__(256) void dec_mfma(
           s.wv[m][t].w[0] = buf_load16(wr, off, 0);
           s.wv[m][t].w[1] = buf_load16(wr, off, 16);
         }
-        s.sc[m] = reinterpret_cast<const float*>(M[m].s + e * M[m].ss)[(n0 >> 7) * (K >> 7) + kb];
+        s.sc[m] = reinterpret_cast<const float*>(mat_s(M[m], e, sh))[(n0 >> 7) * (K >> 7) + kb];
       } else {
-        const __amdgpu_buffer_rsrc_t sr = buf_rsrc(M[m].s + e * M[m].ss, s_bytes);
+        const __amdgpu_buffer_rsrc_t sr = buf_rsrc(mat_s(M[m], e, sh), s_bytes);
         const int run0 = SB * (w + KS * (j + q));  // lane's scale run: unit j + q
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
@@ -677,18 +690,25 @@ __global__ __launch_bounds__(256) void dec_mfma(
   }
 }
 
-// out[t][m] = sum over j ascending of w[t][j] * y[inv_perm[t*k+j]][m]: a
-// gather in router order, so every output has one fixed summation order
-// (WARP BACKENDS.md, "Coherent memory": partials reduced in router order).
-// KM = k (the plan's top-k, 1..16) as a compile-time count: all k row
-// indices and weights are loaded first (uniform: scalar loads), then all k
-// rows, then summed in j order, so a thread waits two memory round trips,
-// not 2k.
+// Fixed-order combine: out[t] = sum over j ascending of w[t,j] * y[inv_perm[t*k+j]]
+// in f32, a gather in router order, so every output has one fixed summation
+// order (WARP BACKENDS.md, "Coherent memory": partials reduced in router
+// order); then + the shared expert's row y_sh[t] (if y_sh), stored to out (if
+// out), and out_bf16[t] = bf16(residual[t] + out[t]) (if residual), the add
+// into the residual stream (dragon.c page, summary: the MoE output added to
+// the stream at the end of a sub-block).  Each
+// thread takes 4 columns of one token.  KM = k (the plan's top-k, 1..16) as a
+// compile-time count: all k row indices and weights are loaded first
+// (uniform: scalar loads), then all k rows, then summed in j order, so a
+// thread waits two memory round trips, not 2k.
 template <int KM>
 __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restrict__ y,
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ inv_perm,
-                                                           float* __restrict__ out, int d) {
+                                                           const float* __restrict__ y_sh,
+                                                           const uint16_t* __restrict__ residual,
+                                                           float* __restrict__ out,
+                                                           uint16_t* __restrict__ out_bf16, int d) {
   const int t = blockIdx.x;
   const int m = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (m >= d) return;
@@ -702,6 +722,10 @@ __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restri
   f32x4 v[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) v[j] = *reinterpret_cast<const f32x4*>(y + (size_t)idx[j] * d + m);
+  f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+  u32x2 rv = {0u, 0u};
+  if (y_sh) sv = *reinterpret_cast<const f32x4*>(y_sh + (size_t)t * d + m);
+  if (residual) rv = *reinterpret_cast<const u32x2*>(residual + (size_t)t * d + m);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
@@ -710,7 +734,13 @@ __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restri
     acc.z += wv[j] * v[j].z;
     acc.w += wv[j] * v[j].w;
   }
-  *reinterpret_cast<f32x4*>(out + (size_t)t * d + m) = acc;
+  if (y_sh) acc = f32x4{acc.x + sv.x, acc.y + sv.y, acc.z + sv.z, acc.w + sv.w};
+  if (out) *reinterpret_cast<f32x4*>(out + (size_t)t * d + m) = acc;
+  if (residual) {
+    const uint32_t o0 = f32_to_bf16_rne(bf16_lo(rv.x) + acc.x), o1 = f32_to_bf16_rne(bf16_hi(rv.x) + acc.y);
+    const uint32_t o2 = f32_to_bf16_rne(bf16_lo(rv.y) + acc.z), o3 = f32_to_bf16_rne(bf16_hi(rv.y) + acc.w);
+    *reinterpret_cast<u32x2*>(out_bf16 + (size_t)t * d + m) = u32x2{o0 | (o1 << 16), o2 | (o3 << 16)};
+  }
 }
 
 }  // namespace moe

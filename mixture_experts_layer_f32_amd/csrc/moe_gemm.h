@@ -203,6 +203,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   if (ti >= *n_tiles) return;
   const int4 tile = tiles[ti];
   const int e = tile.x, p_start = tile.y, rows = tile.z;
+  const bool sh = tile.w != 0;  // the shared expert's rows
   const int n0 = cblk * C::BNM;
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int wm = WGM == 2 ? w >> 2 : 0, wn = WGM == 2 ? w & 3 : w;
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     const int ml = GATEUP ? tl : 0, jl = GATEUP ? 0 : tl;
     const DMat& WL = ml == 0 ? W0 : W1;
     if constexpr (!FP4) {
-      wbase[u] = WL.q + e * WL.qs;
+      wbase[u] = mat_q(WL, e, sh);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int tr = 16 * j + (lane >> 2);
@@ -282,17 +283,17 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     } else if constexpr (CPL == 1) {
       const int tr = lane >> 1;
       wchunk[0] = (lane & 1) ^ ((tr >> 3) & 1);
-      wsrc[u][0] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
-      wsrc[u][1] = WL.s + e * WL.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
+      wsrc[u][0] = mat_q(WL, e, sh) + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+      wsrc[u][1] = mat_s(WL, e, sh) + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
       wsrc16[u] = nullptr;
     } else {
       // load j covers tile rows 16 j + lane / 4
       const int tr = lane >> 2;
 #pragma unroll
       for (int j = 0; j < 2; ++j) wchunk[j] = (lane & 3) ^ (((16 * j + tr) >> 2) & 3);
-      wsrc[u][0] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
-      wsrc16[u] = WL.q + e * WL.qs + (int64_t)min(nw0 + 32 * jl + 16 + tr, N - 1) * rbytes;
-      wsrc[u][1] = WL.s + e * WL.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
+      wsrc[u][0] = mat_q(WL, e, sh) + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+      wsrc16[u] = mat_q(WL, e, sh) + (int64_t)min(nw0 + 32 * jl + 16 + tr, N - 1) * rbytes;
+      wsrc[u][1] = mat_s(WL, e, sh) + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups;
     }
   }
   // e4m3: for k-block kb = lane + 64 q of this column's 128-row block (lane
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     if constexpr (!FP4) {
       const int kbs = K >> 7;
       const DMat& W = m == 0 ? W0 : W1;
-      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
+      const float* sf = reinterpret_cast<const float*>(mat_s(W, e, sh)) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int kb = lane + 64 * q;

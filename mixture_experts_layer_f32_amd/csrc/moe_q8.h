@@ -184,6 +184,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
   if (ti >= *n_tiles) return;
   const int4 tile = tiles[ti];
   const int e = tile.x, p_start = tile.y, rows = tile.z;
+  const bool sh = tile.w != 0;  // the shared expert's rows
   const int n0 = cblk * C::BNM;
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
   const int wm = w >> 2, wn = w & 3;
@@ -230,12 +231,12 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
 #pragma unroll
   for (int j = 0; j < WL; ++j) {
     const int tr = (64 / WCH) * j + lane / WCH;
-    wsrc[j] = WT.q + e * WT.qs + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
+    wsrc[j] = mat_q(WT, e, sh) + (int64_t)min(nw0 + 32 * jl + tr, N - 1) * rbytes;
     wchunk[j] = (lane % WCH) ^ wswz(tr);
   }
   // fp4 scales: load c of lane (r, half) brings the bytes (BK / 32) kk + 4 c +
   // 2 half .. + 1 of row r
-  const uint8_t* wssrc = FP4 ? WT.s + e * WT.ss + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups
+  const uint8_t* wssrc = FP4 ? mat_s(WT, e, sh) + (int64_t)min(nw0 + 32 * jl + r32, N - 1) * sgroups
                              : nullptr;
   // e4m3 block scales of this column's 128-row block: block kb in lane kb % 64
   // of register kb / 64
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q8(
 #pragma unroll
     for (int m = 0; m < (GATEUP ? 2 : 1); ++m) {
       const DMat& W = m == 0 ? W0 : W1;
-      const float* sf = reinterpret_cast<const float*>(W.s + e * W.ss) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
+      const float* sf = reinterpret_cast<const float*>(mat_s(W, e, sh)) + (size_t)(min(nw0, N - 1) >> 7) * kbs;
       scv[m][0] = lane < kbs ? sf[lane] : 1.0f;
       scv[m][1] = lane + 64 < kbs ? sf[lane + 64] : 1.0f;
     }

@@ -411,6 +411,10 @@ __device__ inline int block_exclusive_scan(int v, int* total) {
 // in ascending order, that received at least one slot, and (-1, 0, 0) for
 // the remaining entries up to n_slots; and the grouped-GEMM tile list: for
 // every expert, ceil(count/BM) tiles of (expert, first sorted position, rows).
+// A layer with a shared expert (shT = T tokens, else 0) appends that
+// expert's work after the routed experts': positions S .. S + T - 1 hold
+// tokens 0 .. T - 1, one record (0, S, T, 1) and ceil(T/BM) tiles whose last
+// field 1 marks the shared expert's weights.
 __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__ hist,
                                                      int32_t* __restrict__ base,
                                                      int32_t* __restrict__ counts,
@@ -419,7 +423,8 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
                                                      int32_t* __restrict__ n_active, int n_slots,
                                                      int4* __restrict__ tiles,
                                                      int32_t* __restrict__ n_tiles, int nchunk,
-                                                     int E, int S, int BM) {
+                                                     int E, int S, int BM,
+                                                     int32_t* __restrict__ tok_of, int shT) {
   const int e = threadIdx.x;
   int c_e = 0;
   if (e < E) {
@@ -443,15 +448,22 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   if (e == 0) offsets[E] = S;
   const int act = block_exclusive_scan((e < E && c_e > 0) ? 1 : 0, &tot);
   if (e < E && c_e > 0) slot_info[act] = make_int4(e, off, c_e, 0);
-  if (e == 0) *n_active = tot;
-  for (int i = tot + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
+  const int n_act = tot, sh = shT > 0 ? 1 : 0;
+  if (e == 0) {
+    if (sh) slot_info[n_act] = make_int4(0, S, shT, 1);
+    *n_active = n_act + sh;
+  }
+  for (int i = n_act + sh + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
   const int mt = (e < E) ? (c_e + BM - 1) / BM : 0;
   const int tb = block_exclusive_scan(mt, &tot);
   for (int i = 0; i < mt; ++i) {
     const int rows = min(BM, c_e - i * BM);
     tiles[tb + i] = make_int4(e, off + i * BM, rows, 0);
   }
-  if (e == 0) *n_tiles = tot;
+  const int nsh = (shT + BM - 1) / BM;
+  for (int i = e; i < nsh; i += blockDim.x) tiles[tot + i] = make_int4(0, S + i * BM, min(BM, shT - i * BM), 1);
+  for (int t = e; t < shT; t += blockDim.x) tok_of[S + t] = t;
+  if (e == 0) *n_tiles = tot + nsh;
 }
 
 // perm[offsets[e] + base[chunk][e] + rank[s]] = s; inv_perm[s] = that
@@ -481,7 +493,8 @@ __global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict
 // with a single 64-token chunk): 16 wavefronts take the tokens' top-k, then
 // LDS lane masks give the stable ranks, one scan gives counts, offsets, the
 // per-expert records and the tile list, and the scatter writes perm,
-// inv_perm and the token of each sorted position.
+// inv_perm and the token of each sorted position.  `shared` (0 or 1): the
+// shared expert's record and tiles follow, as in permute_scan.
 template <int NG>
 __global__ __launch_bounds__(1024) void route_small(
     const float* __restrict__ part, int nsplit, const float* __restrict__ bias,
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(1024) void route_small(
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
     int32_t* __restrict__ tok_of, int4* __restrict__ slot_info, int32_t* __restrict__ n_active,
     int n_slots, int4* __restrict__ tiles, int32_t* __restrict__ n_tiles, int T, int E, int k,
-    int renorm, int BM) {
+    int renorm, int BM, int shared) {
   __shared__ unsigned long long mask[MAX_E];
   __shared__ int off_s[MAX_E];
   __shared__ int ids_s[WAVE * MAX_K];  // the ids again, read back without a memory round trip
@@ -520,10 +533,17 @@ __global__ __launch_bounds__(1024) void route_small(
   if (e == 0) offsets[E] = S;
   if (e < E && c_e > 0) slot_info[act] = make_int4(e, off, c_e, 0);
   const int n_act = (tot >> 10) & 1023;
-  if (e == 0) *n_active = n_act;
-  for (int i = n_act + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
+  if (e == 0) {
+    if (shared) slot_info[n_act] = make_int4(0, S, T, 1);
+    *n_active = n_act + shared;
+  }
+  for (int i = n_act + shared + e; i < n_slots; i += blockDim.x) slot_info[i] = make_int4(-1, 0, 0, 0);
   for (int i = 0; i < mt; ++i) tiles[tb + i] = make_int4(e, off + i * BM, min(BM, c_e - i * BM), 0);
-  if (e == 0) *n_tiles = tot >> 20;
+  // a shared expert: its tiles after the routed ones, positions S .. S + T - 1
+  const int n_rt = tot >> 20, nsh = shared ? (T + BM - 1) / BM : 0;
+  if (tid < nsh) tiles[n_rt + tid] = make_int4(0, S + tid * BM, min(BM, T - tid * BM), 1);
+  if (shared && tid < T) tok_of[S + tid] = tid;
+  if (e == 0) *n_tiles = n_rt + nsh;
   __syncthreads();
   for (int s = tid; s < S; s += 1024) {
     const int t = s / k;

@@ -9,7 +9,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (MOE_PATH_AUTO, Plan, mat, moe_forward, moe_plan, moe_plan_set,
+from . import (MOE_PATH_AUTO, Plan, mat, moe_forward, moe_forward_block, moe_plan, moe_plan_set,
                moe_workspace_h_offset, moe_workspace_size)
 
 
@@ -57,10 +57,11 @@ class Runner:
 
     def __init__(self, d: int, f: int, E: int, k: int, fmt: str, renorm: bool, max_tokens: int,
                  path: int = MOE_PATH_AUTO, device="cuda", act_fmt: int = 0,
-                 options: Optional[dict] = None):
+                 options: Optional[dict] = None, shared_expert: bool = False):
         self.d, self.f, self.E, self.k = d, f, E, k
         self.device = device
-        self.plan: Plan = moe_plan(d, f, E, k, max_tokens, fmt, renorm, path, act_fmt)
+        self.plan: Plan = moe_plan(d, f, E, k, max_tokens, fmt, renorm, path, act_fmt,
+                                   shared_expert)
         for opt, val in (options or {}).items():
             moe_plan_set(self.plan, opt, val)
         self.max_tokens = max_tokens
@@ -86,6 +87,19 @@ class Runner:
                     outs.get("topk_ids"), outs.get("topk_w"), outs.get("counts"),
                     outs.get("offsets"), outs.get("perm"), self.workspace,
                     self.workspace.numel(), stream)
+
+    def forward_block(self, W: DeviceWeights, WS: DeviceWeights, x: torch.Tensor,
+                      bias: Optional[torch.Tensor], residual: torch.Tensor,
+                      out_bf16: torch.Tensor, outs: dict, stream=None) -> None:
+        """The layer with the shared expert WS (one expert) and the residual
+        add: out_bf16 = bf16(residual + routed + shared); outs["out"] gets
+        routed + shared in f32 (if present)."""
+        T = x.shape[0]
+        g, u, dn = W.mats()
+        moe_forward_block(self.plan, T, x, W.w_router, bias, g, u, dn, WS.mats(), residual,
+                          out_bf16, outs.get("out"), outs.get("topk_ids"), outs.get("topk_w"),
+                          outs.get("counts"), outs.get("offsets"), outs.get("perm"),
+                          self.workspace, self.workspace.numel(), stream)
 
     def h(self, T: int) -> torch.Tensor:
         """The workspace's h (bf16 bits as int16 [T*k, f], sorted-slot order)."""
