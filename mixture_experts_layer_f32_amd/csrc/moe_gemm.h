@@ -107,8 +107,14 @@ __device__ __forceinline__ void stage_barrier() {
 // 2^-24 each).  The ratios and powers of two of all of a column's blocks are
 // computed once per workgroup, one block per lane.  The rescale of a token
 // chunk's accumulators follows that chunk's last MFMAs of the block, so it
-// overlaps the next chunk's MFMAs.  fp4 scales are applied exactly in the
-// conversion, so there is no rescale.
+// overlaps the next chunk's MFMAs; the last chunk's waits for the next
+// block's first chunk.  fp4 scales are applied exactly in the conversion, so
+// there is no rescale.
+//
+// The kernel runs at the chip's power limit (the shader clock drops to about
+// 1.7 GHz on quantised-normal data, against 2.35 GHz on zeros), so work that
+// does not reach an output costs time even when it hides behind loads: the
+// padding rows of a tile's last chunk are zeros, not copies of a token.
 template <int FMT, bool GATEUP, int TNW, int TM_, int WGM_>
 struct BigCfg {
   static constexpr bool FP4 = FMT != FMT_E4M3;
@@ -329,12 +335,26 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   // k-tail; those inputs are zeroed at decode)
   // e4m3 (K a multiple of 128: no chunk of a stage runs past the row): the
   // activation and the weight loads of stage kk into slot `slot`
+  // lanes whose activation row is past the tile load nothing: those rows of
+  // the tile's last 32-row chunk are zeroed once in every slot below, so the
+  // MFMAs of the padding rows multiply zeros (their outputs are not stored;
+  // zero operands only save switching power)
+  bool alive[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) alive[i] = (AL * w + i) * (64 / C::ACH) + lane / C::ACH < rows;
   auto issue_act = [&](int kk, int slot) {
     const uint8_t* abase = reinterpret_cast<const uint8_t*>(act) + 2 * (size_t)(kk * BK);
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      if (i < n_a) lds_dma16_so(abase, aoff[i], lds_a + 16 * (slot * C::A_V4 + (AL * w + i) * 64));
+      if (i < n_a && alive[i]) lds_dma16_so(abase, aoff[i], lds_a + 16 * (slot * C::A_V4 + (AL * w + i) * 64));
   };
+  {
+    const int r1 = min(BM, 32 * ((rows + 31) >> 5));
+    const int n = (r1 - rows) * C::ACH;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+      for (int idx = (int)threadIdx.x; idx < n; idx += 512) sA[sl][rows * C::ACH + idx] = u32x4{0u, 0u, 0u, 0u};
+  }
   auto issue_wt = [&](int kk, int slot) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u)
@@ -352,7 +372,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     }
 #pragma unroll
     for (int i = 0; i < AL; ++i)
-      if (i < n_a)
+      if (i < n_a && alive[i])
         lds_dma16(asrc[i] + min(k0 + 8 * achunk[i], K - 8), &sA[slot][(AL * w + i) * 64]);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -424,6 +444,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
 #pragma unroll
       for (int t = 0; t < NW; ++t) R[i][t] = zero;
     float p2[NMAT];  // e4m3: the power of two of the current block's scale
+    // the last chunk's rescale at a block's end waits for the next stage,
+    // after that stage's first chunk's MFMAs (it then overlaps MFMAs instead
+    // of ending the stage); its ratio is kept here
+    constexpr bool DEFER = NA > 1 && !FP4;
+    float pend[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) pend[m] = 1.0f;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) p2[m] = FP4 ? 1.0f : lane_of(pw[m], 0);
 
@@ -492,14 +519,30 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
 #pragma unroll
             for (int t = 0; t < NW; ++t) R[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[t][s], R[i][t], 0, 0, 0);
           }
-          if constexpr (ENDBLK) {
+          if constexpr (NEWBLK && DEFER) {
+            if (i == 0) {
 #pragma unroll
-            for (int t = 0; t < NW; ++t) {
-              const float r = ratio[GATEUP ? t : 0];
+              for (int t = 0; t < NW; ++t) {
+                const float r = pend[GATEUP ? t : 0];
 #pragma unroll
-              for (int v = 0; v < 16; ++v) R[i][t][v] *= r;
+                for (int v = 0; v < 16; ++v) R[NA - 1][t][v] *= r;
+              }
             }
           }
+          if constexpr (ENDBLK) {
+            if (!DEFER || i < NA - 1) {
+#pragma unroll
+              for (int t = 0; t < NW; ++t) {
+                const float r = ratio[GATEUP ? t : 0];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) R[i][t][v] *= r;
+              }
+            }
+          }
+        }
+        if constexpr (ENDBLK && DEFER) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) pend[m] = ratio[m];
         }
       }
     };
