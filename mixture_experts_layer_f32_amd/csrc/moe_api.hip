@@ -30,7 +30,7 @@ inline size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 constexpr int GEMV_MAX_T = 16;   // router: wavefront GEMV up to this many tokens, MFMA above
 
 struct Layout {
-  size_t logits, ids, w, counts, offsets, perm, inv_perm, tok_of, rank, hist, base, slot_info, n_active,
+  size_t logits, w3, ids, w, counts, offsets, perm, inv_perm, tok_of, rank, hist, base, slot_info, n_active,
       tiles, n_tiles, h, y, xq, hq, qx, sx, qh, sh, total;
   int nchunk, max_tiles, n_slots;
 };
@@ -104,12 +104,23 @@ int path_for(const moe_plan_s* p, int T) {
   return T <= p->t_decode ? MOE_PATH_DECODE : MOE_PATH_GROUPED;
 }
 
+// router: 256 x 128 MFMA tiles where they alone make 32 blocks (the 64 x 64
+// tiles re-read the weight planes from L2 4x as often; with fewer tiles the
+// larger ones leave the chip underfilled: measured on the d = 7168 layer at
+// 4096 tokens 98 -> 67 us, and slower on the 2048-token OLMoE shape and the
+// 1024-token FP4 layer)
+bool router_big(const moe_plan_s* p, int T) {
+  return (long long)((T + 255) / 256) * ((p->d.n_experts + 127) / 128) >= 32;
+}
+
 // Router K-split: enough blocks to cover the chip, slices of >= 256 inputs
 // (multiples of 32).  Returns the number of slices; *slice gets their width.
 int router_split(const moe_plan_s* p, int T, int* slice) {
   const int d = p->d.d_model, E = p->d.n_experts;
-  const int blocks = T <= GEMV_MAX_T ? (E + 3) / 4 : ((T + 63) / 64) * ((E + 63) / 64);
-  const int target = T <= GEMV_MAX_T ? 2 * p->cus : 4 * p->cus;
+  const int blocks = T <= GEMV_MAX_T    ? (E + 3) / 4
+                     : router_big(p, T)  ? ((T + 255) / 256) * ((E + 127) / 128)
+                                         : ((T + 63) / 64) * ((E + 63) / 64);
+  const int target = T <= GEMV_MAX_T ? 2 * p->cus : router_big(p, T) ? p->cus : 4 * p->cus;
   // few tokens: at most 4 slices, so the top-k sums its slice partials in
   // one round of loads (measured 0.3-1.5 % per step against 6-8 slices)
   const int cap = T <= GEMV_MAX_T ? 4 : MAX_SPLIT;
@@ -215,6 +226,7 @@ Layout layout(const moe_plan_s* p, int T) {
     return at;
   };
   L.logits = take((size_t)router_split(p, T, nullptr) * T * E * 4);
+  L.w3 = take(router_big(p, T) ? 3 * E * d * 2 : 0);  // the router weights as three bf16 planes
   L.ids = take(S * 4);
   L.w = take(S * 4);
   L.counts = take(E * 4);
@@ -810,11 +822,21 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
       router_gemv<1><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
     else if (T <= 4)
       router_gemv<4><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
-    else
+    else if (T <= 8)
       router_gemv<8><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
+    else
+      router_gemv<16><<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
   } else {
-    const dim3 g((T + 63) / 64, (E + 63) / 64, nsplit);
-    router_mfma<<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
+    if (router_big(p, T)) {
+      uint16_t* w3 = reinterpret_cast<uint16_t*>(ws + L.w3);
+      const size_t n = (size_t)E * d;
+      router_split3<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(w_router, w3, n);
+      const dim3 g((T + 255) / 256, (E + 127) / 128, nsplit);
+      router_mfma_big<<<g, 512, 0, s>>>(x, w3, logits, T, d, E, slice);
+    } else {
+      const dim3 g((T + 63) / 64, (E + 63) / 64, nsplit);
+      router_mfma<<<g, 256, 0, s>>>(x, w_router, logits, T, d, E, slice);
+    }
   }
   mark(p, MOE_STAGE_ROUTER, true, s);
   const int ng = (E + WAVE - 1) / WAVE;
@@ -900,13 +922,14 @@ moe_status forward_impl(moe_plan_t p, int32_t T, const uint16_t* x, const float*
   // a6: fixed-order combine
   mark(p, MOE_STAGE_COMBINE, false, s);
   if (!dense) {
-    const dim3 g(T, (d / 4 + 255) / 256);
+    const int ncb = (d / 4 + 255) / 256;
+    const dim3 g((unsigned)((long long)T * ncb));
     const float* y = reinterpret_cast<const float*>(ws + L.y);
     const float* y_sh = shared ? y + (size_t)S * d : nullptr;  // the shared expert's rows
     switch (k) {
 #define MOE_COMBINE(KM)                                                                          \
   case KM:                                                                                       \
-    combine_fixed_order<KM><<<g, 256, 0, s>>>(y, w, inv, y_sh, io.residual, out, io.out_bf16, d); \
+    combine_fixed_order<KM><<<g, 256, 0, s>>>(y, w, inv, y_sh, io.residual, out, io.out_bf16, d, ncb); \
     break;
       MOE_COMBINE(1) MOE_COMBINE(2) MOE_COMBINE(3) MOE_COMBINE(4) MOE_COMBINE(5) MOE_COMBINE(6)
       MOE_COMBINE(7) MOE_COMBINE(8) MOE_COMBINE(9) MOE_COMBINE(10) MOE_COMBINE(11) MOE_COMBINE(12)

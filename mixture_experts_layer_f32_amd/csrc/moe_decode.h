@@ -708,9 +708,12 @@ __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restri
                                                            const float* __restrict__ y_sh,
                                                            const uint16_t* __restrict__ residual,
                                                            float* __restrict__ out,
-                                                           uint16_t* __restrict__ out_bf16, int d) {
-  const int t = blockIdx.x;
-  const int m = (blockIdx.y * 256 + threadIdx.x) * 4;
+                                                           uint16_t* __restrict__ out_bf16, int d,
+                                                           int ncb) {
+  // workgroup = (token, 1024-column block), the column blocks of a token
+  // adjacent in launch order, so its k rows are read whole and together
+  const int t = blockIdx.x / ncb;
+  const int m = ((blockIdx.x - t * ncb) * 256 + threadIdx.x) * 4;
   if (m >= d) return;
   int idx[KM];
   float wv[KM];

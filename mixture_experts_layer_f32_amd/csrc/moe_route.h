@@ -182,6 +182,124 @@ __global__ __launch_bounds__(256) void router_mfma(const uint16_t* __restrict__ 
   }
 }
 
+// w3 = the hi, mid and lo planes of the router weights, each [E][d] bf16
+// (n = E d, a multiple of 4).
+__global__ __launch_bounds__(256) void router_split3(const float* __restrict__ wr,
+                                                     uint16_t* __restrict__ w3, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (4 * i >= n) return;
+  const f32x4 v = reinterpret_cast<const f32x4*>(wr)[i];
+  uint16_t h[4], m[4], l[4];
+  split3_bf16(v.x, h[0], m[0], l[0]);
+  split3_bf16(v.y, h[1], m[1], l[1]);
+  split3_bf16(v.z, h[2], m[2], l[2]);
+  split3_bf16(v.w, h[3], m[3], l[3]);
+  u32x2* o = reinterpret_cast<u32x2*>(w3);
+  o[i] = u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+  o[n / 4 + i] = u32x2{(uint32_t)m[0] | ((uint32_t)m[1] << 16), (uint32_t)m[2] | ((uint32_t)m[3] << 16)};
+  o[n / 2 + i] = u32x2{(uint32_t)l[0] | ((uint32_t)l[1] << 16), (uint32_t)l[2] | ((uint32_t)l[3] << 16)};
+}
+
+// Many tokens and experts: 256-token x 128-expert tiles, 8 wavefronts in a
+// 2 x 4 grid (128 tokens x 32 experts each: four 32-token chunks sharing each
+// B fragment), on the three bf16 planes split once per forward by
+// router_split3.  Each plane is read from L2 once per 256 tokens instead of
+// the 64 x 64 tiles' once per 64, which re-split and re-read it per tile.
+// Same products and the same order of 16-deep steps (hi, mid, lo) within a
+// K-slice as router_mfma.
+__global__ __launch_bounds__(512) void router_mfma_big(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ w3,
+                                                       float* __restrict__ part, int T, int d,
+                                                       int E, int slice) {
+  constexpr int BK = 64, LDK = BK + 8, D = 3, BT = 256, BE = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[BT * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[3][BE * LDK];
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+  const int k0 = blockIdx.z * slice, k1 = min(d, k0 + slice);
+  const int wm0 = (wv >> 2) * 128, wn0 = (wv & 3) * 32;
+  const int nit = (k1 - k0 + BK - 1) / BK;
+  const size_t plane = (size_t)E * d;
+  u32x4 rx[D][4];     // activations: 256 rows x 8 chunks = 2048, 4 per thread
+  u32x4 rw[D][3][2];  // each plane: 128 rows x 8 chunks = 1024, 2 per thread
+  auto load = [&](int it, int set) {
+    const int k = k0 + it * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 512 * i, r = c >> 3, col = (c & 7) * 8;
+      rx[set][i] = t0 + r < T && k + col < k1
+                       ? *reinterpret_cast<const u32x4*>(x + (size_t)(t0 + r) * d + k + col)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i, r = c >> 3, col = (c & 7) * 8;
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        rw[set][p][i] = e0 + r < E && k + col < k1
+                            ? *reinterpret_cast<const u32x4*>(w3 + p * plane + (size_t)(e0 + r) * d + k + col)
+                            : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 512 * i, r = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<u32x4*>(xs + r * LDK + col) = rx[set][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 512 * i, r = c >> 3, col = (c & 7) * 8;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) *reinterpret_cast<u32x4*>(ws[p] + r * LDK + col) = rw[set][p][i];
+    }
+  };
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  auto compute = [&]() {
+    const int r = lane & 31, kh = (lane >> 5) * 8;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 b[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) b[p] = *reinterpret_cast<const bf16x8*>(ws[p] + (wn0 + r) * LDK + kk + kh);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(xs + (wm0 + 32 * c + r) * LDK + kk + kh);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[p], acc[c], 0, 0, 0);
+      }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < D - 1; ++p)
+    if (p < nit) load(p, p);
+  for (int it0 = 0; it0 < nit; it0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int it = it0 + j;
+      if (it >= nit) break;
+      if (it + D - 1 < nit) load(it + D - 1, (j + D - 1) % D);
+      __syncthreads();  // the previous stage's MFMAs are done with LDS
+      store(j);
+      __syncthreads();
+      compute();
+    }
+  }
+  float* out = part + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = t0 + wm0 + 32 * c + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int e = e0 + wn0 + (lane & 31);
+      if (t < T && e < E) out[(size_t)t * E + e] = acc[c][v];
+    }
+}
+
 // ---------------------------------------------------------------- softmax + top-k
 
 constexpr int MAX_E = 1024;
