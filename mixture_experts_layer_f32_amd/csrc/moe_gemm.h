@@ -579,6 +579,55 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     }
     wait_vm<0>();
 
+    // One wavefront row: the output leaves through LDS, each wavefront
+    // turning its 32-row chunk into rows of 16-byte pieces (bf16 h: 64 bytes
+    // of a row per wavefront; f32 y: 256), so the stores are 16 bytes per
+    // lane instead of 2 or 4.  Row strides padded by 8 elements: the writes of
+    // the lane halves (rows r and r + 4) fall in different banks.
+    constexpr int NCW = 32 * TNW, RSW = NCW + 8;
+    constexpr bool TEPI = WGM == 1 && 8 * 32 * RSW * (GATEUP ? 2 : 4) <= (int)sizeof(sW);
+    if constexpr (TEPI) {
+      __syncthreads();  // every wavefront's reads of the last stage are done
+      if constexpr (GATEUP) {
+        uint16_t* ep = reinterpret_cast<uint16_t*>(&sW[0][0]) + w * 32 * RSW;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+#pragma unroll
+          for (int j = 0; j < TNW; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float g = R[i][j][v] * mlast[0], u = R[i][TNW + j][v] * mlast[NMAT - 1];
+              ep[acc_row(v, lane) * RSW + 32 * j + r32] = (uint16_t)f32_to_bf16_rne(silu(g) * u);
+            }
+#pragma unroll
+          for (int q = 0; q < NCW / 16; ++q) {
+            const int idx = lane + 64 * q, row = idx / (NCW / 8), seg = idx % (NCW / 8);
+            const u32x4 val = *reinterpret_cast<const u32x4*>(ep + row * RSW + seg * 8);
+            const int m = 32 * i + row, n = nw0 + seg * 8;
+            if (m < rows && n < N)
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (size_t)(p_start + m) * N + n) = val;
+          }
+        }
+      } else {
+        float* ep = reinterpret_cast<float*>(&sW[0][0]) + w * 32 * RSW;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+#pragma unroll
+          for (int j = 0; j < TNW; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ep[acc_row(v, lane) * RSW + 32 * j + r32] = R[i][j][v] * mlast[0];
+#pragma unroll
+          for (int q = 0; q < NCW / 8; ++q) {
+            const int idx = lane + 64 * q, row = idx / (NCW / 4), seg = idx % (NCW / 4);
+            const f32x4 val = *reinterpret_cast<const f32x4*>(ep + row * RSW + seg * 4);
+            const int m = 32 * i + row, n = nw0 + seg * 4;
+            if (m < rows && n < N)
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + (size_t)(p_start + m) * N + n) = val;
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
 #pragma unroll
