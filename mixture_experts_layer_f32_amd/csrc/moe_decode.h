@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restri
   }
   f32x4 v[KM];
 #pragma unroll
-  for (int j = 0; j < KM; ++j) v[j] = *reinterpret_cast<const f32x4*>(y + (size_t)idx[j] * d + m);
+  for (int j = 0; j < KM; ++j) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)idx[j] * d + m));
   f32x4 sv = {0.f, 0.f, 0.f, 0.f};
   u32x2 rv = {0u, 0u};
   if (y_sh) sv = *reinterpret_cast<const f32x4*>(y_sh + (size_t)t * d + m);
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(256) void combine_fixed_order(const float* __restri
     acc.w += wv[j] * v[j].w;
   }
   if (y_sh) acc = f32x4{acc.x + sv.x, acc.y + sv.y, acc.z + sv.z, acc.w + sv.w};
-  if (out) *reinterpret_cast<f32x4*>(out + (size_t)t * d + m) = acc;
+  if (out) __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(out + (size_t)t * d + m));
   if (residual) {
     const uint32_t o0 = f32_to_bf16_rne(bf16_lo(rv.x) + acc.x), o1 = f32_to_bf16_rne(bf16_hi(rv.x) + acc.y);
     const uint32_t o2 = f32_to_bf16_rne(bf16_lo(rv.y) + acc.z), o3 = f32_to_bf16_rne(bf16_hi(rv.y) + acc.w);
