@@ -501,9 +501,10 @@ def main():
                                                          "COPY_WRITE_CSV"),
                     help="write --traffic from rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--block", action="store_true",
-                    help="time the transformer-block steps around the layer too: RMSNorm of the "
-                         "hidden state, a dense (shared) SwiGLU branch of width f in the same "
-                         "format, and the add into the bf16 residual stream")
+                    help="time the transformer-block step: RMSNorm of the hidden state, then the "
+                         "layer with a shared SwiGLU expert of width f in the same format inside "
+                         "the routed launches and the add into the bf16 residual stream inside "
+                         "the combine; the unfused sequence is timed beside it")
     ap.add_argument("--act-quant", action="store_true",
                     help="the activation-quantised variant: x and h as e4m3 per 128-input group "
                          "(UE8M0 scales), block-scaled fp8 MFMA; opt-in, it changes results")
