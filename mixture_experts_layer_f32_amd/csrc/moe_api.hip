@@ -300,7 +300,8 @@ void launch_big_cfg(int max_tiles, int N, int K, int T, const uint16_t* act, DMa
   constexpr int BNM = BigCfg<FMT, GATEUP, TNW, TM, WGM>::BNM;
   const int nb = (N + BNM - 1) / BNM;
   const dim3 g((unsigned)(8LL * ((max_tiles + 7) / 8) * nb));
-  gemm_big<FMT, GATEUP, TNW, TM, WGM><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb);
+  gemm_big<FMT, GATEUP, TNW, TM, WGM><<<g, 512, 0, st>>>(act, W0, W1, tiles, n_tiles, tok_of, out, N, K, T, nb,
+                                                      max_tiles);
 }
 
 template <int FMT, bool GATEUP, int TNW>

@@ -190,7 +190,7 @@ template <int FMT, bool GATEUP, int TNW, int TM_, int WGM_>
 __global__ __launch_bounds__(512, 1) void gemm_big(
     const uint16_t* __restrict__ act, DMat W0, DMat W1, const int4* __restrict__ tiles,
     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok_of,
-    void* __restrict__ out, int N, int K, int T, int nb) {
+    void* __restrict__ out, int N, int K, int T, int nb, int max_tiles) {
   using C = BigCfg<FMT, GATEUP, TNW, TM_, WGM_>;
   constexpr bool FP4 = C::FP4;
   constexpr int NMAT = C::NMAT, NW = C::NW, TM = C::TM, BK = C::BK, NS = C::NS, AL = C::AL;
@@ -206,8 +206,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   const int L = blockIdx.x, xcd = L & 7, sq = L >> 3;
   const int lt = sq / nb, cblk = sq - lt * nb;
   const int ti = 8 * lt + xcd;
+  // the entry is read beside the count (clamped into the list), so the two
+  // loads take one memory round trip
+  const int4 tile = tiles[min(ti, max_tiles - 1)];
   if (ti >= *n_tiles) return;
-  const int4 tile = tiles[ti];
   const int e = tile.x, p_start = tile.y, rows = tile.z;
   const bool sh = tile.w != 0;  // the shared expert's rows
   const int n0 = cblk * C::BNM;
@@ -308,6 +310,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
   // block after the last); m_last, the last block's mantissa, scales the
   // output
   float pw[NMAT][2], rt[NMAT][2], mlast[NMAT];
+  // (loaded after the prologue's loads are issued: they are first needed by
+  // the first stage's compute)
+  auto load_scales = [&]() {
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
     pw[m][0] = pw[m][1] = rt[m][0] = rt[m][1] = mlast[m] = 1.0f;
@@ -326,6 +331,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
       mlast[m] = mant_part(sf[kbs - 1]);
     }
   }
+  };
   auto lane_of = [](const float (&v)[2], int kb) {  // uniform kb
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? v[0] : v[1]), kb & 63));
   };
@@ -652,6 +658,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big(
     if (p < nk) issue(p, p);
   if constexpr (EARLYW)
     if (NS - 1 < nk) issue_wt(NS - 1, NS - 1);
+  load_scales();
   dispatch_count<TM>(nact, run);
 }
 
