@@ -484,6 +484,10 @@ __global__ __launch_bounds__(256) void dec_mfma(
   // (measured 2-3% faster there; e4m3 skips the issue past the end, measured
   // 2% faster for it).
   constexpr bool ALWAYS = FMT != FMT_E4M3;
+  // gate/up: lane r's token row depends only on the tile, and a wavefront
+  // issues a tile's units one after another, so it is looked up once per tile
+  int row_tile = -1;
+  uint32_t tile_row = 0;
   auto issue = [&](Unit& s, int u) {
     const bool live = u < units;
     u = min(u, units - 1);
@@ -530,14 +534,18 @@ __global__ __launch_bounds__(256) void dec_mfma(
     // tokens by scalar loads, lane r keeping entry r; down reads h[p0 + r]
     uint32_t row = (uint32_t)(p0 + min(r, cnt - 1));
     if (GATEUP) {
-      const int32_t* tp = tok_of + p0;
-      int t = tp[0];
+      if (tile != row_tile) {
+        // the entry's (<= 16) token ids by scalar loads, written to lanes
+        // 0..15 of one register and spread to lane groups 1..3 by a permute
+        row_tile = tile;
+        const int32_t* tp = tok_of + p0;
+        int t = 0;
 #pragma unroll
-      for (int j = 1; j < 16; ++j) {
-        const int tj = tp[min(j, cnt - 1)];
-        t = r == j ? tj : t;
+        for (int j = 0; j < 16; ++j) asm("v_writelane_b32 %0, %1, %2" : "+v"(t) : "s"(tp[min(j, cnt - 1)]), "i"(j));
+        t = __builtin_amdgcn_ds_bpermute(r << 2, t);
+        tile_row = min((uint32_t)t, (uint32_t)(T - 1));
       }
-      row = min((uint32_t)t, (uint32_t)(T - 1));
+      row = tile_row;
     }
     if constexpr (FMT == FMT_E4M3) {
       const uint32_t off = live && r < cnt ? (row * K + k0 + 32 * q) * 2 : BUF_OOB;
