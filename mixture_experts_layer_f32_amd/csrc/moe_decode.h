@@ -363,6 +363,21 @@ __global__ __launch_bounds__(1024) void dec_down(
 // loads: a unit past the end, an input past K or a token column past the
 // count uses an out-of-range offset and reads zeros without a memory access.
 constexpr uint32_t BUF_OOB = 0x80000000u;
+// Offset o if ok, else o with the sign bit set: past the extent of every
+// buffer these kernels read (each is under 2 GiB, which the host checks), so
+// the load returns zeros.  An OR keeps the offset in one register and the
+// load a single instruction; as a select of a computed offset the compiler
+// may instead branch around two copies of the load, whose shared destination
+// register then makes the wavefront wait for every load it has in flight.
+// OOB_SEL takes the OR for NVFP4 (measured 3-8 % faster with it) and the
+// plain select for e2m1 (measured 1-3 % faster with that) and e4m3 (equal).
+__device__ __forceinline__ uint32_t oob_or(bool ok, uint32_t o) {
+  const uint32_t m = ok ? 0u : BUF_OOB;
+  uint32_t v;
+  asm("v_or_b32 %0, %1, %2" : "=v"(v) : "v"(o), "v"(m));
+  return v;
+}
+#define OOB_SEL(ok, o) (FMT == FMT_NVFP4 ? oob_or((ok), (o)) : (ok) ? (o) : BUF_OOB)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
@@ -419,7 +434,7 @@ __device__ __forceinline__ decltype(DecUnitW<FMT>::g) load_scale_run(__amdgpu_bu
                                                                      uint32_t off, int avail) {
   constexpr int SB = dec_run_bytes<FMT>();
   if (avail >= SB || !in) {
-    const uint32_t o = in ? off : BUF_OOB;
+    const uint32_t o = OOB_SEL(in, off);
     if constexpr (FMT == FMT_NVFP4)
       return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, 0));
     else
@@ -507,7 +522,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int n = n0 + 16 * t + r;
-          const uint32_t off = live && n < N ? (uint32_t)n * rb + k0 + 32 * q : BUF_OOB;
+          const uint32_t off = OOB_SEL(live && n < N, (uint32_t)n * rb + k0 + 32 * q);
           s.wv[m][t].w[0] = buf_load16(wr, off, 0);
           s.wv[m][t].w[1] = buf_load16(wr, off, 16);
         }
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const bool in = live && n < N && k0 + 64 * q + 32 * h < K;
-            s.wv[m][t].w[h] = buf_load16(wr, in ? (uint32_t)n * rb + k0 / 2 + 32 * q + 16 * h : BUF_OOB, 0);
+            s.wv[m][t].w[h] = buf_load16(wr, OOB_SEL(in, (uint32_t)n * rb + k0 / 2 + 32 * q + 16 * h), 0);
           }
           if ((j & 3) == 0)
             s.wv[m][t].g = load_scale_run<FMT>(sr, live && n < N && j + q < nu, (uint32_t)n * sgroups + run0,
@@ -548,7 +563,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
       row = tile_row;
     }
     if constexpr (FMT == FMT_E4M3) {
-      const uint32_t off = live && r < cnt ? (row * K + k0 + 32 * q) * 2 : BUF_OOB;
+      const uint32_t off = OOB_SEL(live && r < cnt, (row * K + k0 + 32 * q) * 2);
       s.x[0] = buf_load16(ar, off, 0);
       s.x[1] = buf_load16(ar, off, 16);
       s.x[2] = buf_load16(ar, off, 32);
@@ -557,7 +572,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int k = k0 + 64 * q + 32 * h;
-        const uint32_t off = live && r < cnt && k < K ? (row * K + k) * 2 : BUF_OOB;
+        const uint32_t off = OOB_SEL(live && r < cnt && k < K, (row * K + k) * 2);
 #pragma unroll
         for (int a = 0; a < 4; ++a) s.x[4 * h + a] = buf_load16(ar, off, 16 * a);
       }
@@ -697,6 +712,8 @@ __global__ __launch_bounds__(256) void dec_mfma(
     }
   }
 }
+
+#undef OOB_SEL
 
 // Fixed-order combine: out[t] = sum over j ascending of w[t,j] * y[inv_perm[t*k+j]]
 // in f32, a gather in router order, so every output has one fixed summation
