@@ -498,22 +498,53 @@ __global__ __launch_bounds__(256) void dec_mfma(
   // and a unit waits only for its own loads, not for those issued after it
   // (measured 2-3% faster there; e4m3 skips the issue past the end, measured
   // 2% faster for it).
-  constexpr bool ALWAYS = FMT != FMT_E4M3;
-  // gate/up: lane r's token row depends only on the tile, and a wavefront
-  // issues a tile's units one after another, so it is looked up once per tile
-  int row_tile = -1;
+#ifndef DEC_E4M3_ALWAYS
+#define DEC_E4M3_ALWAYS 0
+#endif
+  constexpr bool ALWAYS = FMT != FMT_E4M3 || DEC_E4M3_ALWAYS;
+  // The issue side walks this wavefront's units in order: (i_jt, i_j) is the
+  // position of the unit last issued (tile i_jt of the workgroup, unit i_j of
+  // that tile), advanced by one per live issue, and the tile's entry and,
+  // for gate/up, lane r's token row are looked up only when the tile changes
+  // (no integer divisions or entry loads per unit).  A unit past the end
+  // keeps the last unit's tile and addresses.
+  int i_jt = 0, i_j = -1;
+  int t_e = 0, t_p0 = 0, t_cnt = 1, t_n0 = 0;
+  bool t_sh = false;
   uint32_t tile_row = 0;
   auto issue = [&](Unit& s, int u) {
     const bool live = u < units;
-    u = min(u, units - 1);
-    const int jt = u / nu;
-    const int j = u - jt * nu;
+    if (live && ++i_j == nu) {
+      i_j = 0;
+      ++i_jt;
+    }
+    const int j = i_j;
     const int kb = w + KS * j;
-    const int tile = b + jt * G;
-    const int ti = tile / tpe, n0 = (tile - ti * tpe) * TR;
-    const int4 info = tiles[ti];
-    const int e = info.x, p0 = info.y, cnt = info.z;
-    const bool sh = info.w != 0;
+    if (live && j == 0) {  // a new tile
+      const int tile = b + i_jt * G;
+      const int ti = tile / tpe;
+      t_n0 = (tile - ti * tpe) * TR;
+      const int4 info = tiles[ti];
+      t_e = info.x;
+      t_p0 = info.y;
+      t_cnt = info.z;
+      t_sh = info.w != 0;
+      if (GATEUP) {
+        // the entry's (<= 16) token ids by scalar loads, written to lanes
+        // 0..15 of one register and spread to lane groups 1..3 by a permute
+        const int32_t* tp = tok_of + t_p0;
+        int tv[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) tv[jj] = tp[min(jj, t_cnt - 1)];
+        int tk = 0;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) asm("v_writelane_b32 %0, %1, %2" : "+v"(tk) : "s"(tv[jj]), "i"(jj));
+        tk = __builtin_amdgcn_ds_bpermute(r << 2, tk);
+        tile_row = min((uint32_t)tk, (uint32_t)(T - 1));
+      }
+    }
+    const int e = t_e, p0 = t_p0, cnt = t_cnt, n0 = t_n0;
+    const bool sh = t_sh;
     const int k0 = kb * KU;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -545,23 +576,9 @@ __global__ __launch_bounds__(256) void dec_mfma(
         s.sc[m] = 0.0f;
       }
     }
-    // activation row of token column r: gate/up takes the entry's (<= 16)
-    // tokens by scalar loads, lane r keeping entry r; down reads h[p0 + r]
-    uint32_t row = (uint32_t)(p0 + min(r, cnt - 1));
-    if (GATEUP) {
-      if (tile != row_tile) {
-        // the entry's (<= 16) token ids by scalar loads, written to lanes
-        // 0..15 of one register and spread to lane groups 1..3 by a permute
-        row_tile = tile;
-        const int32_t* tp = tok_of + p0;
-        int t = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) asm("v_writelane_b32 %0, %1, %2" : "+v"(t) : "s"(tp[min(j, cnt - 1)]), "i"(j));
-        t = __builtin_amdgcn_ds_bpermute(r << 2, t);
-        tile_row = min((uint32_t)t, (uint32_t)(T - 1));
-      }
-      row = tile_row;
-    }
+    // activation row of token column r: gate/up the entry's token r (looked
+    // up above), down h[p0 + r]
+    const uint32_t row = GATEUP ? tile_row : (uint32_t)(p0 + min(r, cnt - 1));
     if constexpr (FMT == FMT_E4M3) {
       const uint32_t off = OOB_SEL(live && r < cnt, (row * K + k0 + 32 * q) * 2);
       s.x[0] = buf_load16(ar, off, 0);
@@ -583,14 +600,13 @@ __global__ __launch_bounds__(256) void dec_mfma(
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const Unit& s, int u) {
+  auto compute = [&](const Unit& s, int j) {  // j: the unit's place in its tile
     // e2m1/nvfp4: park the runs of units j..j+3 (on j = 0 mod 4; the wavefront's
     // own LDS rows, so program order orders the write before the reads), then
     // read this unit's bytes: e2m1 byte h = scale of chunk h; nvfp4 bytes
     // 2h, 2h + 1 = scales of chunk h's two halves
     uint32_t sv[NM][RT];
     if constexpr (FMT != FMT_E4M3) {
-      const int j = u - (u / nu) * nu;
       uint8_t* const base = runs + w * (NM * RT * 16 * RS);
       if ((j & 3) == 0) {
 #pragma unroll
@@ -694,20 +710,24 @@ __global__ __launch_bounds__(256) void dec_mfma(
 #pragma unroll
       for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  // Software pipeline over the unit stream (D - 1 units of loads ahead).
+  // Software pipeline over the unit stream (D - 1 units of loads ahead);
+  // the compute side keeps its own (tile, unit) position like the issue side.
   Unit st[D];
 #pragma unroll
   for (int s = 0; s < D - 1; ++s)
     if (ALWAYS || s < units) issue(st[s], s);
+  int c_jt = 0, c_j = -1;
   for (int u0 = 0; u0 < units; u0 += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       if (ALWAYS || u0 + s + D - 1 < units) issue(st[(s + D - 1) % D], u0 + s + D - 1);
-      const int u = u0 + s;
-      if (u < units) {
-        compute(st[s], u);
-        const int jt = u / nu;
-        if (u - jt * nu == nu - 1) finish(jt);
+      if (u0 + s < units) {
+        if (++c_j == nu) {
+          c_j = 0;
+          ++c_jt;
+        }
+        compute(st[s], c_j);
+        if (c_j == nu - 1) finish(c_jt);
       }
     }
   }

@@ -12,21 +12,25 @@ namespace moe {
 // kernel adds the slices in order 0, 1, ... and then the bias, so every logit
 // has one fixed summation order.
 
-// Few tokens: one wavefront per (expert, K-slice).  The slice is taken in
-// chunks of up to 1024 inputs: a chunk's router weights (four 16-byte loads
-// per lane) and then the activations of TG tokens are all loaded before any
-// arithmetic, so a chunk costs about one memory latency; each lane sums its
-// inputs in ascending order and a wave-wide sum finishes each partial logit.
+// Few tokens: one wavefront per (expert, K-slice), four experts per
+// workgroup.  The slice is taken in chunks of up to 1024 inputs: the
+// workgroup stages the chunk's activations of TG tokens in LDS once (8-byte
+// pieces, all loads issued before the first store), while each wavefront's
+// router weights (four 16-byte loads per lane) are in flight; each lane then
+// sums its inputs in ascending order and a wave-wide sum finishes each
+// partial logit.  (Each wavefront reading the activations from memory itself
+// moved four times the bytes through the caches and issued 16x the loads.)
 template <int TG>
 __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ x,
                                                    const float* __restrict__ wr,
                                                    float* __restrict__ part, int T, int d, int E,
                                                    int slice) {
+  __shared__ u32x2 xs[TG][256];  // TG tokens x 1024 bf16 inputs
   const int e = blockIdx.x * 4 + wave_id();
-  if (e >= E) return;
-  const int lane = lane_id();
+  const bool has_e = e < E;  // every wavefront takes part in the staging
+  const int lane = lane_id(), tid = threadIdx.x;
   const int k0 = blockIdx.y * slice, k1 = min(d, k0 + slice);
-  const float* wrow = wr + (size_t)e * d;
+  const float* wrow = wr + (size_t)min(e, E - 1) * d;
   float* out = part + (size_t)blockIdx.y * T * E;
   for (int t0 = 0; t0 < T; t0 += TG) {
     float acc[TG];
@@ -39,29 +43,37 @@ __global__ __launch_bounds__(256) void router_gemv(const uint16_t* __restrict__ 
       for (int c = 0; c < 4; ++c) {
         const int k = kc + 256 * c + 4 * lane;
         in[c] = k < k1;
-        wv[c] = in[c] ? *reinterpret_cast<const f32x4*>(wrow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
+        wv[c] = has_e && in[c] ? *reinterpret_cast<const f32x4*>(wrow + k) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      u32x2 xv[TG][4];
+      u32x2 st[TG];
 #pragma unroll
-      for (int i = 0; i < TG; ++i)
+      for (int i = 0; i < TG; ++i) {  // piece tid of token row t0 + i
+        const int k = kc + 4 * tid;
+        st[i] = t0 + i < T && k < k1 ? *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + i) * d + k)
+                                     : u32x2{0u, 0u};
+      }
+      __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int k = kc + 256 * c + 4 * lane;
-          xv[i][c] = t0 + i < T && in[c] ? *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + i) * d + k)
-                                         : u32x2{0u, 0u};
-        }
+      for (int i = 0; i < TG; ++i) xs[i][tid] = st[i];
+      __syncthreads();
+      if (has_e) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int i = 0; i < TG; ++i)
-          acc[i] += wv[c].x * bf16_lo(xv[i][c].x) + wv[c].y * bf16_hi(xv[i][c].x) +
-                    wv[c].z * bf16_lo(xv[i][c].y) + wv[c].w * bf16_hi(xv[i][c].y);
+          for (int i = 0; i < TG; ++i) {
+            const u32x2 xv = t0 + i < T && in[c] ? xs[i][64 * c + lane] : u32x2{0u, 0u};
+            acc[i] += wv[c].x * bf16_lo(xv.x) + wv[c].y * bf16_hi(xv.x) + wv[c].z * bf16_lo(xv.y) +
+                      wv[c].w * bf16_hi(xv.y);
+          }
+      }
     }
+    if (has_e) {
 #pragma unroll
-    for (int i = 0; i < TG; ++i) {
-      if (t0 + i < T) {
-        const float sum = wave_sum(acc[i]);
-        if (lane == 0) out[(size_t)(t0 + i) * E + e] = sum;
+      for (int i = 0; i < TG; ++i) {
+        if (t0 + i < T) {
+          const float sum = wave_sum(acc[i]);
+          if (lane == 0) out[(size_t)(t0 + i) * E + e] = sum;
+        }
       }
     }
   }
