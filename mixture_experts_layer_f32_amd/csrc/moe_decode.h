@@ -496,12 +496,13 @@ __global__ __launch_bounds__(256) void dec_mfma(
   // end takes the last unit's addresses with out-of-range offsets (no memory
   // access), so the compiler's load counting sees one pattern on every path
   // and a unit waits only for its own loads, not for those issued after it
-  // (measured 2-3% faster there; e4m3 skips the issue past the end, measured
-  // 2% faster for it).
-#ifndef DEC_E4M3_ALWAYS
-#define DEC_E4M3_ALWAYS 0
-#endif
-  constexpr bool ALWAYS = FMT != FMT_E4M3 || DEC_E4M3_ALWAYS;
+  // (measured 2-3% faster there).  e4m3 skips the issue past the end, so its
+  // units also wait for the loads issued after them (the wavefront keeps one
+  // unit of loads in flight): measured 2-6 % faster than the overlapped form
+  // at 8-32 tokens on the OLMoE shape, and equal at 64 tokens on the d = 7168
+  // layer; three units in flight and 16 wavefronts per CU measured equal or
+  // slower too.
+  constexpr bool ALWAYS = FMT != FMT_E4M3;
   // The issue side walks this wavefront's units in order: (i_jt, i_j) is the
   // position of the unit last issued (tile i_jt of the workgroup, unit i_j of
   // that tile), advanced by one per live issue, and the tile's entry and,
