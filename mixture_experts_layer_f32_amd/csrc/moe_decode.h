@@ -427,13 +427,19 @@ template <int FMT> constexpr int dec_run_stride() { return FMT == FMT_NVFP4 ? 80
 
 // The scale run of one unit of row n: bytes [off, off + SB) of the row's
 // scales, of which `avail` lie inside the row (fewer than SB only on the last
-// unit of a row whose K is not a multiple of 256: the rest read as zero).
+// unit of a row whose K is not a multiple of 256).  Past the row's end a
+// wide load reads the next row's scales, which only multiply the zeros that
+// stand for the inputs past K (weights and activations there read as zero),
+// so every row but the matrix's last (`has_next` false) takes the wide load;
+// the last row's run would reach past the buffer, so it is assembled from
+// byte loads, the bytes past the row reading zero.  (Byte loads for every
+// ragged run made one wavefront per tile wait for all its loads in flight.)
 // Wide loads need no alignment on gfx950 (unaligned buffer access).
 template <int FMT>
 __device__ __forceinline__ decltype(DecUnitW<FMT>::g) load_scale_run(__amdgpu_buffer_rsrc_t sr, bool in,
-                                                                     uint32_t off, int avail) {
+                                                                     uint32_t off, int avail, bool has_next) {
   constexpr int SB = dec_run_bytes<FMT>();
-  if (avail >= SB || !in) {
+  if (avail >= SB || !in || has_next) {
     const uint32_t o = OOB_SEL(in, off);
     if constexpr (FMT == FMT_NVFP4)
       return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, 0));
@@ -572,7 +578,7 @@ __global__ __launch_bounds__(256) void dec_mfma(
           }
           if ((j & 3) == 0)
             s.wv[m][t].g = load_scale_run<FMT>(sr, live && n < N && j + q < nu, (uint32_t)n * sgroups + run0,
-                                                (int)sgroups - run0);
+                                                (int)sgroups - run0, n + 1 < N);
         }
         s.sc[m] = 0.0f;
       }
